@@ -1,0 +1,500 @@
+/*
+ * CPU oracle for token-wise INT4 KV-cache quantization with a block-diagonal
+ * Hadamard rotation, and for paged decode attention over that cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  The product
+ * path (the HIP library) never links, imports or calls it, and it shares no
+ * source, header, table or helper with the HIP kernels.
+ *
+ * It is deliberately plain and slow: scalar loops in the order the method is
+ * described, no blocking, no fusion, no reordering.  The quantization path is
+ * fp32 (that is the arithmetic whose result must be reproduced bit for bit);
+ * attention is fp64.  Build with `gcc -O2 -ffp-contract=off` so that no
+ * multiply-add is fused behind our back, and never with -ffast-math.
+ *
+ * Sources (cited by page title and section):
+ *   [EXPL]  "KVキャッシュを4ビットへ — SAW-INT4とシステムを踏まえたINT4量子化"
+ *           (youngju.dev blog explainer of the SAW-INT4 preprint).
+ *           Sections used: "KVキャッシュこそが本当のボトルネックである理由"
+ *           (the KV cache as bottleneck; paged layout, fused attention),
+ *           "素朴なINT4はなぜ崩れるのか" (naive INT4; token-wise scales),
+ *           "回転のトリック — ブロック対角アダマール" (block-diagonal Hadamard),
+ *           "システムこそが設計である — 融合カーネル" and its figure
+ *           (fused rotate + quantize + append into paged KV blocks).
+ *   [SUMM]  "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World
+ *           LLM Serving" (gist.science AI-generated summary), sections on the
+ *           problem, the solution and the results.
+ * Where the pages leave a step open, the reading taken is stated at the step.
+ * Every such reading is one the HIP path must reproduce exactly.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD (-1)
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 <-> binary32, written from the format definitions.          */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float float_of(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* binary16 -> binary32.  Every half value is exactly representable. */
+float kvq_oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t expo = (uint32_t)(h >> 10) & 0x1Fu;
+    uint32_t frac = (uint32_t)h & 0x3FFu;
+    float mag;
+    if (expo == 0x1Fu) {
+        mag = frac ? NAN : INFINITY;
+    } else if (expo == 0) {
+        /* subnormal: frac * 2^-24, exact in binary32 */
+        mag = ldexpf((float)frac, -24);
+    } else {
+        mag = ldexpf((float)(frac | 0x400u), (int)expo - 25);
+    }
+    return sign ? -mag : mag;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even. */
+uint16_t kvq_oracle_f32_to_f16(float f)
+{
+    uint32_t u = bits_of(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t expo = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x7FFFFFu;
+
+    if (expo == 0xFFu) {                        /* Inf or NaN */
+        return (uint16_t)(sign | 0x7C00u | (frac ? 0x200u : 0u));
+    }
+    /* Work with the exact value  m * 2^(e) where m is a 24-bit integer. */
+    if (expo == 0 && frac == 0) return sign;   /* signed zero */
+    uint32_t m;
+    int e;
+    if (expo == 0) { m = frac; e = -149; }     /* binary32 subnormal */
+    else { m = frac | 0x800000u; e = (int)expo - 150; }
+
+    /* Target: half normal values are M * 2^(E-25) with M in [1024, 2047],
+     * E in [1, 30]; subnormals are M * 2^-24 with M in [0, 1023].
+     * Find the exponent q of the unit in the last place of the result. */
+    /* value = m * 2^e; position of the leading bit: */
+    int lead = 31 - __builtin_clz(m) + e;      /* value in [2^lead, 2^(lead+1)) */
+    int q = lead - 10;                          /* ulp exponent for a normal half */
+    if (q < -24) q = -24;                       /* subnormal range: fixed ulp 2^-24 */
+    /* round m * 2^e to a multiple of 2^q, ties to even */
+    int shift = q - e;                          /* number of bits to drop */
+    uint64_t M;
+    if (shift <= 0) {
+        M = (uint64_t)m << (-shift);
+    } else if (shift > 40) {
+        M = 0;                                  /* far below half an ulp */
+    } else {
+        uint64_t mm = m;
+        uint64_t kept = mm >> shift;
+        uint64_t rem = mm & ((1ull << shift) - 1);
+        uint64_t half = 1ull << (shift - 1);
+        if (rem > half || (rem == half && (kept & 1ull))) kept += 1;
+        M = kept;
+    }
+    /* Rounding may have carried into a new binade. */
+    if (M >= 2048) { M >>= 1; q += 1; }
+    if (q < -24) return sign;                   /* cannot happen, kept for clarity */
+    if (M < 1024) {
+        /* subnormal (q == -24) or zero */
+        return (uint16_t)(sign | (uint16_t)M);
+    }
+    int E = q + 25;                             /* biased half exponent */
+    if (E >= 31) return (uint16_t)(sign | 0x7C00u);   /* overflow to infinity */
+    return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)(M - 1024));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-diagonal Hadamard rotation  ([EXPL] "回転のトリック").               */
+/* ------------------------------------------------------------------------ */
+
+/* Reading: the Hadamard matrix is Sylvester's, in natural order
+ * (H_2n = [[H, H], [H, -H]]); the rotation is R = H / sqrt(Bh), so it is
+ * orthogonal and its own inverse, as the section requires.  The fp32 factor
+ * is the round-to-nearest binary32 value of 1/sqrt(Bh).  For the block sizes
+ * the cache supports these are 0x3E3504F3 (Bh=32), 0x3E000000 (Bh=64) and
+ * 0x3DB504F3 (Bh=128); a test pins them against a 50-digit computation. */
+float kvq_oracle_hadamard_scale(int bh)
+{
+    if (bh <= 0) return 1.0f;
+    return (float)(1.0 / sqrt((double)bh));
+}
+
+/* Unnormalised FWHT applied independently to each contiguous block of Bh
+ * entries (the rotation never crosses a block, which is what keeps it
+ * compatible with the paged layout).  Stages run with the butterfly span h
+ * ascending 1, 2, 4, ..., Bh/2; each butterfly replaces (u, v) by
+ * (u + v, u - v), one binary32 operation each. */
+void kvq_oracle_fwht_f32(float *y, int n, int bh)
+{
+    if (bh <= 1) return;
+    for (int b0 = 0; b0 + bh <= n; b0 += bh) {
+        for (int h = 1; h < bh; h <<= 1) {
+            for (int i = 0; i < bh; i++) {
+                if (i & h) continue;
+                float u = y[b0 + i];
+                float v = y[b0 + i + h];
+                y[b0 + i] = u + v;
+                y[b0 + i + h] = u - v;
+            }
+        }
+    }
+}
+
+/* fp64 rotation R.x = H.x / sqrt(Bh) per block (used for the query and the
+ * inverse rotation of the attention output; R is its own inverse). */
+void kvq_oracle_rotate_f64(double *x, int n, int bh)
+{
+    if (bh <= 0) return;
+    double c = 1.0 / sqrt((double)bh);
+    for (int b0 = 0; b0 + bh <= n; b0 += bh) {
+        for (int h = 1; h < bh; h <<= 1) {
+            for (int i = 0; i < bh; i++) {
+                if (i & h) continue;
+                double u = x[b0 + i];
+                double v = x[b0 + i + h];
+                x[b0 + i] = u + v;
+                x[b0 + i + h] = u - v;
+            }
+        }
+        for (int i = 0; i < bh; i++) x[b0 + i] *= c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Token-wise INT4 quantization of one vector ([EXPL] "素朴なINT4は..." for    */
+/* the one-scale-per-token choice, "回転のトリック" for rotating first, and   */
+/* the fused-kernel figure for the order rotate -> quantize -> append).       */
+/* ------------------------------------------------------------------------ */
+
+#define ORACLE_MAX_D 1024
+
+/* x: D fp16 values of one (token, KV head, K-or-V).  Writes D/2 packed bytes
+ * and one fp16 scale.  Steps:
+ *   1. widen to fp32 (exact);
+ *   2. if Bh > 0: block FWHT (above), then multiply by the fp32 1/sqrt(Bh);
+ *   3. m = max |y|;
+ *   4. scale s32 = m / 7 (IEEE division), stored as s16 = fp16(s32) (RNE).
+ *      Reading: symmetric absmax scale, no zero point, stored in fp16, and
+ *      the codes are computed against the stored s16 so that decode sees
+ *      exactly the scale the codes were made with;
+ *   5. if s16 == 0 every code is 0; else code = clamp(rint(y / s16), -8, 7)
+ *      with IEEE division and rounding half to even;
+ *   6. two's-complement nibbles, element 2j in the low nibble of byte j. */
+int kvq_oracle_quantize_vector(const uint16_t *x, int d, int bh,
+                               uint8_t *codes, uint16_t *scale_out)
+{
+    if (d <= 0 || d > ORACLE_MAX_D || (d & 1)) return ORACLE_BAD;
+    if (bh < 0 || (bh > 0 && (bh > d || (bh & (bh - 1)) || d % bh))) return ORACLE_BAD;
+    float y[ORACLE_MAX_D];
+    for (int i = 0; i < d; i++) y[i] = kvq_oracle_f16_to_f32(x[i]);
+    if (bh > 1) {
+        kvq_oracle_fwht_f32(y, d, bh);
+        float c = kvq_oracle_hadamard_scale(bh);
+        for (int i = 0; i < d; i++) y[i] = y[i] * c;
+    }
+    float m = 0.0f;
+    for (int i = 0; i < d; i++) {
+        float a = fabsf(y[i]);
+        if (a > m) m = a;
+    }
+    float s32 = m / 7.0f;
+    uint16_t s16 = kvq_oracle_f32_to_f16(s32);
+    float s = kvq_oracle_f16_to_f32(s16);
+    for (int j = 0; j < d / 2; j++) {
+        int c[2];
+        for (int t = 0; t < 2; t++) {
+            int code = 0;
+            if (s != 0.0f) {
+                float qv = y[2 * j + t] / s;
+                code = (int)rintf(qv);
+                if (code < -8) code = -8;
+                if (code > 7) code = 7;
+            }
+            c[t] = code;
+        }
+        codes[j] = (uint8_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4));
+    }
+    *scale_out = s16;
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Paged layout ([EXPL] "KVキャッシュこそが..." names the paged layout; the  */
+/* fused-kernel figure appends each token into a paged block).               */
+/* Reading: per (physical page, KV head) one tile of                          */
+/*   codes[P][D/2] bytes followed by scales[P] little-endian fp16;            */
+/* tiles ordered [page][head]; separate pools for K and V.                   */
+/* The page table is int32 [batch][max_pages_per_seq], logical page ->       */
+/* physical page; token position pos of sequence b lives in logical page     */
+/* pos / P at slot pos % P.                                                  */
+/* ------------------------------------------------------------------------ */
+
+static int64_t tile_bytes(int d, int p) { return (int64_t)p * (d / 2) + 2 * (int64_t)p; }
+
+int64_t kvq_oracle_tile_bytes(int d, int p) { return tile_bytes(d, p); }
+
+/* Locate (physical page, slot) of token position pos of sequence seq.
+ * Returns -1 on any out-of-range index. */
+static int64_t locate(const int32_t *page_table, int max_pages, int64_t num_pages,
+                      int seq, int pos, int p, int *slot)
+{
+    if (pos < 0 || seq < 0) return -1;
+    int lp = pos / p;
+    if (lp >= max_pages) return -1;
+    int64_t page = page_table[(int64_t)seq * max_pages + lp];
+    if (page < 0 || page >= num_pages) return -1;
+    *slot = pos % p;
+    return page;
+}
+
+/* Quantize every new token's K and V and write them into their slots; no
+ * other byte of either pool changes (past tokens are never revisited). */
+int kvq_oracle_kv_quant_append(const uint16_t *k_new, const uint16_t *v_new,
+                               const int32_t *token_seq, const int32_t *token_pos,
+                               int32_t num_tokens, const int32_t *page_table,
+                               int32_t max_pages_per_seq, uint8_t *k_pool,
+                               uint8_t *v_pool, int64_t num_pages,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t had_block)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0) return ORACLE_BAD;
+    int64_t tb = tile_bytes(head_dim, page_size);
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int32_t t = 0; t < num_tokens; t++) {
+        int slot = 0;
+        int64_t page = locate(page_table, max_pages_per_seq, num_pages,
+                              token_seq[t], token_pos[t], page_size, &slot);
+        if (page < 0) { bad = 1; continue; }
+        for (int h = 0; h < num_kv_heads; h++) {
+            for (int which = 0; which < 2; which++) {
+                const uint16_t *src = (which == 0 ? k_new : v_new) +
+                                      ((int64_t)t * num_kv_heads + h) * head_dim;
+                uint8_t *tile = (which == 0 ? k_pool : v_pool) +
+                                (page * num_kv_heads + h) * tb;
+                uint16_t s16;
+                if (kvq_oracle_quantize_vector(src, head_dim, had_block,
+                                               tile + (int64_t)slot * (head_dim / 2),
+                                               &s16) != ORACLE_OK) {
+                    bad = 1;
+                    continue;
+                }
+                uint8_t *sp = tile + (int64_t)page_size * (head_dim / 2) + 2 * slot;
+                sp[0] = (uint8_t)(s16 & 0xFF);
+                sp[1] = (uint8_t)(s16 >> 8);
+            }
+        }
+    }
+    return bad ? ORACLE_BAD : ORACLE_OK;
+}
+
+/* fp16 baseline append: copy each token's fp16 K/V into fp16 pools laid out
+ * [page][head][slot][D]. */
+int kvq_oracle_kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
+                              const int32_t *token_seq, const int32_t *token_pos,
+                              int32_t num_tokens, const int32_t *page_table,
+                              int32_t max_pages_per_seq, uint16_t *k_pool,
+                              uint16_t *v_pool, int64_t num_pages,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size)
+{
+    int bad = 0;
+    for (int32_t t = 0; t < num_tokens; t++) {
+        int slot = 0;
+        int64_t page = locate(page_table, max_pages_per_seq, num_pages,
+                              token_seq[t], token_pos[t], page_size, &slot);
+        if (page < 0) { bad = 1; continue; }
+        for (int h = 0; h < num_kv_heads; h++) {
+            int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim;
+            int64_t dst = ((page * num_kv_heads + h) * page_size + slot) * (int64_t)head_dim;
+            memcpy(k_pool + dst, k_new + src, (size_t)head_dim * 2);
+            memcpy(v_pool + dst, v_new + src, (size_t)head_dim * 2);
+        }
+    }
+    return bad ? ORACLE_BAD : ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the paged cache, fp64.                              */
+/* Reading: query heads qh map to KV head qh / (Hq / Hkv); the caller's       */
+/* softmax_scale multiplies the dot product; because R is orthogonal,         */
+/* (R q).(R k) = q.k, so the query is rotated instead of un-rotating keys,    */
+/* and the weighted sum of rotated values is rotated back at the end.        */
+/* A context length <= 0 gives a zero output row.                             */
+/* ------------------------------------------------------------------------ */
+
+static double dequant(const uint8_t *tile, int d, int p, int slot, int i)
+{
+    uint8_t byte = tile[(int64_t)slot * (d / 2) + i / 2];
+    int nib = (i & 1) ? (byte >> 4) : (byte & 0xF);
+    int code = (nib & 8) ? nib - 16 : nib;
+    const uint8_t *sp = tile + (int64_t)p * (d / 2) + 2 * slot;
+    uint16_t s16 = (uint16_t)(sp[0] | (sp[1] << 8));
+    return (double)code * (double)kvq_oracle_f16_to_f32(s16);
+}
+
+/* Generic softmax attention for one (sequence, query head) over L keys
+ * provided by a callback-free loop: k_at/v_at fill a D-vector for key j. */
+static void attend_one(const double *qrot, int L, int d, double scale,
+                       void (*fetch)(const void *ctx, int j, int which, double *out),
+                       const void *ctx, double *out)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double kv[ORACLE_MAX_D];
+    double M = -INFINITY;
+    for (int j = 0; j < L; j++) {
+        fetch(ctx, j, 0, kv);
+        double dot = 0.0;
+        for (int i = 0; i < d; i++) dot += qrot[i] * kv[i];
+        z[j] = scale * dot;
+        if (z[j] > M) M = z[j];
+    }
+    double wsum = 0.0;
+    for (int i = 0; i < d; i++) out[i] = 0.0;
+    for (int j = 0; j < L; j++) {
+        double w = exp(z[j] - M);
+        wsum += w;
+        fetch(ctx, j, 1, kv);
+        for (int i = 0; i < d; i++) out[i] += w * kv[i];
+    }
+    for (int i = 0; i < d; i++) out[i] = (L > 0) ? out[i] / wsum : 0.0;
+    free(z);
+}
+
+typedef struct {
+    const uint8_t *k_pool, *v_pool;
+    const int32_t *page_table;
+    int max_pages;
+    int64_t num_pages;
+    int seq, kvh, hkv, d, p;
+    int fp16;               /* 1: fp16 pools, 0: INT4 pools */
+} paged_ctx;
+
+static void fetch_paged(const void *vctx, int j, int which, double *out)
+{
+    const paged_ctx *c = (const paged_ctx *)vctx;
+    int slot = 0;
+    int64_t page = locate(c->page_table, c->max_pages, c->num_pages, c->seq, j, c->p, &slot);
+    if (c->fp16) {
+        const uint16_t *pool = (const uint16_t *)(which == 0 ? c->k_pool : c->v_pool);
+        const uint16_t *row = pool + ((page * c->hkv + c->kvh) * c->p + slot) * (int64_t)c->d;
+        for (int i = 0; i < c->d; i++) out[i] = (double)kvq_oracle_f16_to_f32(row[i]);
+    } else {
+        const uint8_t *pool = which == 0 ? c->k_pool : c->v_pool;
+        const uint8_t *tile = pool + (page * c->hkv + c->kvh) * tile_bytes(c->d, c->p);
+        for (int i = 0; i < c->d; i++) out[i] = dequant(tile, c->d, c->p, slot, i);
+    }
+}
+
+static int decode_common(const uint16_t *q, const void *k_pool, const void *v_pool,
+                         int64_t num_pages, const int32_t *page_table,
+                         int32_t max_pages_per_seq, const int32_t *context_lens,
+                         int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t page_size, int32_t had_block,
+                         float softmax_scale, float *out, int fp16)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        head_dim > ORACLE_MAX_D || page_size <= 0 || num_q_heads % num_kv_heads)
+        return ORACLE_BAD;
+    for (int b = 0; b < batch; b++) {
+        int L = context_lens[b];
+        if (L > (int64_t)max_pages_per_seq * page_size) return ORACLE_BAD;
+        for (int lp = 0; lp < (L + page_size - 1) / page_size; lp++) {
+            int32_t pg = page_table[(int64_t)b * max_pages_per_seq + lp];
+            if (pg < 0 || pg >= num_pages) return ORACLE_BAD;
+        }
+    }
+    int group = num_q_heads / num_kv_heads;
+    int64_t units = (int64_t)batch * num_q_heads;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t u = 0; u < units; u++) {
+        int b = (int)(u / num_q_heads), qh = (int)(u % num_q_heads);
+        double qrot[ORACLE_MAX_D], o[ORACLE_MAX_D];
+        const uint16_t *qrow = q + ((int64_t)b * num_q_heads + qh) * head_dim;
+        for (int i = 0; i < head_dim; i++) qrot[i] = (double)kvq_oracle_f16_to_f32(qrow[i]);
+        if (!fp16) kvq_oracle_rotate_f64(qrot, head_dim, had_block);
+        paged_ctx c = { (const uint8_t *)k_pool, (const uint8_t *)v_pool, page_table,
+                        max_pages_per_seq, num_pages, b, qh / group, num_kv_heads,
+                        head_dim, page_size, fp16 };
+        int L = context_lens[b];
+        attend_one(qrot, L, head_dim, (double)softmax_scale, fetch_paged, &c, o);
+        if (!fp16 && L > 0) kvq_oracle_rotate_f64(o, head_dim, had_block);
+        float *orow = out + ((int64_t)b * num_q_heads + qh) * head_dim;
+        for (int i = 0; i < head_dim; i++) orow[i] = (float)o[i];
+    }
+    return ORACLE_OK;
+}
+
+int kvq_oracle_paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool,
+                                      const uint8_t *v_pool, int64_t num_pages,
+                                      const int32_t *page_table, int32_t max_pages_per_seq,
+                                      const int32_t *context_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size,
+                                      int32_t had_block, float softmax_scale, float *out)
+{
+    return decode_common(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq,
+                         context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                         page_size, had_block, softmax_scale, out, 0);
+}
+
+int kvq_oracle_paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool,
+                                      const uint16_t *v_pool, int64_t num_pages,
+                                      const int32_t *page_table, int32_t max_pages_per_seq,
+                                      const int32_t *context_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size,
+                                      float softmax_scale, float *out)
+{
+    return decode_common(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq,
+                         context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                         page_size, 0, softmax_scale, out, 1);
+}
+
+/* Dense reference: softmax(q . K^T * scale) . V for one sequence, fp64, with
+ * no paging, no rotation and no quantization.  q [Hq][D], K and V [L][Hkv][D]. */
+typedef struct { const double *k, *v; int hkv, kvh, d; } dense_ctx;
+
+static void fetch_dense(const void *vctx, int j, int which, double *out)
+{
+    const dense_ctx *c = (const dense_ctx *)vctx;
+    const double *src = (which == 0 ? c->k : c->v) + ((int64_t)j * c->hkv + c->kvh) * c->d;
+    for (int i = 0; i < c->d; i++) out[i] = src[i];
+}
+
+int kvq_oracle_dense_decode_f64(const double *q, const double *k, const double *v,
+                                int32_t L, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, double softmax_scale, double *out)
+{
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        head_dim <= 0 || head_dim > ORACLE_MAX_D)
+        return ORACLE_BAD;
+    int group = num_q_heads / num_kv_heads;
+    for (int qh = 0; qh < num_q_heads; qh++) {
+        dense_ctx c = { k, v, num_kv_heads, qh / group, head_dim };
+        attend_one(q + (int64_t)qh * head_dim, L, head_dim, softmax_scale, fetch_dense, &c,
+                   out + (int64_t)qh * head_dim);
+    }
+    return ORACLE_OK;
+}
+
+int kvq_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
