@@ -1,0 +1,459 @@
+"""Benchmark of the INT4 KV-cache hot path on one MI355X.
+
+One step = the whole hot path over one batch: kv_quant_append of the batch's
+new tokens (rotate, quantize, paged append) followed by
+paged_decode_attn_int4 over every sequence (split-K partial kernel + merge
+and inverse rotation).  Workload: 256 concurrent sequences with context
+lengths uniform in [1024, 8192] (seeded), 8 KV heads x 128, 32 query heads,
+Hadamard block 64, page size 16, pages shuffled over a shared pool; every
+input is synthetic and resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is whole-step throughput in algorithmic GB/s
+(the bytes the method must move: the INT4 K/V tiles of every cached token,
+the page-table entries, queries and outputs, and the append's fp16 input and
+INT4 output).  `roofline` is for the dominant kernel (the decode partial
+kernel), timed with HIP events recorded on the library's stream.  Secondary
+measurements (append bandwidth on a 65,536-token call, rotation on/off at
+128K context, per-layer latency at batch 1 and 32K context, the fp16
+baseline) are reported under "extra"; `cpu_baseline` times the CPU oracle on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+INT4_BYTES_PER_TOKEN_HEAD = 2 * (64 + 2)   # K and V: 64 code bytes + 2 scale bytes each
+FP16_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2
+APPEND_BYTES_PER_TOKEN_HEAD = 2 * (128 * 2) + INT4_BYTES_PER_TOKEN_HEAD   # read fp16 K,V; write INT4
+
+
+def decode_bytes(w, int4=True):
+    """Algorithmic bytes of one decode call: cached K/V of every attended token,
+    page-table entries, query (fp16) and output (fp32)."""
+    import numpy as np
+    ctx = np.maximum(w.context_lens.astype(np.int64), 0)
+    per = INT4_BYTES_PER_TOKEN_HEAD if int4 else FP16_BYTES_PER_TOKEN_HEAD
+    kv = int(ctx.sum()) * w.num_kv_heads * per
+    pages = int(((ctx + w.page_size - 1) // w.page_size).sum()) * 4
+    q = w.batch * w.num_q_heads * w.head_dim * 2
+    out = w.batch * w.num_q_heads * w.head_dim * 4
+    return kv + pages + q + out
+
+
+def append_bytes(T, hkv):
+    """Algorithmic bytes of one append call of T tokens: fp16 K/V rows read,
+    INT4 codes+scales written, (seq, pos, page-table) read."""
+    return T * hkv * APPEND_BYTES_PER_TOKEN_HEAD + T * 12
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_kv_cache_quant_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+DECODE_KERNEL_SRC = ("decode_valu.hip",)
+DECODE_KERNEL_NAME = "decode_partial_kernel<true>"
+
+
+def _traffic_from_profile(kernel_hash):
+    """HBM bytes per launch of the decode partial kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other code."""
+    path = os.path.join(ROOT, "profiles", "decode_int4_c4_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256_16") != kernel_hash:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Per-launch durations from torch.cuda events (hipEvents) on the current stream."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.pairs = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+
+def build_int4_cache(w, dev, layer=0, had_block=None):
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    bh = w.had_block if had_block is None else had_block
+    tb = kvq.page_tile_bytes(w.head_dim, w.page_size)
+    kp = torch.zeros((w.num_pages, w.num_kv_heads, tb), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    pt = torch.as_tensor(w.table(layer), device=dev)
+    for b in range(w.batch):
+        L = int(w.prefill_lens[b])
+        if L <= 0:
+            continue
+        k, v = w.rows(layer, b, 0, L, dev)
+        seq = torch.full((L,), b, dtype=torch.int32, device=dev)
+        pos = torch.arange(L, dtype=torch.int32, device=dev)
+        kvq.kv_quant_append(k, v, seq, pos, pt, kp, vp, w.page_size, bh)
+    return kp, vp, pt
+
+
+def build_fp16_cache(w, dev, layer=0):
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+    kp = torch.zeros(shape, dtype=torch.float16, device=dev)
+    vp = torch.zeros_like(kp)
+    pt = torch.as_tensor(w.table(layer), device=dev)
+    for b in range(w.batch):
+        L = int(w.prefill_lens[b])
+        if L <= 0:
+            continue
+        k, v = w.rows(layer, b, 0, L, dev)
+        seq = torch.full((L,), b, dtype=torch.int32, device=dev)
+        pos = torch.arange(L, dtype=torch.int32, device=dev)
+        kvq.kv_append_fp16(k, v, seq, pos, pt, kp, vp, w.page_size)
+    return kp, vp, pt
+
+
+def time_calls(fn, iters, warmup):
+    """Mean GPU time (ms) of fn() over iters calls, events around each call."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = []
+    for _ in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    first S sequences' append + decode, timed on the host cores."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+
+    def run(S):
+        sub_need = (w.context_lens[:S] + w.page_size - 1) // w.page_size
+        npg = int(sub_need.sum())
+        pt = np.full((S, int(sub_need.max())), -1, np.int32)
+        off = 0
+        for b in range(S):
+            pt[b, :sub_need[b]] = np.arange(off, off + sub_need[b], dtype=np.int32)
+            off += int(sub_need[b])
+        tb = oracle.tile_bytes(w.head_dim, w.page_size)
+        kp = np.zeros((npg, w.num_kv_heads, tb), np.uint8)
+        vp = np.zeros_like(kp)
+        for b in range(S):  # prefill (setup, not timed)
+            L = int(w.prefill_lens[b])
+            k, v = w.rows(0, b, 0, L, "cpu")
+            oracle.kv_quant_append(k.numpy(), v.numpy(), np.full(L, b, np.int32),
+                                   np.arange(L, dtype=np.int32), pt, kp, vp, w.had_block, w.page_size)
+        k_new = np.stack([w.rows(0, b, int(w.append_pos[b]), 1, "cpu")[0].numpy()[0] for b in range(S)])
+        v_new = np.stack([w.rows(0, b, int(w.append_pos[b]), 1, "cpu")[1].numpy()[0] for b in range(S)])
+        q = w.query(0, "cpu").numpy()[:S]
+        t0 = time.perf_counter()
+        oracle.kv_quant_append(k_new, v_new, np.arange(S, dtype=np.int32), w.append_pos[:S].copy(), pt, kp, vp,
+                               w.had_block, w.page_size)
+        oracle.paged_decode_attn_int4(q, kp, vp, pt, w.context_lens[:S].copy(), w.num_kv_heads, w.page_size,
+                                      w.had_block, w.softmax_scale)
+        dt = time.perf_counter() - t0
+        sub = wl.Workload(**{**w.__dict__, "batch": S, "context_lens": w.context_lens[:S],
+                              "per_layer_page_tables": None})
+        nbytes = decode_bytes(sub) + append_bytes(S, w.num_kv_heads)
+        return dt, nbytes
+
+    S = 2
+    dt, nbytes = run(S)
+    if dt < budget_s / 4:
+        S = int(min(w.batch, max(S + 1, math.floor(S * budget_s / max(dt, 1e-3) * 0.8))))
+        dt, nbytes = run(S)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"first {S} of {w.batch} sequences: append of their new tokens + fp64 decode "
+                      f"over their contexts (sum {int(w.context_lens[:S].sum())} tokens), "
+                      "same shapes, CPU-generated values"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="main workload only (no extra measurements)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the hot path is "
+              "per-GPU data-parallel and no multi-GPU run is part of this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvq.lib()
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------- main workload: decode step with append ----------------
+    w = wl.c4()
+    kp, vp, pt = build_int4_cache(w, dev)
+    k_new, v_new = w.append_rows(0, dev)
+    seq = torch.as_tensor(w.append_seq, device=dev)
+    pos = torch.as_tensor(w.append_pos, device=dev)
+    q = w.query(0, dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    maxctx = int(w.context_lens.max())
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, maxctx, w.page_size),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    mid = torch.cuda.Event(enable_timing=True)
+    mid.record()
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        kvq.kv_quant_append(k_new, v_new, seq, pos, pt, kp, vp, w.page_size, w.had_block)
+        if ev is not None:
+            ev[0].record()
+        kvq.paged_decode_attn_int4(q, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.had_block, w.softmax_scale,
+                                   maxctx, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events around each kernel phase
+    evs = []
+    kvq.set_decode_phase_event(None)
+    phase = []
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        em = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        em.record()                       # instantiate; re-recorded by the library
+        phase.append((e0, e1, em, e2))
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        e0, e1, em, e2 = phase[i]
+        kvq.set_decode_phase_event(em)
+        e0.record()
+        step(ev=(e1,))
+        e2.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kvq.set_decode_phase_event(None)
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+    t_append = [p[0].elapsed_time(p[1]) for p in phase]
+    t_partial = [p[1].elapsed_time(p[2]) for p in phase]
+    t_combine = [p[2].elapsed_time(p[3]) for p in phase]
+    mean = lambda xs: sum(xs) / len(xs)
+
+    dbytes = decode_bytes(w)
+    abytes = append_bytes(int(w.append_seq.size), w.num_kv_heads)
+    step_bytes = dbytes + abytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the partial kernel moves the tiles, page table and queries (outputs go via the workspace)
+    ctx = w.context_lens.astype(np.int64)
+    partial_alg = (int(ctx.sum()) * w.num_kv_heads * INT4_BYTES_PER_TOKEN_HEAD
+                   + int(((ctx + 15) // 16).sum()) * 4 + w.batch * w.num_q_heads * w.head_dim * 2)
+    achieved = partial_alg / (mean(t_partial) * 1e-3) / 1e9
+    khash = _src_hash(*DECODE_KERNEL_SRC)
+    traffic = _traffic_from_profile(khash)
+
+    result = {
+        "metric": "INT4 paged decode-attn HBM GB/s (% of peak); rotate-quant-append tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step with append: batch 256, ctx U[1024,8192] (seeded), 8 KV heads x 128, "
+                        "32 query heads, Hadamard block 64, page size 16, shuffled page pool",
+            "kv_format": "INT4 codes + fp16 scale per (token, KV head)",
+            "global_batch": w.batch,
+            "context_tokens": int(w.context_lens.sum()),
+            "bytes_per_step": step_bytes,
+            "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+            "append_tokens_per_s": round(w.batch / (mean(t_append) * 1e-3), 1),
+            "decode_ms": round(mean(t_partial) + mean(t_combine), 5),
+            "append_ms": round(mean(t_append), 5),
+            "host_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "kernel": DECODE_KERNEL_NAME,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": partial_alg,
+            "avg_launch_ms": round(mean(t_partial), 5),
+            "kernel_source_sha256_16": khash,
+        },
+    }
+    del kp, vp, ws, k_new, v_new
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        result["extra"] = extra_measurements(dev, args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def extra_measurements(dev, args):
+    import numpy as np
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
+    ex = {}
+
+    # Append bandwidth: 256 sequences x 256 consecutive tokens in one call.
+    w = wl.c2_stream()
+    tb = kvq.page_tile_bytes(w.head_dim, w.page_size)
+    kp = torch.zeros((w.num_pages, w.num_kv_heads, tb), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    k, v = w.append_rows(0, dev)
+    seq = torch.as_tensor(w.append_seq, device=dev)
+    pos = torch.as_tensor(w.append_pos, device=dev)
+    pt = torch.as_tensor(w.page_table, device=dev)
+    T = int(w.append_seq.size)
+    nb = append_bytes(T, w.num_kv_heads)
+    for bh in (64, 0):
+        ms, med = time_calls(lambda: kvq.kv_quant_append(k, v, seq, pos, pt, kp, vp, w.page_size, bh), 20, 3)
+        ex[f"append_65536tok_bh{bh}"] = {"ms": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                                         "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                                         "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    # decode-time append (1 token per sequence)
+    w2 = wl.c2()
+    k2, v2 = w2.append_rows(0, dev)
+    s2 = torch.as_tensor(w2.append_seq, device=dev)
+    p2 = torch.as_tensor(w2.append_pos, device=dev)
+    ms, med = time_calls(lambda: kvq.kv_quant_append(k2, v2, s2, p2, pt, kp, vp, 16, 64), 50, 5)
+    ex["append_256x1tok_bh64"] = {"ms": round(ms, 5), "tokens_per_s": round(256 / (ms * 1e-3), 1)}
+    del kp, vp, k, v
+    torch.cuda.empty_cache()
+
+    # Rotation on vs off: batch 8 x 131,072 context, page size 32.
+    rot = {}
+    for bh in (128, 0):
+        w5 = wl.c5(had_block=bh)
+        kp, vp, pt = build_int4_cache(w5, dev, had_block=bh)
+        q = w5.query(0, dev)
+        cl = torch.as_tensor(w5.context_lens, device=dev)
+        out = torch.empty((w5.batch, w5.num_q_heads, w5.head_dim), dtype=torch.float32, device=dev)
+        ws = torch.empty(kvq.workspace_bytes(w5.batch, 32, 8, 131072, 32), dtype=torch.uint8, device=dev)
+        ms, med = time_calls(lambda: kvq.paged_decode_attn_int4(q, kp, vp, pt, cl, 8, 32, bh, w5.softmax_scale,
+                                                                131072, out=out, workspace=ws), 20, 3)
+        nb = decode_bytes(w5)
+        rot[bh] = ms
+        ex[f"decode_8x128k_bh{bh}"] = {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                                       "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        del kp, vp
+        torch.cuda.empty_cache()
+    ex["rotation_overhead_pct"] = round(100 * (rot[128] / rot[0] - 1), 2)
+
+    # Latency-sensitive: batch 1, 32K context, 36 layers with distinct pools.
+    w3 = wl.c3()
+    caches = [build_int4_cache(w3, dev, layer=l) for l in range(w3.layers)]
+    qs = [w3.query(l, dev) for l in range(w3.layers)]
+    cl = torch.as_tensor(w3.context_lens, device=dev)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.workspace_bytes(1, 32, 8, 32768, 16), dtype=torch.uint8, device=dev)
+
+    def all_layers():
+        for l in range(w3.layers):
+            kpl, vpl, ptl = caches[l]
+            kvq.paged_decode_attn_int4(qs[l], kpl, vpl, ptl, cl, 8, 16, 128, w3.softmax_scale, 32768,
+                                       out=out, workspace=ws)
+    ms, med = time_calls(all_layers, 10, 2)
+    nb = decode_bytes(w3) * w3.layers
+    ex["decode_b1_32k_36layers"] = {"ms_per_step": round(ms, 5), "us_per_layer": round(1000 * ms / w3.layers, 3),
+                                    "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                                    "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    del caches
+    torch.cuda.empty_cache()
+
+    # fp16 baseline on the main workload.
+    w = wl.c4()
+    kp, vp, pt = build_fp16_cache(w, dev)
+    q = w.query(0, dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    maxctx = int(w.context_lens.max())
+    out = torch.empty((w.batch, 32, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.workspace_bytes(w.batch, 32, 8, maxctx, 16), dtype=torch.uint8, device=dev)
+    ms, med = time_calls(lambda: kvq.paged_decode_attn_fp16(q, kp, vp, pt, cl, 8, 16, w.softmax_scale, maxctx,
+                                                            out=out, workspace=ws), 10, 2)
+    nb = decode_bytes(w, int4=False)
+    ex["decode_fp16_c4"] = {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                            "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    del kp, vp
+    torch.cuda.empty_cache()
+    return ex
+
+
+if __name__ == "__main__":
+    sys.exit(main())

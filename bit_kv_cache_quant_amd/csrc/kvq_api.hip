@@ -1,0 +1,320 @@
+// C ABI of the INT4 KV-cache library: argument validation, split choice and
+// kernel launches.  The contract of every entry point is documented in
+// include/kvq.h.
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::kHeadDim;
+
+bool valid_page_size(int32_t p) { return p == 16 || p == 32; }
+bool valid_had_block(int32_t bh) { return bh == 0 || bh == 32 || bh == 64 || bh == 128; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int log2i(int32_t v) { int s = 0; while ((1 << s) < v) ++s; return s; }
+
+// Split-K choice shared by the workspace query and the decode calls.
+// Aim for about 1024 work items so that all 256 compute units get several,
+// and cap a split at 1024 tokens so that long and short sequences balance.
+void choose_split(int32_t batch, int32_t num_kv_heads, int32_t head_chunks, int32_t max_context_len,
+                  int32_t page_size, int32_t pages_per_split, int32_t *pps, int32_t *nsplit) {
+    const int32_t npages = max_context_len > 0 ? (max_context_len + page_size - 1) / page_size : 1;
+    int32_t p = pages_per_split;
+    if (p <= 0) {
+        const int64_t items = (int64_t)batch * num_kv_heads * head_chunks;
+        const int64_t want = items >= 1024 ? 1 : (1024 + items - 1) / items;
+        p = (int32_t)((npages + want - 1) / want);
+        const int32_t cap = 1024 / page_size;
+        if (p > cap) p = cap;
+        if (p < 1) p = 1;
+    }
+    *pps = p;
+    *nsplit = (npages + p - 1) / p;
+}
+
+int32_t head_chunks_of(int32_t num_q_heads, int32_t num_kv_heads) {
+    const int32_t group = num_q_heads / num_kv_heads;
+    return (group + kvq::kHeadsPerChunk - 1) / kvq::kHeadsPerChunk;
+}
+
+size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, int32_t nsplit) {
+    return (size_t)batch * num_q_heads * nsplit * (kHeadDim + 2) * sizeof(float);
+}
+
+// Timing hook (see kvq_set_decode_phase_event in include/kvq.h).
+void *g_phase_event = nullptr;
+
+// Optional debug mode (environment variable KVQ_CHECK=1): copy the page table
+// and lengths to the host (this synchronises the stream) and range-check them.
+bool debug_checks_enabled() {
+    static int enabled = -1;
+    if (enabled < 0) {
+        const char *e = getenv("KVQ_CHECK");
+        enabled = (e && e[0] == '1') ? 1 : 0;
+    }
+    return enabled == 1;
+}
+
+int check_append_indices(const int32_t *token_seq, const int32_t *token_pos, int32_t num_tokens,
+                         const int32_t *page_table, int32_t max_pages_per_seq, int64_t num_pages,
+                         int32_t page_size, hipStream_t stream) {
+    int32_t *seq = (int32_t *)malloc(sizeof(int32_t) * num_tokens);
+    int32_t *pos = (int32_t *)malloc(sizeof(int32_t) * num_tokens);
+    int rc = KVQ_OK;
+    if (!seq || !pos) { free(seq); free(pos); return KVQ_ERR_INVALID_ARG; }
+    if (hipMemcpyAsync(seq, token_seq, sizeof(int32_t) * num_tokens, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(pos, token_pos, sizeof(int32_t) * num_tokens, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        rc = KVQ_ERR_HIP;
+    }
+    for (int32_t t = 0; rc == KVQ_OK && t < num_tokens; ++t) {
+        if (seq[t] < 0 || pos[t] < 0 || pos[t] / page_size >= max_pages_per_seq) { rc = KVQ_ERR_INVALID_ARG; break; }
+        int32_t page = -1;
+        const int32_t *src = page_table + (int64_t)seq[t] * max_pages_per_seq + pos[t] / page_size;
+        if (hipMemcpy(&page, src, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) { rc = KVQ_ERR_HIP; break; }
+        if (page < 0 || page >= num_pages) rc = KVQ_ERR_INVALID_ARG;
+    }
+    free(seq);
+    free(pos);
+    return rc;
+}
+
+int check_decode_indices(const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                         int32_t batch, int32_t max_context_len, int64_t num_pages, int32_t page_size,
+                         hipStream_t stream) {
+    const size_t n = (size_t)batch * max_pages_per_seq;
+    int32_t *pt = (int32_t *)malloc(sizeof(int32_t) * n);
+    int32_t *cl = (int32_t *)malloc(sizeof(int32_t) * batch);
+    int rc = KVQ_OK;
+    if (!pt || !cl) { free(pt); free(cl); return KVQ_ERR_INVALID_ARG; }
+    if (hipMemcpyAsync(pt, page_table, sizeof(int32_t) * n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(cl, context_lens, sizeof(int32_t) * batch, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        rc = KVQ_ERR_HIP;
+    }
+    for (int32_t b = 0; rc == KVQ_OK && b < batch; ++b) {
+        if (cl[b] > max_context_len || (int64_t)cl[b] > (int64_t)max_pages_per_seq * page_size) { rc = KVQ_ERR_INVALID_ARG; break; }
+        for (int32_t p = 0; p < (cl[b] + page_size - 1) / page_size; ++p) {
+            const int32_t v = pt[(size_t)b * max_pages_per_seq + p];
+            if (v < 0 || v >= num_pages) { rc = KVQ_ERR_INVALID_ARG; break; }
+        }
+    }
+    free(pt);
+    free(cl);
+    return rc;
+}
+
+int validate_append(const void *k_new, const void *v_new, const int32_t *token_seq, const int32_t *token_pos,
+                    int32_t num_tokens, const int32_t *page_table, int32_t max_pages_per_seq,
+                    const void *k_pool, const void *v_pool, int64_t num_pages, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+        return KVQ_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim || !valid_page_size(page_size)) return KVQ_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return KVQ_OK;
+    if (!k_new || !v_new || !token_seq || !token_pos || !page_table || !k_pool || !v_pool)
+        return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return KVQ_ERR_INVALID_ARG;
+    if ((int64_t)num_tokens * num_kv_heads * 2 / 16 + 1 >= 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+int validate_decode(const void *q, const void *k_pool, const void *v_pool, int64_t num_pages,
+                    const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                    int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, const float *out) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
+        num_pages <= 0 || max_context_len < 0)
+        return KVQ_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads) return KVQ_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim || !valid_page_size(page_size)) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * page_size) return KVQ_ERR_INVALID_ARG;
+    if (batch == 0) return KVQ_OK;
+    if (!q || !k_pool || !v_pool || !page_table || !context_lens || !out) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
+    if (batch > 65535) return KVQ_ERR_UNSUPPORTED;   // grid.z limit
+    return KVQ_OK;
+}
+
+int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *v_pool, int64_t num_pages,
+                  const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                  int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale, float *out,
+                  void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *stream) {
+    int rc = validate_decode(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
+                             max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, out);
+    if (rc != KVQ_OK) return rc;
+    if (int4 && !valid_had_block(had_block)) return KVQ_ERR_UNSUPPORTED;
+    if (pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
+    if (batch == 0) return KVQ_OK;
+    const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
+    int32_t pps = 0, nsplit = 0;
+    choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
+    if (nsplit > 65535 || (int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
+    const size_t need = workspace_bytes_for(batch, num_q_heads, nsplit);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_checks_enabled()) {
+        rc = check_decode_indices(page_table, max_pages_per_seq, context_lens, batch, max_context_len, num_pages,
+                                  page_size, st);
+        if (rc != KVQ_OK) return rc;
+    }
+    kvq::DecodeArgs a{};
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.page_table = page_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * nsplit * kHeadDim;
+    a.tile_bytes = int4 ? (int64_t)kvq_page_tile_bytes(head_dim, page_size) : (int64_t)page_size * head_dim * 2;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.head_chunks = chunks;
+    a.page_size = page_size;
+    a.page_shift = log2i(page_size);
+    a.had_block = int4 ? had_block : 0;
+    a.pages_per_split = pps;
+    a.num_splits = nsplit;
+    a.score_scale = softmax_scale * 1.4426950408889634f;
+    hipError_t e = int4 ? kvq::launch_decode_int4(a, st) : kvq::launch_decode_fp16(a, st);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+    if (g_phase_event && hipEventRecord(static_cast<hipEvent_t>(g_phase_event), st) != hipSuccess)
+        return KVQ_ERR_HIP;
+    e = kvq::launch_combine(a, int4 && had_block > 0, st);
+    return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_string(int status) {
+    switch (status) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_INVALID_ARG: return "invalid argument";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported head_dim, page_size, had_block or size";
+        case KVQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case KVQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t kvq_page_tile_bytes(int32_t head_dim, int32_t page_size) {
+    if (head_dim != kHeadDim || !valid_page_size(page_size)) return 0;
+    return (size_t)page_size * (head_dim / 2) + 2 * (size_t)page_size;
+}
+
+int kv_quant_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *token_seq,
+                    const int32_t *token_pos, int32_t num_tokens, const int32_t *page_table,
+                    int32_t max_pages_per_seq, uint8_t *k_pool, uint8_t *v_pool, int64_t num_pages,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t had_block,
+                    void *stream) {
+    int rc = validate_append(k_new, v_new, token_seq, token_pos, num_tokens, page_table, max_pages_per_seq,
+                             k_pool, v_pool, num_pages, num_kv_heads, head_dim, page_size);
+    if (rc != KVQ_OK) return rc;
+    if (!valid_had_block(had_block)) return KVQ_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return KVQ_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_checks_enabled()) {
+        rc = check_append_indices(token_seq, token_pos, num_tokens, page_table, max_pages_per_seq, num_pages,
+                                  page_size, st);
+        if (rc != KVQ_OK) return rc;
+    }
+    kvq::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.token_seq = token_seq;
+    a.token_pos = token_pos;
+    a.page_table = page_table;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.tile_bytes = (int64_t)kvq_page_tile_bytes(head_dim, page_size);
+    a.num_tokens = num_tokens;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.num_kv_heads = num_kv_heads;
+    a.page_size = page_size;
+    a.page_shift = log2i(page_size);
+    a.had_block = had_block;
+    return kvq::launch_quant_append(a, st) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new, const int32_t *token_seq,
+                   const int32_t *token_pos, int32_t num_tokens, const int32_t *page_table,
+                   int32_t max_pages_per_seq, uint16_t *k_pool, uint16_t *v_pool, int64_t num_pages,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size, void *stream) {
+    int rc = validate_append(k_new, v_new, token_seq, token_pos, num_tokens, page_table, max_pages_per_seq,
+                             k_pool, v_pool, num_pages, num_kv_heads, head_dim, page_size);
+    if (rc != KVQ_OK) return rc;
+    if (num_tokens == 0) return KVQ_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_checks_enabled()) {
+        rc = check_append_indices(token_seq, token_pos, num_tokens, page_table, max_pages_per_seq, num_pages,
+                                  page_size, st);
+        if (rc != KVQ_OK) return rc;
+    }
+    kvq::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.token_seq = token_seq;
+    a.token_pos = token_pos;
+    a.page_table = page_table;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.tile_bytes = (int64_t)page_size * head_dim * 2;
+    a.num_tokens = num_tokens;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.num_kv_heads = num_kv_heads;
+    a.page_size = page_size;
+    a.page_shift = log2i(page_size);
+    a.had_block = 0;
+    return kvq::launch_append_fp16(a, st) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_context_len, int32_t page_size,
+                                         int32_t pages_per_split) {
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        head_dim != kHeadDim || !valid_page_size(page_size) || pages_per_split < 0 || max_context_len < 0)
+        return 0;
+    int32_t pps = 0, nsplit = 0;
+    choose_split(batch, num_kv_heads, head_chunks_of(num_q_heads, num_kv_heads), max_context_len, page_size,
+                 pages_per_split, &pps, &nsplit);
+    return workspace_bytes_for(batch, num_q_heads, nsplit);
+}
+
+int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,
+                           const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                           int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale,
+                           float *out, void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                           void *stream) {
+    return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
+                         max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
+                         softmax_scale, out, workspace, workspace_bytes, pages_per_split, stream);
+}
+
+int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, int64_t num_pages,
+                           const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                           int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t page_size, float softmax_scale, float *out,
+                           void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *stream) {
+    return decode_common(false, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
+                         max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, 0, softmax_scale, out,
+                         workspace, workspace_bytes, pages_per_split, stream);
+}
+
+int kvq_set_decode_phase_event(void *event) {
+    g_phase_event = event;
+    return KVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI (kvq_api.hip) and the kernels.
+// Not installed; the public interface is include/kvq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;          // the only supported head dimension
+constexpr int kCodeBytesPerRow = kHeadDim / 2;
+constexpr int kHeadsPerChunk = 4;      // query heads handled together per KV head
+
+struct AppendArgs {
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    const int32_t *token_seq;
+    const int32_t *token_pos;
+    const int32_t *page_table;
+    void *k_pool;
+    void *v_pool;
+    int64_t tile_bytes;        // INT4: bytes per (page, head) tile; fp16: P*D*2
+    int32_t num_tokens;
+    int32_t max_pages_per_seq;
+    int32_t num_kv_heads;
+    int32_t page_size;
+    int32_t page_shift;        // log2(page_size)
+    int32_t had_block;
+};
+
+struct DecodeArgs {
+    const uint16_t *q;
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    float *out;
+    float *ws_o;               // [batch][num_q_heads][num_splits][kHeadDim]
+    float *ws_ml;              // [batch][num_q_heads][num_splits][2]  (max in log2 units, sum)
+    int64_t tile_bytes;
+    int32_t max_pages_per_seq;
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;             // num_q_heads / num_kv_heads
+    int32_t head_chunks;       // ceil(group / kHeadsPerChunk)
+    int32_t page_size;
+    int32_t page_shift;
+    int32_t had_block;
+    int32_t pages_per_split;
+    int32_t num_splits;
+    float score_scale;         // softmax_scale * log2(e): scores are kept in log2 units
+};
+
+hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_append_fp16(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_decode_int4(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_fp16(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream);
+
+}  // namespace kvq

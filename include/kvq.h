@@ -1,0 +1,209 @@
+/*
+ * kvq.h — C ABI of the MI355X (gfx950) INT4 KV-cache library.
+ *
+ * The library implements the serving-side hot path of token-wise INT4
+ * KV-cache quantization with a block-diagonal Hadamard rotation:
+ *   - kv_quant_append: for every new token, rotate its fp16 K and V per
+ *     block, quantize each (token, KV head) vector to INT4 with one fp16
+ *     scale, and write the result into a paged cache through a page table,
+ *     touching nothing else;
+ *   - paged_decode_attn_int4: one decode step of grouped-query attention over
+ *     that cache, dequantizing in registers; the query is rotated instead of
+ *     the keys, and the output is rotated back;
+ *   - kv_append_fp16 / paged_decode_attn_fp16: the same two operations on an
+ *     unquantized fp16 paged cache, as the baseline.
+ *
+ * Sources (cited by page title and section):
+ *   [EXPL] "KVキャッシュを4ビットへ — SAW-INT4とシステムを踏まえたINT4量子化"
+ *          (youngju.dev explainer of the SAW-INT4 preprint):
+ *          "KVキャッシュこそが本当のボトルネックである理由" — paged layout and fused
+ *          attention as serving constraints;
+ *          "素朴なINT4はなぜ崩れるのか" — token-wise INT4, one scale per token,
+ *          quantized on arrival and appended, past tokens never revisited;
+ *          "回転のトリック — ブロック対角アダマール" — orthogonal, invertible
+ *          Hadamard rotation applied within blocks;
+ *          "システムこそが設計である — 融合カーネル" and its figure — one fused
+ *          kernel: K,V fp16 -> block Hadamard -> token-wise INT4 -> append to
+ *          the paged KV block.
+ *   [SUMM] "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World
+ *          LLM Serving" (gist.science summary): the same method, compatible
+ *          with paged memory and fused attention.
+ *
+ * Conventions for every entry point
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     The caller allocates and frees every buffer; the library allocates
+ *     nothing and keeps no state between calls apart from the optional
+ *     timing hook kvq_set_decode_phase_event.  All entry points are
+ *     re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return; they never synchronize.
+ *   - Return value: KVQ_OK (0) on success, a negative KVQ_ERR_* code
+ *     otherwise.  Argument errors are detected on the host before anything is
+ *     launched, so a failing call has no effect.  KVQ_ERR_HIP reports a
+ *     launch failure from the HIP runtime.
+ *   - head_dim must be 128; page_size must be 16 or 32; had_block must be 0
+ *     (no rotation: naive INT4), 32, 64 or 128; num_q_heads must be a
+ *     multiple of num_kv_heads; pools and workspace must be 16-byte aligned.
+ *   - Device-side contract (not checked, because checking would need a
+ *     synchronisation): page_table entries that are read lie in
+ *     [0, num_pages); (seq, pos) pairs are unique within one append call;
+ *     context_lens[b] <= max_context_len <= max_pages_per_seq * page_size.
+ *
+ * Layouts
+ *   K/V input:      fp16 [num_tokens][num_kv_heads][head_dim] (row-major).
+ *   Query:          fp16 [batch][num_q_heads][head_dim].
+ *   Output:         fp32 [batch][num_q_heads][head_dim].
+ *   page_table:     int32 [batch][max_pages_per_seq]: logical page -> physical
+ *                   page; position pos of sequence b lives in logical page
+ *                   pos / page_size, slot pos % page_size.
+ *   INT4 pools:     uint8 [num_pages][num_kv_heads][tile], one pool for K and
+ *                   one for V, tile = page_size*head_dim/2 + 2*page_size bytes
+ *                   (1056 for P=16, 2112 for P=32): first page_size rows of
+ *                   head_dim/2 code bytes (two's-complement nibbles, element
+ *                   2j in the low nibble of byte j), then page_size
+ *                   little-endian fp16 scales.
+ *   fp16 pools:     fp16 [num_pages][num_kv_heads][page_size][head_dim].
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad combination */
+    KVQ_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / had_block outside the supported set */
+    KVQ_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+    KVQ_ERR_HIP = -4            /* the HIP runtime reported an error */
+};
+
+/* Static, human-readable text for a status code (host function). */
+const char *kvq_status_string(int status);
+
+/* Bytes of one (page, KV head) INT4 tile: page_size*head_dim/2 + 2*page_size.
+ * Returns 0 for unsupported arguments. */
+size_t kvq_page_tile_bytes(int32_t head_dim, int32_t page_size);
+
+/*
+ * kv_quant_append — fused rotate -> quantize -> paged append ([EXPL] figure
+ * in "システムこそが設計である — 融合カーネル"; token-wise scales from
+ * "素朴なINT4はなぜ崩れるのか"; block rotation from "回転のトリック").
+ *
+ * For each token t < num_tokens, each KV head h and each of K, V, with
+ * x = the fp16 row k_new[t][h][:] (resp. v_new):
+ *   1. y = fp32(x); if had_block > 0, each contiguous block of had_block
+ *      entries gets the unnormalised fast Walsh-Hadamard transform in the
+ *      fixed order of butterfly spans 1, 2, 4, ... (each butterfly
+ *      (u, v) -> (u + v, u - v) is one fp32 operation), then every entry is
+ *      multiplied by the fp32 value nearest 1/sqrt(had_block);
+ *   2. m = max |y|; scale s = fp16(m / 7) rounded to nearest even;
+ *   3. code_i = clamp(round-half-even(y_i / s), -8, 7) with IEEE division
+ *      (all codes 0 when s is 0);
+ *   4. the D/2 code bytes and s are written to slot token_pos[t] % page_size
+ *      of physical page page_table[token_seq[t]][token_pos[t] / page_size].
+ * The results are bit-exact with that definition.  No other byte of either
+ * pool changes.
+ *
+ *   k_new, v_new          fp16 [num_tokens][num_kv_heads][head_dim]
+ *   token_seq, token_pos  int32 [num_tokens]
+ *   page_table            int32 [*][max_pages_per_seq]
+ *   k_pool, v_pool        uint8 [num_pages][num_kv_heads][tile], written in place
+ * num_tokens == 0 is a no-op returning KVQ_OK.
+ */
+int kv_quant_append(const uint16_t *k_new, const uint16_t *v_new,
+                    const int32_t *token_seq, const int32_t *token_pos, int32_t num_tokens,
+                    const int32_t *page_table, int32_t max_pages_per_seq,
+                    uint8_t *k_pool, uint8_t *v_pool, int64_t num_pages,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                    int32_t had_block, void *stream);
+
+/*
+ * Workspace size for the decode entry points: partial softmax states of the
+ * split-K reduction, fp32.  `pages_per_split` = 0 lets the library choose
+ * (the same choice the decode call makes for the same arguments).
+ */
+size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t page_size,
+                                         int32_t pages_per_split);
+
+/*
+ * paged_decode_attn_int4 — one decode step of attention over the INT4 paged
+ * cache ([EXPL] "KVキャッシュこそが..." (paged layout, fused attention) and
+ * "回転のトリック" (the rotation R = H/sqrt(Bh) is orthogonal and its own
+ * inverse, so (R q).(R k) = q.k)).
+ *
+ * For sequence b, query head qh, KV head h = qh / (num_q_heads/num_kv_heads),
+ * L = context_lens[b]:
+ *   q' = R q (fp32), keys and values are code * scale read from the tiles,
+ *   z_j = softmax_scale * (q' . k_j), w = softmax(z) over j < L,
+ *   out[b][qh] = R (sum_j w_j v_j).
+ * L <= 0 gives a zero row.  had_block must be the value the cache was
+ * written with (0 = no rotation).  The work is split over page ranges
+ * ("split-K"); partial softmax states go to `workspace` and a second kernel
+ * merges them, so the result does not depend on the split beyond fp32
+ * rounding.
+ *
+ *   q              fp16 [batch][num_q_heads][head_dim]
+ *   k_pool, v_pool uint8 [num_pages][num_kv_heads][tile]
+ *   page_table     int32 [batch][max_pages_per_seq]
+ *   context_lens   int32 [batch]
+ *   out            fp32 [batch][num_q_heads][head_dim]
+ *   workspace      >= paged_decode_attn_workspace_bytes(...) bytes of device memory
+ *   pages_per_split  0 = library's choice, else the number of pages per split
+ * batch == 0 is a no-op returning KVQ_OK.
+ */
+int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                           int64_t num_pages, const int32_t *page_table,
+                           int32_t max_pages_per_seq, const int32_t *context_lens,
+                           int32_t batch, int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                           int32_t had_block, float softmax_scale, float *out,
+                           void *workspace, size_t workspace_bytes,
+                           int32_t pages_per_split, void *stream);
+
+/*
+ * kv_append_fp16 — baseline append: copy each new token's fp16 K/V rows into
+ * fp16 pools [num_pages][num_kv_heads][page_size][head_dim] through the page
+ * table.  Same arguments and contract as kv_quant_append without had_block.
+ */
+int kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
+                   const int32_t *token_seq, const int32_t *token_pos, int32_t num_tokens,
+                   const int32_t *page_table, int32_t max_pages_per_seq,
+                   uint16_t *k_pool, uint16_t *v_pool, int64_t num_pages,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size, void *stream);
+
+/*
+ * paged_decode_attn_fp16 — baseline decode over fp16 pools: the same
+ * computation as paged_decode_attn_int4 with unquantized keys and values and
+ * no rotation.  Same arguments as paged_decode_attn_int4 without had_block.
+ */
+int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                           int64_t num_pages, const int32_t *page_table,
+                           int32_t max_pages_per_seq, const int32_t *context_lens,
+                           int32_t batch, int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                           float softmax_scale, float *out, void *workspace,
+                           size_t workspace_bytes, int32_t pages_per_split, void *stream);
+
+/*
+ * kvq_set_decode_phase_event — timing hook for benchmarks and profilers.
+ * When `event` (a hipEvent_t passed as void*) is non-NULL, every later call of
+ * a decode entry point records it on its stream right after the split-K
+ * partial kernel and before the combine kernel, so that the caller can time
+ * the two kernels separately with events recorded before and after the call.
+ * NULL switches the hook off.  This is the library's only process-wide
+ * setting; set it while no decode call is in flight.  Returns KVQ_OK.
+ */
+int kvq_set_decode_phase_event(void *event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

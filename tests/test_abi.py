@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvq.h declares, and rejects bad arguments on the host before any
+launch.  No call here reaches a kernel."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_kv_cache_quant_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    for must in ("kv_quant_append", "paged_decode_attn_int4", "kv_append_fp16",
+                 "paged_decode_attn_fp16", "paged_decode_attn_workspace_bytes",
+                 "kvq_page_tile_bytes", "kvq_status_string"):
+        assert must in names
+    assert set(names) == set(kvq.SIGNATURES), "binding signatures must cover the header exactly"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_tile_bytes():
+    assert kvq.status_string(kvq.KVQ_OK) == "ok"
+    assert "workspace" in kvq.status_string(kvq.KVQ_ERR_WORKSPACE)
+    assert kvq.page_tile_bytes(128, 16) == 1056
+    assert kvq.page_tile_bytes(128, 32) == 2112
+    assert kvq.page_tile_bytes(64, 16) == 0
+    assert kvq.page_tile_bytes(128, 8) == 0
+
+
+def test_workspace_query():
+    # 1 sequence, ctx 256, P 16 -> 16 pages; 8 KV heads -> 1 page per split
+    n = kvq.workspace_bytes(1, 32, 8, 256, 16)
+    assert n == 1 * 32 * 16 * (128 + 2) * 4
+    assert kvq.workspace_bytes(1, 32, 8, 256, 16, pages_per_split=4) == 32 * 4 * 130 * 4
+    assert kvq.workspace_bytes(0, 32, 8, 256, 16) == 0
+    assert kvq.workspace_bytes(1, 30, 8, 256, 16) == 0      # Hq not a multiple of Hkv
+    # long sequences are capped at 1024 tokens per split
+    assert kvq.workspace_bytes(256, 32, 8, 8193, 16) == 256 * 32 * 9 * 130 * 4
+
+
+FAKE = 0x1000  # an aligned, never-dereferenced address
+
+
+def _append(**kw):
+    a = dict(k=FAKE, v=FAKE, seq=FAKE, pos=FAKE, T=4, pt=FAKE, maxp=4, kp=FAKE, vp=FAKE, npages=8,
+             hkv=8, d=128, P=16, bh=64, stream=None)
+    a.update(kw)
+    return kvq.lib().kv_quant_append(a["k"], a["v"], a["seq"], a["pos"], a["T"], a["pt"], a["maxp"],
+                                     a["kp"], a["vp"], a["npages"], a["hkv"], a["d"], a["P"], a["bh"],
+                                     a["stream"])
+
+
+def test_append_host_validation_rejects_before_launch():
+    assert _append(d=64) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(P=8) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(bh=16) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(bh=256) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(k=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _append(kp=FAKE + 4) == kvq.KVQ_ERR_INVALID_ARG    # misaligned pool
+    assert _append(T=-1) == kvq.KVQ_ERR_INVALID_ARG
+    assert _append(hkv=0) == kvq.KVQ_ERR_INVALID_ARG
+    assert _append(T=0, k=None, v=None) == kvq.KVQ_OK          # empty call: no-op
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, npages=8, pt=FAKE, maxp=4, cl=FAKE, B=2, maxctx=64, hq=32, hkv=8,
+             d=128, P=16, bh=64, scale=0.088, out=FAKE, ws=FAKE, wsb=1 << 20, pps=0, stream=None)
+    a.update(kw)
+    return kvq.lib().paged_decode_attn_int4(a["q"], a["kp"], a["vp"], a["npages"], a["pt"], a["maxp"],
+                                            a["cl"], a["B"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["P"],
+                                            a["bh"], a["scale"], a["out"], a["ws"], a["wsb"], a["pps"],
+                                            a["stream"])
+
+
+def test_decode_host_validation_rejects_before_launch():
+    assert _decode(d=256) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(P=64) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(bh=48) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(hq=30) == kvq.KVQ_ERR_INVALID_ARG
+    assert _decode(maxctx=65) == kvq.KVQ_ERR_INVALID_ARG      # exceeds max_pages * P
+    assert _decode(q=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _decode(out=FAKE + 8) == kvq.KVQ_ERR_INVALID_ARG
+    assert _decode(ws=None) == kvq.KVQ_ERR_WORKSPACE
+    assert _decode(wsb=100) == kvq.KVQ_ERR_WORKSPACE
+    assert _decode(pps=-1) == kvq.KVQ_ERR_INVALID_ARG
+    assert _decode(B=0, q=None, out=None) == kvq.KVQ_OK       # empty batch: no-op
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kvq, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        kvq.lib()
+
+
+def test_binding_rejects_mis_shaped_pools_before_launch():
+    """A pool smaller than [num_pages][Hkv][tile] (or [num_pages][Hkv][P][D]
+    for fp16) is refused on the host, before any pointer reaches a kernel."""
+    import torch
+    k = torch.zeros((2, 8, 128), dtype=torch.float16)
+    idx = torch.zeros(2, dtype=torch.int32)
+    pt = torch.zeros((1, 4), dtype=torch.int32)
+    half_pool = torch.zeros((4, 8, 16, 64), dtype=torch.float16)     # last dim halved
+    with pytest.raises(ValueError, match="pools must"):
+        kvq.kv_append_fp16(k, k, idx, idx, pt, half_pool, half_pool, 16)
+    short_tile = torch.zeros((4, 8, 1024), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="pools must"):
+        kvq.kv_quant_append(k, k, idx, idx, pt, short_tile, short_tile, 16, 64)
+    q = torch.zeros((1, 32, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="pools must"):
+        kvq.paged_decode_attn_int4(q, short_tile, short_tile, pt, torch.zeros(1, dtype=torch.int32), 8, 16, 64,
+                                   0.088, 64)

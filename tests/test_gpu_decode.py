@@ -1,0 +1,113 @@
+"""GPU parity of paged_decode_attn_int4 / paged_decode_attn_fp16 with the
+fp64 oracle: max-abs error <= 2e-3 on the same cache (the GPU cache is first
+checked byte-for-byte against the oracle's own cache built from the same
+inputs), plus split-count invariance and edge cases."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_quant_amd as kvq
+import oracle
+import workloads as wl
+from gpu_util import ATOL, append_step, fp16_pools, int4_pools, prefill, say
+
+pytestmark = pytest.mark.gpu
+D = wl.HEAD_DIM
+
+
+def _int4_case(w: wl.Workload, dev, layer=0, had_block=None, pages_per_split=0, check_cache=True):
+    bh = w.had_block if had_block is None else had_block
+    kp, vp = int4_pools(w, dev)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    say(f"prefill {w.name} layer {layer} bh={bh}")
+    prefill(w, layer, dev, kp, vp, bh, host_pools=(hk, hv))
+    append_step(w, layer, dev, kp, vp, bh, host_pools=(hk, hv))
+    if check_cache:
+        assert np.array_equal(kp.cpu().numpy(), hk), "GPU K cache differs from the oracle's"
+        assert np.array_equal(vp.cpu().numpy(), hv), "GPU V cache differs from the oracle's"
+    q = w.query(layer, dev)
+    pt = torch.as_tensor(w.table(layer), device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    maxctx = int(max(w.context_lens.max(), 0))
+    say(f"decode {w.name} B={w.batch} maxctx={maxctx} pps={pages_per_split}")
+    out = kvq.paged_decode_attn_int4(q, kp, vp, pt, cl, w.num_kv_heads, w.page_size, bh, w.softmax_scale,
+                                     maxctx, pages_per_split=pages_per_split)
+    torch.cuda.synchronize()
+    want = oracle.paged_decode_attn_int4(q.cpu().numpy(), hk, hv, w.table(layer), w.context_lens,
+                                         w.num_kv_heads, w.page_size, bh, w.softmax_scale)
+    return out.cpu().numpy(), want, (kp, vp, q, pt, cl, maxctx, bh)
+
+
+def _assert_close(got, want, atol=ATOL):
+    err = np.max(np.abs(got.astype(np.float64) - want.astype(np.float64))) if got.size else 0.0
+    assert np.all(np.isfinite(got))
+    assert err <= atol, f"max-abs error {err:.3e} > {atol}"
+    return err
+
+
+def test_decode_c1(dev):
+    w = wl.c1()
+    got, want, _ = _int4_case(w, dev)
+    _assert_close(got, want)
+
+
+@pytest.mark.parametrize("page_size", [16, 32])
+@pytest.mark.parametrize("had_block", [0, 32, 64, 128])
+def test_decode_ragged_lengths(dev, had_block, page_size):
+    lens = [0, 1, 15, 16, 17, 100, 333, 64, 5]
+    w = wl.small(len(lens), lens, had_block, page_size, cfg_id=60 + had_block + page_size)
+    got, want, _ = _int4_case(w, dev)
+    _assert_close(got, want)
+    assert np.all(got[0] == 0), "a zero-length sequence gives a zero row"
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_gqa_groups(dev, group):
+    lens = [50, 200, 17]
+    w = wl.small(len(lens), lens, 64, 16, cfg_id=80 + group, num_kv_heads=2, num_q_heads=2 * group)
+    got, want, _ = _int4_case(w, dev)
+    _assert_close(got, want)
+
+
+def test_decode_split_invariance(dev):
+    lens = [700, 1500, 33]
+    w = wl.small(len(lens), lens, 128, 16, cfg_id=90)
+    got, want, (kp, vp, q, pt, cl, maxctx, bh) = _int4_case(w, dev)
+    _assert_close(got, want)
+    outs = []
+    for pps in (1, 3, 7, 64, 200):
+        o = kvq.paged_decode_attn_int4(q, kp, vp, pt, cl, w.num_kv_heads, w.page_size, bh, w.softmax_scale,
+                                       maxctx, pages_per_split=pps)
+        outs.append(o.cpu().numpy())
+    # Different splits only reorder fp32 sums: the differences scale with the
+    # output's magnitude (|o| reaches ~20 with the x20 outlier channels).
+    bound = 1e-5 * max(1.0, float(np.max(np.abs(got))))
+    for o in outs:
+        assert np.max(np.abs(o - got)) <= bound
+
+
+def test_decode_fp16_baseline(dev):
+    lens = [0, 1, 17, 300, 64]
+    w = wl.small(len(lens), lens, 0, 16, cfg_id=95)
+    kp, vp = fp16_pools(w, dev)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    prefill(w, 0, dev, kp, vp, 0, fp16=True, host_pools=(hk, hv))
+    append_step(w, 0, dev, kp, vp, 0, fp16=True, host_pools=(hk, hv))
+    q = w.query(0, dev)
+    out = kvq.paged_decode_attn_fp16(q, kp, vp, torch.as_tensor(w.page_table, device=dev),
+                                     torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, w.page_size,
+                                     w.softmax_scale, int(max(lens)))
+    torch.cuda.synchronize()
+    want = oracle.paged_decode_attn_fp16(q.cpu().numpy(), hk, hv, w.page_table, w.context_lens, w.num_kv_heads,
+                                         w.page_size, w.softmax_scale)
+    _assert_close(out.cpu().numpy(), want)
+
+
+def test_decode_rotation_off_matches_naive_oracle(dev):
+    """had_block = 0 is naive INT4: the same kernels with no rotation."""
+    lens = [120, 47]
+    w = wl.small(len(lens), lens, 0, 32, cfg_id=97)
+    got, want, _ = _int4_case(w, dev, had_block=0)
+    _assert_close(got, want)
