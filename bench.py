@@ -64,8 +64,8 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-DECODE_KERNEL_SRC = ("decode_valu.hip",)
-DECODE_KERNEL_NAME = "decode_partial_kernel<true>"
+DECODE_KERNEL_SRC = ("decode_mfma.hip",)
+DECODE_KERNEL_NAME = "decode_int4_mfma_kernel<64, 16>"
 
 
 def _traffic_from_profile(kernel_hash):

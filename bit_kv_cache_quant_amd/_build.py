@@ -21,6 +21,7 @@ SOURCES = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
     "decode_valu.hip": [],
+    "decode_mfma.hip": [],
     "combine.hip": [],
 }
 

@@ -31,6 +31,9 @@ void choose_split(int32_t batch, int32_t num_kv_heads, int32_t head_chunks, int3
         if (p > cap) p = cap;
         if (p < 1) p = 1;
     }
+    // A split is a whole number of 64-token chunks.
+    const int32_t chunk_pages = kvq::kChunkTokens / page_size;
+    p = ((p + chunk_pages - 1) / chunk_pages) * chunk_pages;
     *pps = p;
     *nsplit = (npages + p - 1) / p;
 }
@@ -185,7 +188,7 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.pages_per_split = pps;
     a.num_splits = nsplit;
     a.score_scale = softmax_scale * 1.4426950408889634f;
-    hipError_t e = int4 ? kvq::launch_decode_int4(a, st) : kvq::launch_decode_fp16(a, st);
+    hipError_t e = int4 ? kvq::launch_decode_int4_mfma(a, st) : kvq::launch_decode_fp16(a, st);
     if (e != hipSuccess) return KVQ_ERR_HIP;
     if (g_phase_event && hipEventRecord(static_cast<hipEvent_t>(g_phase_event), st) != hipSuccess)
         return KVQ_ERR_HIP;

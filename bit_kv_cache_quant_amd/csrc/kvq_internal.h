@@ -10,6 +10,7 @@ namespace kvq {
 constexpr int kHeadDim = 128;          // the only supported head dimension
 constexpr int kCodeBytesPerRow = kHeadDim / 2;
 constexpr int kHeadsPerChunk = 4;      // query heads handled together per KV head
+constexpr int kChunkTokens = 64;       // decode processes tokens in chunks of 64
 
 struct AppendArgs {
     const uint16_t *k_new;
@@ -55,6 +56,7 @@ struct DecodeArgs {
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_append_fp16(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_decode_int4(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fp16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream);
 

@@ -47,10 +47,13 @@ def test_status_strings_and_tile_bytes():
 
 
 def test_workspace_query():
-    # 1 sequence, ctx 256, P 16 -> 16 pages; 8 KV heads -> 1 page per split
+    # 1 sequence, ctx 256, P 16 -> 16 pages; a split is a whole number of
+    # 64-token chunks (4 pages of 16, 2 of 32)
     n = kvq.workspace_bytes(1, 32, 8, 256, 16)
-    assert n == 1 * 32 * 16 * (128 + 2) * 4
+    assert n == 1 * 32 * 4 * (128 + 2) * 4
     assert kvq.workspace_bytes(1, 32, 8, 256, 16, pages_per_split=4) == 32 * 4 * 130 * 4
+    assert kvq.workspace_bytes(1, 32, 8, 256, 16, pages_per_split=1) == 32 * 4 * 130 * 4
+    assert kvq.workspace_bytes(1, 32, 8, 256, 32, pages_per_split=1) == 32 * 4 * 130 * 4
     assert kvq.workspace_bytes(0, 32, 8, 256, 16) == 0
     assert kvq.workspace_bytes(1, 30, 8, 256, 16) == 0      # Hq not a multiple of Hkv
     # long sequences are capped at 1024 tokens per split
