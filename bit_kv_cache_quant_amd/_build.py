@@ -21,7 +21,8 @@ SOURCES = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
     "decode_valu.hip": [],
-    "decode_mfma.hip": [],
+    # MFMA results straight into VGPRs (no accumulator-register copies)
+    "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "combine.hip": [],
 }
 

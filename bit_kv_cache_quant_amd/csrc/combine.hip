@@ -6,70 +6,141 @@
 // rotated basis is brought back by applying R once more.  That is done after
 // the merge, since merging (a weighted sum) commutes with R.
 //
-// One 64-thread block per (sequence, query head); thread t owns dims t and
-// t + 64.  Partial state of split s: running max M_s (log2 units), running sum
-// l_s, unnormalised output o_s.  Merge: M = max M_s, l = sum l_s 2^(M_s - M),
+// Partial state of split s: running max M_s (log2 units), running sum l_s,
+// unnormalised output o_s.  Merge: M = max M_s, l = sum l_s 2^(M_s - M),
 // o = sum o_s 2^(M_s - M) / l.
+//
+// One wave merges one (sequence, query head): lane t owns dims 2t and 2t+1,
+// so the butterflies of the inverse FWHT are one in-register step (span 1)
+// and lane exchanges (spans 2..64); no LDS and no block barrier on that path.
+// With many splits per sequence (batch 1, long context) four waves share one
+// (sequence, head): each merges every fourth split, and the four partial
+// states are merged once more through LDS.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, int rotate_back) {
-    const int unit = blockIdx.x;                 // b * num_q_heads + qh
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// Merge splits s0, s0 + step, ... of one unit: returns (M, l) and o for dims
+// 2t, 2t + 1 (relative to M).
+__device__ __forceinline__ void merge_splits(const float *ml, const float *po, int nsplit, int s0, int step,
+                                             int t, float &M, float &lsum, float &o0, float &o1) {
+    float mloc = -INFINITY;
+    for (int s = s0 + t * step; s < nsplit; s += 64 * step) mloc = fmaxf(mloc, ml[2 * s]);
+    M = wave_max(mloc);
+    float lloc = 0.0f;
+    for (int s = s0 + t * step; s < nsplit; s += 64 * step) lloc = fmaf(ml[2 * s + 1], exp2f(ml[2 * s] - M), lloc);
+    lsum = wave_sum(lloc);
+    o0 = 0.0f;
+    o1 = 0.0f;
+#pragma unroll 8
+    for (int s = s0; s < nsplit; s += step) {
+        const float w = exp2f(ml[2 * s] - M);
+        const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)s * kHeadDim + 2 * t);
+        o0 = fmaf(v.x, w, o0);
+        o1 = fmaf(v.y, w, o1);
+    }
+}
+
+// Inverse rotation of 128 values held as (2t, 2t+1) by lane t, then store.
+__device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh, int t, float *out) {
+    if (bh > 0) {
+        float u = o0 + o1, v = o0 - o1;          // span 1: inside the lane
+        o0 = u;
+        o1 = v;
+        for (int span = 2; span < bh; span <<= 1) {
+            const int m = span >> 1;              // partner lane for dims 2t ^ span
+            const bool upper = (t & m) != 0;
+            const float p0 = __shfl_xor(o0, m);
+            const float p1 = __shfl_xor(o1, m);
+            o0 = upper ? (p0 - o0) : (o0 + p0);
+            o1 = upper ? (p1 - o1) : (o1 + p1);
+        }
+        const float c = rsqrtf(static_cast<float>(bh));
+        o0 *= c;
+        o1 *= c;
+    }
+    *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(o0, o1);
+}
+
+// WIDE = false: 4 units per block, one wave each.  WIDE = true: one unit per
+// block, 4 waves each merging every 4th split.
+template <bool WIDE>
+__global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a, int rotate_back) {
+    const int wave = threadIdx.x >> 6;
+    const int t = threadIdx.x & 63;
+    const int unit = WIDE ? blockIdx.x : blockIdx.x * kWaves + wave;   // b * num_q_heads + qh
+    if (unit >= a.batch * a.num_q_heads) return;
     const int b = unit / a.num_q_heads;
-    const int t = threadIdx.x;
     float *out = a.out + (int64_t)unit * kHeadDim;
     const int L = a.context_lens[b];
     if (L <= 0) {
-        out[t] = 0.0f;
-        out[t + 64] = 0.0f;
+        if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
         return;
     }
     const int npages = (L + a.page_size - 1) >> a.page_shift;
     const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
     const float *ml = a.ws_ml + (int64_t)unit * a.num_splits * 2;
     const float *po = a.ws_o + (int64_t)unit * a.num_splits * kHeadDim;
+    const int bh = rotate_back ? a.had_block : 0;
 
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-    float lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float f = exp2f(ml[2 * s] - M);
-        lsum = fmaf(ml[2 * s + 1], f, lsum);
-        o0 = fmaf(po[(int64_t)s * kHeadDim + t], f, o0);
-        o1 = fmaf(po[(int64_t)s * kHeadDim + t + 64], f, o1);
+    float M, lsum, o0, o1;
+    if constexpr (!WIDE) {
+        merge_splits(ml, po, nsplit, 0, 1, t, M, lsum, o0, o1);
+    } else {
+        merge_splits(ml, po, nsplit, wave, kWaves, t, M, lsum, o0, o1);
+        __shared__ float sm[kWaves], sl[kWaves];
+        __shared__ float so[kWaves][kHeadDim];
+        if (t == 0) {
+            sm[wave] = M;
+            sl[wave] = lsum;
+        }
+        so[wave][2 * t] = o0;
+        so[wave][2 * t + 1] = o1;
+        __syncthreads();
+        if (wave != 0) return;
+        M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        lsum = 0.0f;
+        o0 = 0.0f;
+        o1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = (sm[w] == -INFINITY) ? 0.0f : exp2f(sm[w] - M);
+            lsum = fmaf(sl[w], f, lsum);
+            o0 = fmaf(so[w][2 * t], f, o0);
+            o1 = fmaf(so[w][2 * t + 1], f, o1);
+        }
     }
     const float inv = 1.0f / lsum;
-    __shared__ float x[kHeadDim];
-    x[t] = o0 * inv;
-    x[t + 64] = o1 * inv;
-    const int bh = rotate_back ? a.had_block : 0;
-    if (bh > 0) {
-        __syncthreads();
-        for (int span = 1; span < bh; span <<= 1) {
-            // butterfly number t: lower index i has bit `span` clear
-            const int i = ((t / span) * 2 * span) + (t % span);
-            const float u = x[i], v = x[i + span];
-            __syncthreads();
-            x[i] = u + v;
-            x[i + span] = u - v;
-            __syncthreads();
-        }
-        const float c = rsqrtf(static_cast<float>(bh));
-        out[t] = x[t] * c;
-        out[t + 64] = x[t + 64] * c;
-    } else {
-        out[t] = x[t];
-        out[t + 64] = x[t + 64];
-    }
+    rotate_back_and_store(o0 * inv, o1 * inv, bh, t, out);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream) {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(64), 0, stream,
-                       a, rotate_back ? 1 : 0);
+    const int units = a.batch * a.num_q_heads;
+    // Many splits per sequence (long context, small batch): spread each unit's
+    // splits over 4 waves; otherwise one wave per unit.
+    if (a.num_splits >= 32) {
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, stream, a,
+                           rotate_back ? 1 : 0);
+    } else {
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
+                           stream, a, rotate_back ? 1 : 0);
+    }
     return hipGetLastError();
 }
 

@@ -24,17 +24,29 @@
 //         at -8 sum_d L (per row), so the integer result is exactly
 //         sum_d L_d c_d.
 //   p.v : the unnormalised weight times the value scale, P = p s_V, is
-//         written as a 28-bit unsigned fixed-point integer relative to the
+//         written as a 28-bit unsigned fixed-point integer F relative to the
 //         largest P of the head in the 64-token chunk, split the same way
-//         into four 7-bit limbs (again one row per (head, limb)); values
-//         enter as sign-extended int8 codes.
+//         into four 7-bit limbs (again one row per (head, limb)).  Values
+//         also enter as offset-binary nibbles u = c + 8; the MFMA gives
+//         sum_t F_t u_t exactly, and 8 sum_t F_t (one number per head and
+//         chunk) is subtracted in fp32.
 // Limbs are recombined with integer shifts (exact) and one fp32 fma.  The
-// only approximations are the 2^-28 relative roundings of q' and P and fp32
-// accumulation, far inside the 2e-3 tolerance.
+// approximations are the 2^-28 relative roundings of q' and P, and fp32
+// rounding of the accumulation and of the offset subtraction (relative
+// error ~1e-6), far inside the 2e-3 tolerance.
 //
-// Layout of one wave (64 lanes, g = lane / 16, j = lane % 16), per chunk of
-// 64 tokens (4 groups t of 16 tokens; a group is one page of 16 tokens or
-// half a page of 32):
+// Work decomposition: one wave owns one work item (sequence, KV head, 4 of
+// its query heads, a page range of at most 1024 tokens) and walks it in
+// chunks of 64 tokens, loading chunk c+1 while it computes chunk c.  A block
+// holds the 4 waves of 4 KV heads of the same sequence and page range: they
+// read adjacent tiles of the same pages (DRAM locality) and share nothing but
+// LDS space.  The grid is ordered page-range-major (blockIdx.y): every
+// sequence's first range is dispatched before any second range, so the short
+// and partial ranges of long sequences come last instead of forming a tail.
+//
+// Layout of one wave (64 lanes, g = lane / 16, j = lane % 16), per chunk
+// (4 groups t of 16 tokens; a group is one page of 16 tokens or half a page
+// of 32):
 //   q.k  A (query limbs): lane row j = (head j/4, limb j%4), k-slots of lane
 //        group g = dims 32g + 2e (MFMA 0) and 32g + 2e + 1 (MFMA 1), e < 16.
 //        B (keys): lane column j = token j of the group; the lane's 16-byte
@@ -49,11 +61,12 @@
 //        1 KiB of LDS; lane (g, j) reads back the 16 tokens of group g for
 //        head j/4 and keeps limb j%4 (A operand of p.v).
 //   p.v  B (values): lane column j = dims 8j..8j+7 of MFMA m (dim 8j+m),
-//        k-slots = the 16 tokens of group g: one dword load per token,
-//        sign-extended to bytes and byte-transposed in registers.
+//        k-slots = the 16 tokens of group g.  Values are loaded like keys,
+//        16 bytes per lane (1 KiB per instruction), written to LDS and read
+//        back by column (dword j of the 16 rows of group g), then split into
+//        nibble bytes and byte-transposed in registers.
+//   All cache bytes are read with non-temporal 16-byte loads.
 //        D: lane (g, j) gets rows (head g, limbs 0..3) for dim 8j+m.
-// A block of 4 waves owns one work item (sequence, KV head, 4 query heads,
-// page range); waves take chunks round-robin and merge through LDS at the end.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -63,7 +76,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 64;            // tokens per chunk
+constexpr int kChunk = kChunkTokens;  // 64 tokens per chunk
 constexpr int kH = kHeadsPerChunk;    // 4 query heads
 
 __device__ __forceinline__ float half_to_float(uint32_t bits) {
@@ -73,6 +86,11 @@ __device__ __forceinline__ float half_to_float(uint32_t bits) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 // All-reduce inside each row of 16 lanes; every lane of the row gets the result.
@@ -92,29 +110,33 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Low / high nibbles of 8 two's-complement codes as offset-binary bytes (c + 8).
-__device__ __forceinline__ void split_offset(uint32_t w, uint32_t &lo, uint32_t &hi) {
-    const uint32_t x = w ^ 0x88888888u;
-    lo = x & 0x0F0F0F0Fu;
-    hi = (x >> 4) & 0x0F0F0F0Fu;
+__device__ __forceinline__ int row_sum16_i(int v) {
+    v += dpp_i<0xB1>(v);
+    v += dpp_i<0x4E>(v);
+    v += dpp_i<0x141>(v);
+    v += dpp_i<0x140>(v);
+    return v;
 }
 
-// Low / high nibbles of 8 two's-complement codes as sign-extended bytes.
-// For u = c + 8 in [0, 15]: (u + 0x78) stays below 0x100 per byte, and
-// xor 0x80 then gives u - 8 = c modulo 256.
-__device__ __forceinline__ void split_signed(uint32_t w, uint32_t &lo, uint32_t &hi) {
-    uint32_t l, h;
-    split_offset(w, l, h);
-    lo = (l + 0x78787878u) ^ 0x80808080u;
-    hi = (h + 0x78787878u) ^ 0x80808080u;
+// Orders LDS traffic between the lanes of one wave (no cross-wave sharing).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Low / high nibbles of 8 two's-complement codes as offset-binary bytes
+// (c + 8 = c xor 8 on 4 bits).  Each is one 3-input bitwise op on gfx950
+// (v_bitop3), plus one shift for the high nibbles.
+__device__ __forceinline__ void split_offset(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    lo = (w ^ 0x08080808u) & 0x0F0F0F0Fu;
+    hi = ((w >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
 }
 
 // 4x4 byte transpose: out[k] byte r = in[r] byte k.
 __device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0,
                                            uint32_t &o1, uint32_t &o2, uint32_t &o3) {
-    // v_perm_b32(x, y, sel): bytes 0-3 of the selector pick from y (0..3) and x (4..7).
+    // v_perm_b32(x, y, sel): selector bytes 0-3 pick bytes of y, 4-7 bytes of x.
     const uint32_t ab02 = __builtin_amdgcn_perm(b, a, 0x06020400u);  // a0 b0 a2 b2
     const uint32_t ab13 = __builtin_amdgcn_perm(b, a, 0x07030501u);  // a1 b1 a3 b3
     const uint32_t cd02 = __builtin_amdgcn_perm(d, c, 0x06020400u);  // c0 d0 c2 d2
@@ -129,28 +151,73 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Exact value of a (head, *) row group of 4 limb results: sum_r 2^(21-7r) D_r,
-// returned as fp32 (one rounding).
+// sum_r 2^(21-7r) D_r of one (head, limbs 0..3) row group, as fp32 (one rounding).
 __device__ __forceinline__ float limbs_to_float(v4i d) {
     const int hi = (d[0] << 7) + d[1];
     const int lo = (d[2] << 7) + d[3];
     return fmaf(static_cast<float>(hi), 16384.0f, static_cast<float>(lo));
 }
 
-struct Shared {
-    float q[kWaves][kH][kHeadDim];        // rotated queries (per wave, setup)
-    uint32_t pfix[kWaves][kH][kChunk];     // fixed-point P hand-off
-    float mo[kWaves][kH][kHeadDim];        // merge: unnormalised outputs
-    float mm[kWaves][kH];
-    float ml[kWaves][kH];
+// Value codes of one chunk pass through LDS to be read back by column: one
+// 16-token group is 16 rows x 64 bytes; groups sit 1088 bytes apart so that
+// a wave reading dword j of row e of all 4 groups hits 64 distinct banks.
+constexpr int kVGroupStride = 16 * kCodeBytesPerRow + 64;
+
+struct WaveShared {
+    uint32_t qlimb[kH][4][2][4][4];   // [head][limb][parity][lane group][dword]
+    uint32_t pfix[kH][kChunk];        // fixed-point P of the current chunk
+    uint8_t vtile[4 * kVGroupStride]; // value codes of the current chunk
 };
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load that does not allocate in the L1 cache: the cache is
+// read once per step, and on gfx950 this is the load shape that keeps enough
+// requests in flight to approach the HBM roofline on scattered 1 KiB tiles.
+__device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Raw cache bytes of one chunk, as loaded.
+struct ChunkData {
+    uint4 k[4];          // keys: group t, token j, dims 32g..32g+31
+    uint4 v[4];          // values: group t, bytes 16*lane .. 16*lane+15 of its 1 KiB of codes
+    uint32_t ks[4];      // key scale (fp16 bits) of group t, token j
+    uint32_t vs[4];      // value scale (fp16 bits) of group t, token j
+};
+
+template <int P>
+__device__ __forceinline__ void load_chunk(ChunkData &cd, const uint8_t *kpool, const uint8_t *vpool,
+                                           const int64_t (&tile_off)[4], const int (&slot0)[4], int lane) {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint8_t *kt = kpool + tile_off[t];
+        const uint8_t *vt = vpool + tile_off[t];
+        cd.k[t] = stream_load16(kt + (slot0[t] + j) * kCodeBytesPerRow + 16 * g);
+        cd.v[t] = stream_load16(vt + slot0[t] * kCodeBytesPerRow + 16 * lane);
+        cd.ks[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(kt + P * kCodeBytesPerRow + 2 * (slot0[t] + j)));
+        cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(vt + P * kCodeBytesPerRow + 2 * (slot0[t] + j)));
+    }
+}
 
 template <int BH, int P>
 __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a) {
-    const int s = blockIdx.x;
-    const int hk = blockIdx.y / a.head_chunks;
-    const int chunk_id = blockIdx.y - hk * a.head_chunks;
-    const int b = blockIdx.z;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    // blockIdx.x = (sequence, quad of head slots), blockIdx.y = page range;
+    // a head slot is (KV head, chunk of 4 of its query heads).
+    const int head_slots = a.num_kv_heads * a.head_chunks;
+    const int quads = (head_slots + kWaves - 1) / kWaves;
+    const int b = blockIdx.x / quads;
+    const int slot = (blockIdx.x - b * quads) * kWaves + wave;
+    if (slot >= head_slots) return;
+    const int hk = slot / a.head_chunks;
+    const int chunk_id = slot - hk * a.head_chunks;
+    const int s = blockIdx.y;
     const int L = a.context_lens[b];
     if (L <= 0) return;
     const int npages = (L + P - 1) / P;
@@ -161,171 +228,164 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     const int tok_end = min(p1 * P, L);
     const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
 
-    __shared__ Shared sh;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;
-    const int j = lane & 15;
+    __shared__ WaveShared shared_all[kWaves];
+    WaveShared &sh = shared_all[wave];
     const int qh0 = hk * a.group + chunk_id * kH;
     const int nheads = min(kH, a.group - chunk_id * kH);
 
-    // ---- setup: rotated query, fixed-point limbs, per-head score scale ----
+    // Physical pages of this range (at most 64): lane i holds page p0 + i.
+    const int32_t *pt = a.page_table + (int64_t)b * a.max_pages_per_seq;
+    const int my_page = (p0 + lane < p1) ? pt[p0 + lane] : 0;
+
+    // ---- setup: rotated query as fixed-point limbs; row g = head g ----
+    float qv[8];
     {
-        // lane loads 8 dims of one head: head lane/16, dims 8*(lane%16)..+7
-        const int hq = lane >> 4, d0 = (lane & 15) * 8;
-        float x[8];
+        const int hq = g;  // lane (g, j) holds dims 8j..8j+7 of head g
         if (hq < nheads) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * a.num_q_heads + qh0 + hq) * kHeadDim + d0);
-            x[0] = half_to_float(raw.x); x[1] = half_to_float(raw.x >> 16);
-            x[2] = half_to_float(raw.y); x[3] = half_to_float(raw.y >> 16);
-            x[4] = half_to_float(raw.z); x[5] = half_to_float(raw.z >> 16);
-            x[6] = half_to_float(raw.w); x[7] = half_to_float(raw.w >> 16);
+            const uint4 raw = *reinterpret_cast<const uint4 *>(
+                a.q + ((int64_t)b * a.num_q_heads + qh0 + hq) * kHeadDim + 8 * j);
+            qv[0] = half_to_float(raw.x); qv[1] = half_to_float(raw.x >> 16);
+            qv[2] = half_to_float(raw.y); qv[3] = half_to_float(raw.y >> 16);
+            qv[4] = half_to_float(raw.z); qv[5] = half_to_float(raw.z >> 16);
+            qv[6] = half_to_float(raw.w); qv[7] = half_to_float(raw.w >> 16);
         } else {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) x[r] = 0.0f;
+            for (int r = 0; r < 8; ++r) qv[r] = 0.0f;
         }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) sh.q[wave][hq][d0 + r] = x[r];
         if constexpr (BH > 0) {
-            // butterflies over the 128 dims of each head: 64 per head and stage,
-            // each lane doing 4 (one per head)
-            for (int span = 1; span < BH; span <<= 1) {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const int i = ((lane / span) * 2 * span) + (lane % span);
-                float u[kH], v[kH];
 #pragma unroll
-                for (int h = 0; h < kH; ++h) { u[h] = sh.q[wave][h][i]; v[h] = sh.q[wave][h][i + span]; }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int span = 1; span < 8; span <<= 1) {
 #pragma unroll
-                for (int h = 0; h < kH; ++h) { sh.q[wave][h][i] = u[h] + v[h]; sh.q[wave][h][i + span] = u[h] - v[h]; }
+                for (int r = 0; r < 8; ++r) {
+                    if (r & span) continue;
+                    const float u = qv[r], v = qv[r + span];
+                    qv[r] = u + v;
+                    qv[r + span] = u - v;
+                }
             }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    // Lane (g, j): row (head j/4, limb j%4); dims 32g..32g+31.
-    const int arow_head = j >> 2;
-    const int arow_limb = j & 3;
-    float qv[32];
-    float amax = 0.0f;
-    const float rot_scale = (BH > 0) ? rsqrtf(static_cast<float>(BH)) : 1.0f;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
-        qv[d] = sh.q[wave][arow_head][32 * g + d] * rot_scale;
-        amax = fmaxf(amax, fabsf(qv[d]));
+            for (int m = 1; m < BH / 8; m <<= 1) {
+                const bool upper = (j & m) != 0;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float p = __shfl_xor(qv[r], m, 16);
+                    qv[r] = upper ? (p - qv[r]) : (qv[r] + p);
+                }
+            }
+            const float c = rsqrtf(static_cast<float>(BH));
+#pragma unroll
+            for (int r = 0; r < 8; ++r) qv[r] *= c;
+        }
     }
-    // max over the head's 128 dims: lanes j, j+16, j+32, j+48 hold its 4 quarters
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(qv[r]));
+    amax = row_max16(amax);
     int qexp = 0;
     if (amax > 0.0f) (void)frexpf(amax, &qexp);      // amax < 2^qexp
     const float qmul = ldexpf(1.0f, 27 - qexp);
-    v4i qa0, qa1;        // A operands: MFMA 0 (even dims), MFMA 1 (odd dims)
-    int limb_sum = 0;    // sum over this lane's 32 dims of its limb
+    int lsum[4] = {0, 0, 0, 0};
     {
-        uint32_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
+        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int k = 0; k < 8; ++k) {
+            const int X = static_cast<int>(rintf(qv[k] * qmul));
+            const int limb[4] = {X >> 21, (X >> 14) & 127, (X >> 7) & 127, X & 127};
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int X = static_cast<int>(rintf(qv[2 * e + t] * qmul));
-                int limb;
-                if (arow_limb == 0) limb = X >> 21;
-                else limb = (X >> (21 - 7 * arow_limb)) & 127;
-                limb_sum += limb;
-                const uint32_t byte = static_cast<uint32_t>(limb) & 0xFFu;
-                if (t == 0) w0[e >> 2] |= byte << (8 * (e & 3));
-                else w1[e >> 2] |= byte << (8 * (e & 3));
+            for (int r = 0; r < 4; ++r) {
+                lsum[r] += limb[r];
+                w[r][k & 1] |= (static_cast<uint32_t>(limb[r]) & 0xFFu) << (8 * (k >> 1));
             }
         }
-        qa0 = v4i{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3]};
-        qa1 = v4i{(int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
-    }
-    // Sum of each row's limbs over all 128 dims (4 lane groups).
-    limb_sum += __shfl_xor(limb_sum, 16);
-    limb_sum += __shfl_xor(limb_sum, 32);
-    // Accumulator init for q.k: lane (g, j) holds rows (head g, limbs 0..3);
-    // row (g, r) is A-row 4g + r, whose total sits in lane 4g + r.
-    v4i qk_init;
+        // dim 8j + k sits at lane group j/4, slot 4 (j%4) + k/2 of parity k%2
 #pragma unroll
-    for (int r = 0; r < 4; ++r) qk_init[r] = -8 * __shfl(limb_sum, 4 * g + r);
-    // Score scale of head g (this lane's D rows): 2^(E_g - 27) * softmax_scale * log2(e)
-    const int qexp_g = __shfl(qexp, 4 * g);
-    const float score_mul = ldexpf(a.score_scale, qexp_g - 27);
+        for (int r = 0; r < 4; ++r) {
+            sh.qlimb[g][r][0][j >> 2][j & 3] = w[r][0];
+            sh.qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
+        }
+    }
+    v4i qk_init;    // rows (head g, limbs 0..3): -8 sum_d L, offset-binary keys
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
+    const float score_mul = ldexpf(a.score_scale, qexp - 27);   // head g
+    wave_lds_sync();
+    v4i qa0, qa1;   // A operands: row (head j/4, limb j%4), k-slots of group g
+    {
+        const uint4 e0 = *reinterpret_cast<const uint4 *>(&sh.qlimb[j >> 2][j & 3][0][g][0]);
+        const uint4 e1 = *reinterpret_cast<const uint4 *>(&sh.qlimb[j >> 2][j & 3][1][g][0]);
+        qa0 = v4i{(int)e0.x, (int)e0.y, (int)e0.z, (int)e0.w};
+        qa1 = v4i{(int)e1.x, (int)e1.y, (int)e1.z, (int)e1.w};
+    }
 
-    // ---- main loop over chunks ----
+    // ---- main loop: chunk c computed while chunk c+1 loads ----
     float m_run = -INFINITY;     // running max (log2 units) of head g, uniform in row g
     float l_lane = 0.0f;         // this lane's part of the running sum
     float o_acc[8];              // head g, dims 8j + m
 #pragma unroll
     for (int m = 0; m < 8; ++m) o_acc[m] = 0.0f;
 
-    const int32_t *pt = a.page_table + (int64_t)b * a.max_pages_per_seq;
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
     const int64_t head_off = (int64_t)hk * a.tile_bytes;
     const int64_t page_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
+    const int last_rel = p1 - 1 - p0;
 
-    for (int c = wave; c < nchunks; c += kWaves) {
-        const int T0 = tok_begin + c * kChunk;
-        // physical pages of the 4 groups (clamped to a valid page past the end)
+    auto load = [&](int c, ChunkData &cd) {
         int64_t tile_off[4];
         int slot0[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int tok = T0 + 16 * t;
-            const int lp = min(tok / P, npages - 1);
+            const int tok = tok_begin + c * kChunk + 16 * t;
+            const int rel = min(tok / P - p0, last_rel);        // clamp past the end
             slot0[t] = tok % P;
-            const int32_t phys = (int32_t)uniform((uint32_t)pt[lp]);
+            const int32_t phys = __builtin_amdgcn_readlane(my_page, rel);
             tile_off[t] = (int64_t)phys * page_stride + head_off;
         }
-        // loads: keys (16 B per lane and group), key and value scales, values
-        uint4 kraw[4];
-        float ks[4], vs[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint8_t *kt = kpool + tile_off[t];
-            const uint8_t *vt = vpool + tile_off[t];
-            kraw[t] = *reinterpret_cast<const uint4 *>(kt + (slot0[t] + j) * kCodeBytesPerRow + 16 * g);
-            ks[t] = half_to_float(*reinterpret_cast<const uint16_t *>(kt + P * kCodeBytesPerRow + 2 * (slot0[t] + j)));
-            vs[t] = half_to_float(*reinterpret_cast<const uint16_t *>(vt + P * kCodeBytesPerRow + 2 * (slot0[t] + j)));
-        }
-        uint32_t vraw[16];
-        {
-            // lane (g, j): group g's 16 tokens, dims 8j..8j+7 (dword j of each row)
-            int64_t toff = 0;
-            int sl = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (g == t) { toff = tile_off[t]; sl = slot0[t]; }
-            }
-            const uint8_t *vt = vpool + toff + sl * kCodeBytesPerRow + 4 * j;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) vraw[e] = *reinterpret_cast<const uint32_t *>(vt + e * kCodeBytesPerRow);
-        }
+        load_chunk<P>(cd, kpool, vpool, tile_off, slot0, lane);
+    };
 
-        // q.k for the 4 groups: z[t] = score of head g, token 16t + j (log2 units)
+    auto compute = [&](int c, ChunkData &cd) {
+        const int T0 = tok_begin + c * kChunk;
+        // Values to LDS first: the column read-back and nibble transposes do
+        // not depend on the softmax, so their latency overlaps the q.k work.
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            *reinterpret_cast<uint4 *>(&sh.vtile[t * kVGroupStride + 16 * lane]) = cd.v[t];
+
+        // q.k: z[t] = score of head g, token 16t + j (log2 units)
         float z[4];
         float zmax = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             uint32_t lo[4], hi[4];
-            split_offset(kraw[t].x, lo[0], hi[0]);
-            split_offset(kraw[t].y, lo[1], hi[1]);
-            split_offset(kraw[t].z, lo[2], hi[2]);
-            split_offset(kraw[t].w, lo[3], hi[3]);
+            split_offset(cd.k[t].x, lo[0], hi[0]);
+            split_offset(cd.k[t].y, lo[1], hi[1]);
+            split_offset(cd.k[t].z, lo[2], hi[2]);
+            split_offset(cd.k[t].w, lo[3], hi[3]);
             v4i d = mfma(qa0, v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]}, qk_init);
             d = mfma(qa1, v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}, d);
-            const int tok = T0 + 16 * t + j;
-            const float sc = limbs_to_float(d) * score_mul * ks[t];
-            z[t] = (tok < tok_end) ? sc : -INFINITY;
+            const bool valid = T0 + 16 * t + j < tok_end;
+            const float sc = limbs_to_float(d) * score_mul * half_to_float(cd.ks[t]);
+            z[t] = valid ? sc : -INFINITY;
             zmax = fmaxf(zmax, z[t]);
         }
+
+        // Value columns: lane (g, j) takes dword j (dims 8j..8j+7) of the 16
+        // rows of group g, then transposes the nibble words of 4 tokens at a
+        // time, so that vw[4 q4 + k] holds code byte k (dims 8j + 2k and
+        // 8j + 2k + 1) of tokens 4 q4 .. 4 q4 + 3.
+        wave_lds_sync();
+        uint32_t vw[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            vw[e] = *reinterpret_cast<const uint32_t *>(&sh.vtile[g * kVGroupStride + e * kCodeBytesPerRow + 4 * j]);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint32_t t0, t1, t2, t3;
+            transpose4(vw[4 * q4], vw[4 * q4 + 1], vw[4 * q4 + 2], vw[4 * q4 + 3], t0, t1, t2, t3);
+            vw[4 * q4] = t0; vw[4 * q4 + 1] = t1; vw[4 * q4 + 2] = t2; vw[4 * q4 + 3] = t3;
+        }
+
         // online softmax for head g (row g)
         zmax = row_max16(zmax);
         if (zmax > m_run) {
@@ -341,8 +401,8 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         for (int t = 0; t < 4; ++t) {
             const float p = exp2f(z[t] - m_run);          // 0 for masked tokens
             l_lane += p;
-            const int tok = T0 + 16 * t + j;
-            pv[t] = (tok < tok_end) ? p * vs[t] : 0.0f;   // masked scales may be garbage
+            const bool valid = T0 + 16 * t + j < tok_end;
+            pv[t] = valid ? p * half_to_float(cd.vs[t]) : 0.0f;   // masked scales may be garbage
             pmax = fmaxf(pmax, pv[t]);
         }
         pmax = row_max16(pmax);
@@ -350,19 +410,22 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         if (pmax > 0.0f) (void)frexpf(pmax, &pexp);        // pv < 2^pexp
         const float pmul = ldexpf(1.0f, 27 - pexp);
         const float pback = ldexpf(1.0f, pexp - 27);
+        float fsum = 0.0f;   // sum of this lane's fixed-point P (exact: < 2^29)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t F = static_cast<uint32_t>(fmaf(pv[t], pmul, 0.5f));
-            sh.pfix[wave][g][16 * t + j] = F;
+            sh.pfix[g][16 * t + j] = F;
+            fsum += static_cast<float>(F);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Values enter as offset-binary codes u = c + 8, so sum_t F_t c_t =
+        // sum_t F_t u_t - 8 sum_t F_t; the second term is one number per head.
+        const float corr = 8.0f * pback * row_sum16(fsum);
+        wave_lds_sync();
         // A operand of p.v: row (head j/4, limb j%4), tokens of group g
         v4i pa;
         {
-            const uint4 *src = reinterpret_cast<const uint4 *>(&sh.pfix[wave][arow_head][16 * g]);
-            const int shift = 21 - 7 * arow_limb;
+            const uint4 *src = reinterpret_cast<const uint4 *>(&sh.pfix[j >> 2][16 * g]);
+            const int shift = 21 - 7 * (j & 3);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const uint4 f = src[q4];
@@ -371,61 +434,52 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
                 pa[q4] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // B operands of p.v: sign-extended value codes, transposed to
-        // (dim 8j + m) x (16 tokens of group g)
-        uint32_t lo[16], hi[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) split_signed(vraw[e], lo[e], hi[e]);
-        // lo[e] bytes: dims 8j+0, +2, +4, +6 of token e; hi[e]: +1, +3, +5, +7
-        v4i vb[8];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            uint32_t t0, t1, t2, t3;
-            transpose4(lo[4 * q4], lo[4 * q4 + 1], lo[4 * q4 + 2], lo[4 * q4 + 3], t0, t1, t2, t3);
-            vb[0][q4] = (int)t0; vb[2][q4] = (int)t1; vb[4][q4] = (int)t2; vb[6][q4] = (int)t3;
-            transpose4(hi[4 * q4], hi[4 * q4 + 1], hi[4 * q4 + 2], hi[4 * q4 + 3], t0, t1, t2, t3);
-            vb[1][q4] = (int)t0; vb[3][q4] = (int)t1; vb[5][q4] = (int)t2; vb[7][q4] = (int)t3;
-        }
+        wave_lds_sync();
         const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const v4i d = mfma(pa, vb[m], zero);
-            o_acc[m] = fmaf(limbs_to_float(d), pback, o_acc[m]);
+        for (int k = 0; k < 4; ++k) {
+            v4i ve, vo;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint32_t lo, hi;
+                split_offset(vw[4 * q4 + k], lo, hi);
+                ve[q4] = (int)lo;
+                vo[q4] = (int)hi;
+            }
+            const v4i de = mfma(pa, ve, zero);
+            const v4i dd = mfma(pa, vo, zero);
+            o_acc[2 * k] = fmaf(limbs_to_float(de), pback, o_acc[2 * k]) - corr;
+            o_acc[2 * k + 1] = fmaf(limbs_to_float(dd), pback, o_acc[2 * k + 1]) - corr;
         }
+    };
+
+    // Two buffers used alternately: no register copies between chunks.  The
+    // prefetch is issued unconditionally (past the end it re-reads the last
+    // chunk, an L2 hit) so that the number of loads in flight is the same on
+    // every path and the wait before each compute covers only the older buffer.
+    ChunkData buf0, buf1;
+    load(0, buf0);
+    const int last = nchunks - 1;
+    for (int c = 0; c < nchunks; c += 2) {
+        load(min(c + 1, last), buf1);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of any use of buf0
+        compute(c, buf0);
+        if (c + 1 >= nchunks) break;
+        load(min(c + 2, last), buf0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c + 1, buf1);
     }
 
-    // ---- merge the 4 waves' states of this block ----
+    // ---- write this range's partial state ----
     const float l_row = row_sum16(l_lane);
-    if (j == 0) {
-        sh.mm[wave][g] = m_run;
-        sh.ml[wave][g] = l_row;
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) sh.mo[wave][g][8 * j + m] = o_acc[m];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kH * kHeadDim; idx += kThreads) {
-        const int h = idx / kHeadDim;
-        const int d = idx - h * kHeadDim;
-        if (h >= nheads) continue;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.mm[w][h]);
-        float acc = 0.0f, lsum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = (sh.mm[w][h] == -INFINITY) ? 0.0f : exp2f(sh.mm[w][h] - M);
-            acc = fmaf(sh.mo[w][h][d], f, acc);
-            lsum = fmaf(sh.ml[w][h], f, lsum);
-        }
-        const int64_t unit = ((int64_t)b * a.num_q_heads + qh0 + h) * a.num_splits + s;
-        a.ws_o[unit * kHeadDim + d] = acc;
-        if (d == 0) {
-            a.ws_ml[unit * 2 + 0] = M;
-            a.ws_ml[unit * 2 + 1] = lsum;
+    if (g < nheads) {
+        const int64_t unit = ((int64_t)b * a.num_q_heads + qh0 + g) * a.num_splits + s;
+        float4 *dst = reinterpret_cast<float4 *>(a.ws_o + unit * kHeadDim + 8 * j);
+        dst[0] = make_float4(o_acc[0], o_acc[1], o_acc[2], o_acc[3]);
+        dst[1] = make_float4(o_acc[4], o_acc[5], o_acc[6], o_acc[7]);
+        if (j == 0) {
+            a.ws_ml[unit * 2 + 0] = m_run;
+            a.ws_ml[unit * 2 + 1] = l_row;
         }
     }
 }
@@ -433,7 +487,8 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
 }  // namespace
 
 hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * a.head_chunks), (unsigned)a.batch);
+    const int quads = (a.num_kv_heads * a.head_chunks + kWaves - 1) / kWaves;
+    const dim3 grid((unsigned)(a.batch * quads), (unsigned)a.num_splits, 1);
     const dim3 block(kThreads);
 #define KVQ_LAUNCH(BHV, PV) hipLaunchKernelGGL((decode_int4_mfma_kernel<BHV, PV>), grid, block, 0, stream, a)
     if (a.page_size == 16) {

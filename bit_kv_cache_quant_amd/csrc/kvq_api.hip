@@ -16,22 +16,24 @@ bool valid_had_block(int32_t bh) { return bh == 0 || bh == 32 || bh == 64 || bh 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int log2i(int32_t v) { int s = 0; while ((1 << s) < v) ++s; return s; }
 
-// Split-K choice shared by the workspace query and the decode calls.
-// Aim for about 1024 work items so that all 256 compute units get several,
-// and cap a split at 1024 tokens so that long and short sequences balance.
+// Split-K choice shared by the workspace query and the decode calls.  One
+// split is one wave's work item.  Aim for about 2048 of them (two per SIMD)
+// when the batch alone does not provide that many; a split is a whole number
+// of 64-token chunks and at most 1024 tokens, so that long and short
+// sequences balance and a wave can hold its range's page-table entries one
+// per lane.  A caller's pages_per_split is rounded and capped the same way.
 void choose_split(int32_t batch, int32_t num_kv_heads, int32_t head_chunks, int32_t max_context_len,
                   int32_t page_size, int32_t pages_per_split, int32_t *pps, int32_t *nsplit) {
     const int32_t npages = max_context_len > 0 ? (max_context_len + page_size - 1) / page_size : 1;
     int32_t p = pages_per_split;
     if (p <= 0) {
         const int64_t items = (int64_t)batch * num_kv_heads * head_chunks;
-        const int64_t want = items >= 1024 ? 1 : (1024 + items - 1) / items;
+        const int64_t want = items >= 2048 ? 1 : (2048 + items - 1) / items;
         p = (int32_t)((npages + want - 1) / want);
-        const int32_t cap = 1024 / page_size;
-        if (p > cap) p = cap;
-        if (p < 1) p = 1;
     }
-    // A split is a whole number of 64-token chunks.
+    const int32_t cap = kvq::kMaxSplitTokens / page_size;
+    if (p > cap) p = cap;
+    if (p < 1) p = 1;
     const int32_t chunk_pages = kvq::kChunkTokens / page_size;
     p = ((p + chunk_pages - 1) / chunk_pages) * chunk_pages;
     *pps = p;
@@ -139,7 +141,7 @@ int validate_decode(const void *q, const void *k_pool, const void *v_pool, int64
     if (batch == 0) return KVQ_OK;
     if (!q || !k_pool || !v_pool || !page_table || !context_lens || !out) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
-    if (batch > 65535) return KVQ_ERR_UNSUPPORTED;   // grid.z limit
+    if ((int64_t)batch * num_kv_heads > (1ll << 30)) return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
 }
 
@@ -158,6 +160,7 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     int32_t pps = 0, nsplit = 0;
     choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
     if (nsplit > 65535 || (int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (!int4 && batch > 65535) return KVQ_ERR_UNSUPPORTED;   // fp16 kernel: batch is grid z
     const size_t need = workspace_bytes_for(batch, num_q_heads, nsplit);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
