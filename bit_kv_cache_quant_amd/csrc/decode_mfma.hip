@@ -15,25 +15,25 @@
 // token-head).  Both products are exact integer contractions once the fp32
 // operand is written in fixed point, so they map onto int8 MFMA:
 //
-//   q.k : the rotated, pre-scaled query of head hq is written as a 28-bit
-//         fixed-point integer X = round(q' 2^(27-E)), E the exponent of
-//         max|q'| of that head, split into limbs X = L0 2^21 + L1 2^14 +
-//         L2 2^7 + L3 (L0 signed, L1..L3 in [0,127]).  One MFMA row per
-//         (head, limb): 4 heads x 4 limbs fill the 16 rows.  Keys enter as
-//         offset-binary nibbles u = c + 8 in [0, 15]; the accumulator starts
-//         at -8 sum_d L (per row), so the integer result is exactly
-//         sum_d L_d c_d.
+//   q.k : the rotated, pre-scaled query of head hq is written as a 21-bit
+//         fixed-point integer X = round(q' 2^(20-E)), E the exponent of
+//         max|q'| of that head, split into limbs X = L0 2^14 + L1 2^7 + L2
+//         (L0 signed, L1, L2 in [0,127]).  One MFMA row per (head, limb):
+//         4 heads x 3 limbs use 12 of the 16 rows (the 4th limb row of each
+//         head is zero).  Keys enter as offset-binary nibbles u = c + 8 in
+//         [0, 15]; the accumulator starts at -8 sum_d L (per row), so the
+//         integer result is exactly sum_d L_d c_d.
 //   p.v : the unnormalised weight times the value scale, P = p s_V, is
-//         written as a 28-bit unsigned fixed-point integer F relative to the
+//         written as a 21-bit unsigned fixed-point integer F relative to the
 //         largest P of the head in the 64-token chunk, split the same way
-//         into four 7-bit limbs (again one row per (head, limb)).  Values
+//         into three 7-bit limbs (again one row per (head, limb)).  Values
 //         also enter as offset-binary nibbles u = c + 8; the MFMA gives
 //         sum_t F_t u_t exactly, and 8 sum_t F_t (one number per head and
 //         chunk) is subtracted in fp32.
-// Limbs are recombined with integer shifts (exact) and one fp32 fma.  The
-// approximations are the 2^-28 relative roundings of q' and P, and fp32
-// rounding of the accumulation and of the offset subtraction (relative
-// error ~1e-6), far inside the 2e-3 tolerance.
+// Limbs are recombined with integer shifts (exact, below 2^31) and one
+// conversion.  The approximations are the 2^-21 relative roundings of q' and
+// P, and fp32 rounding of the accumulation and of the offset subtraction
+// (relative error ~1e-6), far inside the 2e-3 tolerance.
 //
 // Work decomposition: one wave owns one work item (sequence, KV head, 4 of
 // its query heads, a page range of at most 1024 tokens) and walks it in
@@ -60,19 +60,21 @@
 //   P hand-off: each lane writes its fixed-point P (one dword per token) to
 //        1 KiB of LDS; lane (g, j) reads back the 16 tokens of group g for
 //        head j/4 and keeps limb j%4 (A operand of p.v).
-//   p.v  B (values): lane column j = dims 8j..8j+7 of MFMA m (dim 8j+m),
-//        k-slots = the 16 tokens of group g.  Values are loaded like keys,
-//        16 bytes per lane (1 KiB per instruction), written to LDS and read
-//        back by column (dword j of the 16 rows of group g), then split into
-//        nibble bytes and byte-transposed in registers.
+//   p.v  B (values): lane column j = dim 16m + j of MFMA m, k-slots = the
+//        16 tokens of group g.  Values are loaded like keys, 16 bytes per
+//        lane (1 KiB per instruction), written to LDS, and read back with
+//        gfx950's transposed 4-bit LDS read (ds_read_b64_tr_b4): one read
+//        gives a lane one dim of 16 tokens as 16 nibbles, which split into
+//        the operand's bytes with two bit operations each.
+//        D: lane (g, j) gets rows (head g, limbs) for dim 16m + j.
 //   All cache bytes are read with non-temporal 16-byte loads.
-//        D: lane (g, j) gets rows (head g, limbs 0..3) for dim 8j+m.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -151,17 +153,24 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// sum_r 2^(21-7r) D_r of one (head, limbs 0..3) row group, as fp32 (one rounding).
+// D0 2^14 + D1 2^7 + D2 of one (head, limbs 0..2) row group, exact in 32
+// bits (|D0| <= 2^16 for q.k; 0 <= D0 < 64*127*15 for p.v), then one rounding.
 __device__ __forceinline__ float limbs_to_float(v4i d) {
-    const int hi = (d[0] << 7) + d[1];
-    const int lo = (d[2] << 7) + d[3];
-    return fmaf(static_cast<float>(hi), 16384.0f, static_cast<float>(lo));
+    const int s = (((d[0] << 7) + d[1]) << 7) + d[2];
+    return static_cast<float>(s);
+}
+__device__ __forceinline__ float ulimbs_to_float(v4i d) {
+    const uint32_t s = (((static_cast<uint32_t>(d[0]) << 7) + static_cast<uint32_t>(d[1])) << 7) +
+                       static_cast<uint32_t>(d[2]);
+    return static_cast<float>(s);
 }
 
-// Value codes of one chunk pass through LDS to be read back by column: one
-// 16-token group is 16 rows x 64 bytes; groups sit 1088 bytes apart so that
-// a wave reading dword j of row e of all 4 groups hits 64 distinct banks.
-constexpr int kVGroupStride = 16 * kCodeBytesPerRow + 64;
+// Value codes of one chunk pass through LDS to be read back transposed: one
+// 16-token group is 16 rows of 64 code bytes, stored with an 80-byte row
+// pitch so that the 16 lanes of a transposed read (one 8-byte word from each
+// of the group's 16 rows) hit distinct banks.
+constexpr int kVRowPitch = 80;
+constexpr int kVGroupStride = 16 * kVRowPitch;
 
 struct WaveShared {
     uint32_t qlimb[kH][4][2][4][4];   // [head][limb][parity][lane group][dword]
@@ -283,16 +292,16 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     amax = row_max16(amax);
     int qexp = 0;
     if (amax > 0.0f) (void)frexpf(amax, &qexp);      // amax < 2^qexp
-    const float qmul = ldexpf(1.0f, 27 - qexp);
+    const float qmul = ldexpf(1.0f, 20 - qexp);
     int lsum[4] = {0, 0, 0, 0};
     {
-        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]
+        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]; limb 3 stays 0
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int X = static_cast<int>(rintf(qv[k] * qmul));
-            const int limb[4] = {X >> 21, (X >> 14) & 127, (X >> 7) & 127, X & 127};
+            const int limb[3] = {X >> 14, (X >> 7) & 127, X & 127};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 3; ++r) {
                 lsum[r] += limb[r];
                 w[r][k & 1] |= (static_cast<uint32_t>(limb[r]) & 0xFFu) << (8 * (k >> 1));
             }
@@ -304,10 +313,11 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
             sh.qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
         }
     }
-    v4i qk_init;    // rows (head g, limbs 0..3): -8 sum_d L, offset-binary keys
+    v4i qk_init;    // rows (head g, limbs 0..2, zero row): -8 sum_d L, offset-binary keys
 #pragma unroll
-    for (int r = 0; r < 4; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
-    const float score_mul = ldexpf(a.score_scale, qexp - 27);   // head g
+    for (int r = 0; r < 3; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
+    qk_init[3] = 0;
+    const float score_mul = ldexpf(a.score_scale, qexp - 20);   // head g
     wave_lds_sync();
     v4i qa0, qa1;   // A operands: row (head j/4, limb j%4), k-slots of group g
     {
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     // ---- main loop: chunk c computed while chunk c+1 loads ----
     float m_run = -INFINITY;     // running max (log2 units) of head g, uniform in row g
     float l_lane = 0.0f;         // this lane's part of the running sum
-    float o_acc[8];              // head g, dims 8j + m
+    float o_acc[8];              // head g, dims 16m + j
 #pragma unroll
     for (int m = 0; m < 8; ++m) o_acc[m] = 0.0f;
 
@@ -346,11 +356,12 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
 
     auto compute = [&](int c, ChunkData &cd) {
         const int T0 = tok_begin + c * kChunk;
-        // Values to LDS first: the column read-back and nibble transposes do
-        // not depend on the softmax, so their latency overlaps the q.k work.
+        // Values to LDS first (row r = lane / 4, 16-byte part lane % 4): the
+        // transposed read-back does not depend on the softmax, so its latency
+        // overlaps the q.k work.
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            *reinterpret_cast<uint4 *>(&sh.vtile[t * kVGroupStride + 16 * lane]) = cd.v[t];
+            *reinterpret_cast<uint4 *>(&sh.vtile[t * kVGroupStride + (lane >> 2) * kVRowPitch + 16 * (lane & 3)]) = cd.v[t];
 
         // q.k: z[t] = score of head g, token 16t + j (log2 units)
         float z[4];
@@ -370,20 +381,16 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
             zmax = fmaxf(zmax, z[t]);
         }
 
-        // Value columns: lane (g, j) takes dword j (dims 8j..8j+7) of the 16
-        // rows of group g, then transposes the nibble words of 4 tokens at a
-        // time, so that vw[4 q4 + k] holds code byte k (dims 8j + 2k and
-        // 8j + 2k + 1) of tokens 4 q4 .. 4 q4 + 3.
+        // Value columns by transposed 4-bit LDS reads: lane (g, n) points at
+        // the 8-byte word m (dims 16m..16m+15) of token n of group g, and lane
+        // (g, i) receives dim 16m + i of the 16 tokens (token n in nibble n).
         wave_lds_sync();
-        uint32_t vw[16];
+        uint2 vt[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            vw[e] = *reinterpret_cast<const uint32_t *>(&sh.vtile[g * kVGroupStride + e * kCodeBytesPerRow + 4 * j]);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            uint32_t t0, t1, t2, t3;
-            transpose4(vw[4 * q4], vw[4 * q4 + 1], vw[4 * q4 + 2], vw[4 * q4 + 3], t0, t1, t2, t3);
-            vw[4 * q4] = t0; vw[4 * q4 + 1] = t1; vw[4 * q4 + 2] = t2; vw[4 * q4 + 3] = t3;
+        for (int m = 0; m < 8; ++m) {
+            const v2i r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(
+                &sh.vtile[g * kVGroupStride + j * kVRowPitch + 8 * m]));
+            vt[m] = make_uint2(static_cast<uint32_t>(r.x), static_cast<uint32_t>(r.y));
         }
 
         // online softmax for head g (row g)
@@ -408,9 +415,9 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         pmax = row_max16(pmax);
         int pexp = 0;
         if (pmax > 0.0f) (void)frexpf(pmax, &pexp);        // pv < 2^pexp
-        const float pmul = ldexpf(1.0f, 27 - pexp);
-        const float pback = ldexpf(1.0f, pexp - 27);
-        float fsum = 0.0f;   // sum of this lane's fixed-point P (exact: < 2^29)
+        const float pmul = ldexpf(1.0f, 20 - pexp);
+        const float pback = ldexpf(1.0f, pexp - 20);
+        float fsum = 0.0f;   // sum of this lane's fixed-point P (exact: < 2^23)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t F = static_cast<uint32_t>(fmaf(pv[t], pmul, 0.5f));
@@ -421,62 +428,52 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         // sum_t F_t u_t - 8 sum_t F_t; the second term is one number per head.
         const float corr = 8.0f * pback * row_sum16(fsum);
         wave_lds_sync();
-        // A operand of p.v: row (head j/4, limb j%4), tokens of group g
+        // A operand of p.v: row (head j/4, limb j%4; limb 3 is zero), tokens
+        // of group g in the k-slot order of the transposed value words:
+        // dword 0 = tokens 0,2,4,6; 1 = 1,3,5,7; 2 = 8,10,12,14; 3 = 9,11,13,15.
         v4i pa;
         {
             const uint4 *src = reinterpret_cast<const uint4 *>(&sh.pfix[j >> 2][16 * g]);
-            const int shift = 21 - 7 * (j & 3);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const uint4 f = src[q4];
-                const uint32_t b0 = (f.x >> shift) & 127u, b1 = (f.y >> shift) & 127u;
-                const uint32_t b2 = (f.z >> shift) & 127u, b3 = (f.w >> shift) & 127u;
-                pa[q4] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
-            }
+            const uint4 f0 = src[0], f1 = src[1], f2 = src[2], f3 = src[3];
+            const int limb = j & 3;
+            const int shift = 14 - 7 * limb;
+            const uint32_t mask = (limb == 3) ? 0u : 127u;
+            auto L = [&](uint32_t f) { return (f >> (shift & 31)) & mask; };
+            pa[0] = (int)(L(f0.x) | (L(f0.z) << 8) | (L(f1.x) << 16) | (L(f1.z) << 24));
+            pa[1] = (int)(L(f0.y) | (L(f0.w) << 8) | (L(f1.y) << 16) | (L(f1.w) << 24));
+            pa[2] = (int)(L(f2.x) | (L(f2.z) << 8) | (L(f3.x) << 16) | (L(f3.z) << 24));
+            pa[3] = (int)(L(f2.y) | (L(f2.w) << 8) | (L(f3.y) << 16) | (L(f3.w) << 24));
         }
         wave_lds_sync();
         const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v4i ve, vo;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                uint32_t lo, hi;
-                split_offset(vw[4 * q4 + k], lo, hi);
-                ve[q4] = (int)lo;
-                vo[q4] = (int)hi;
-            }
-            const v4i de = mfma(pa, ve, zero);
-            const v4i dd = mfma(pa, vo, zero);
-            o_acc[2 * k] = fmaf(limbs_to_float(de), pback, o_acc[2 * k]) - corr;
-            o_acc[2 * k + 1] = fmaf(limbs_to_float(dd), pback, o_acc[2 * k + 1]) - corr;
+        for (int m = 0; m < 8; ++m) {
+            // nibble n = token n -> bytes: tokens (0,2,4,6) (1,3,5,7) (8,..,14) (9,..,15)
+            uint32_t e0, o0, e1, o1;
+            split_offset(vt[m].x, e0, o0);
+            split_offset(vt[m].y, e1, o1);
+            const v4i d = mfma(pa, v4i{(int)e0, (int)o0, (int)e1, (int)o1}, zero);
+            o_acc[m] = fmaf(ulimbs_to_float(d), pback, o_acc[m]) - corr;
         }
     };
 
-    // Two buffers used alternately: no register copies between chunks.  The
-    // prefetch is issued unconditionally (past the end it re-reads the last
-    // chunk, an L2 hit) so that the number of loads in flight is the same on
-    // every path and the wait before each compute covers only the older buffer.
-    ChunkData buf0, buf1;
-    load(0, buf0);
-    const int last = nchunks - 1;
-    for (int c = 0; c < nchunks; c += 2) {
-        load(min(c + 1, last), buf1);
-        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of any use of buf0
-        compute(c, buf0);
-        if (c + 1 >= nchunks) break;
-        load(min(c + 2, last), buf0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(c + 1, buf1);
+    // Load then compute, one chunk at a time: with the footprint this small,
+    // five waves fit per SIMD and hide each other's memory latency.  (A
+    // register double buffer costs two waves per SIMD and its waits were
+    // measured to gain nothing.)
+    for (int c = 0; c < nchunks; ++c) {
+        ChunkData buf;
+        load(c, buf);
+        compute(c, buf);
     }
 
     // ---- write this range's partial state ----
     const float l_row = row_sum16(l_lane);
     if (g < nheads) {
         const int64_t unit = ((int64_t)b * a.num_q_heads + qh0 + g) * a.num_splits + s;
-        float4 *dst = reinterpret_cast<float4 *>(a.ws_o + unit * kHeadDim + 8 * j);
-        dst[0] = make_float4(o_acc[0], o_acc[1], o_acc[2], o_acc[3]);
-        dst[1] = make_float4(o_acc[4], o_acc[5], o_acc[6], o_acc[7]);
+        float *dst = a.ws_o + unit * kHeadDim + j;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dst[16 * m] = o_acc[m];
         if (j == 0) {
             a.ws_ml[unit * 2 + 0] = m_run;
             a.ws_ml[unit * 2 + 1] = l_row;
