@@ -36,13 +36,16 @@
 // (relative error ~1e-6), far inside the 2e-3 tolerance.
 //
 // Work decomposition: one wave owns one work item (sequence, KV head, 4 of
-// its query heads, a page range of at most 1024 tokens) and walks it in
-// chunks of 64 tokens, loading chunk c+1 while it computes chunk c.  A block
-// holds the 4 waves of 4 KV heads of the same sequence and page range: they
-// read adjacent tiles of the same pages (DRAM locality) and share nothing but
-// LDS space.  The grid is ordered page-range-major (blockIdx.y): every
-// sequence's first range is dispatched before any second range, so the short
-// and partial ranges of long sequences come last instead of forming a tail.
+// its query heads, a page range of at most 2048 tokens) and walks it in
+// chunks of 64 tokens.  A block holds the 4 waves of 4 KV heads of the same
+// sequence and page range: they read adjacent tiles of the same pages (DRAM
+// locality) and share nothing but LDS space.  The grid is ordered
+// page-range-major (blockIdx.y), aligned so that each sequence's last,
+// partial range sits at the highest blockIdx.y: whole ranges are dispatched
+// first and the short remainders last (longest-first), so the launch does not
+// end on a few long ranges.  Ranges are long because every partial result
+// written back costs far more than its size in lost read bandwidth (writes
+// interleaved with the streaming reads).
 //
 // Layout of one wave (64 lanes, g = lane / 16, j = lane % 16), per chunk
 // (4 groups t of 16 tokens; a group is one page of 16 tokens or half a page
@@ -226,12 +229,16 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     if (slot >= head_slots) return;
     const int hk = slot / a.head_chunks;
     const int chunk_id = slot - hk * a.head_chunks;
-    const int s = blockIdx.y;
     const int L = a.context_lens[b];
     if (L <= 0) return;
     const int npages = (L + P - 1) / P;
+    // Page range s of this sequence.  Ranges are dispatched so that every
+    // sequence's last (partial) range has the highest blockIdx.y: full ranges
+    // start first and the short remainders fill the end of the launch.
+    const int nsplit_b = (npages + a.pages_per_split - 1) / a.pages_per_split;
+    const int s = (int)blockIdx.y - (a.num_splits - nsplit_b);
+    if (s < 0) return;
     const int p0 = s * a.pages_per_split;
-    if (p0 >= npages) return;
     const int p1 = min(p0 + a.pages_per_split, npages);
     const int tok_begin = p0 * P;
     const int tok_end = min(p1 * P, L);
@@ -242,9 +249,11 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     const int qh0 = hk * a.group + chunk_id * kH;
     const int nheads = min(kH, a.group - chunk_id * kH);
 
-    // Physical pages of this range (at most 64): lane i holds page p0 + i.
+    // Physical pages of this range (at most 128): lane i holds pages p0 + i
+    // and p0 + 64 + i.
     const int32_t *pt = a.page_table + (int64_t)b * a.max_pages_per_seq;
-    const int my_page = (p0 + lane < p1) ? pt[p0 + lane] : 0;
+    const int my_page_lo = (p0 + lane < p1) ? pt[p0 + lane] : 0;
+    const int my_page_hi = (p0 + 64 + lane < p1) ? pt[p0 + 64 + lane] : 0;
 
     // ---- setup: rotated query as fixed-point limbs; row g = head g ----
     float qv[8];
@@ -348,7 +357,8 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
             const int tok = tok_begin + c * kChunk + 16 * t;
             const int rel = min(tok / P - p0, last_rel);        // clamp past the end
             slot0[t] = tok % P;
-            const int32_t phys = __builtin_amdgcn_readlane(my_page, rel);
+            const int32_t phys = rel < 64 ? __builtin_amdgcn_readlane(my_page_lo, rel)
+                                          : __builtin_amdgcn_readlane(my_page_hi, rel - 64);
             tile_off[t] = (int64_t)phys * page_stride + head_off;
         }
         load_chunk<P>(cd, kpool, vpool, tile_off, slot0, lane);

@@ -19,9 +19,12 @@ int log2i(int32_t v) { int s = 0; while ((1 << s) < v) ++s; return s; }
 // Split-K choice shared by the workspace query and the decode calls.  One
 // split is one wave's work item.  Aim for about 2048 of them (two per SIMD)
 // when the batch alone does not provide that many; a split is a whole number
-// of 64-token chunks and at most 1024 tokens, so that long and short
-// sequences balance and a wave can hold its range's page-table entries one
-// per lane.  A caller's pages_per_split is rounded and capped the same way.
+// of 64-token chunks and at most 2048 tokens (a wave holds its range's
+// page-table entries in two registers, one entry per lane each).  Splits are
+// not made shorter than needed: each one writes a partial result, and those
+// writes, interleaved with the cache reads, cost far more read bandwidth
+// than their size.  A caller's pages_per_split is rounded and capped the
+// same way.
 void choose_split(int32_t batch, int32_t num_kv_heads, int32_t head_chunks, int32_t max_context_len,
                   int32_t page_size, int32_t pages_per_split, int32_t *pps, int32_t *nsplit) {
     const int32_t npages = max_context_len > 0 ? (max_context_len + page_size - 1) / page_size : 1;

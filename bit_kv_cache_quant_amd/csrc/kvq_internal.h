@@ -11,7 +11,7 @@ constexpr int kHeadDim = 128;          // the only supported head dimension
 constexpr int kCodeBytesPerRow = kHeadDim / 2;
 constexpr int kHeadsPerChunk = 4;      // query heads handled together per KV head
 constexpr int kChunkTokens = 64;       // decode processes tokens in chunks of 64
-constexpr int kMaxSplitTokens = 1024;  // longest page range one decode wave takes
+constexpr int kMaxSplitTokens = 2048;  // longest page range one decode wave takes
 
 struct AppendArgs {
     const uint16_t *k_new;

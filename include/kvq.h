@@ -156,7 +156,7 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   out            fp32 [batch][num_q_heads][head_dim]
  *   workspace      >= paged_decode_attn_workspace_bytes(...) bytes of device memory
  *   pages_per_split  0 = library's choice, else the number of pages per split,
- *                  rounded up to whole 64-token chunks and capped at 1024 tokens
+ *                  rounded up to whole 64-token chunks and capped at 2048 tokens
  * batch == 0 is a no-op returning KVQ_OK.
  */
 int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,

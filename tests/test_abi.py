@@ -56,8 +56,9 @@ def test_workspace_query():
     assert kvq.workspace_bytes(1, 32, 8, 256, 32, pages_per_split=1) == 32 * 4 * 130 * 4
     assert kvq.workspace_bytes(0, 32, 8, 256, 16) == 0
     assert kvq.workspace_bytes(1, 30, 8, 256, 16) == 0      # Hq not a multiple of Hkv
-    # long sequences are capped at 1024 tokens per split
-    assert kvq.workspace_bytes(256, 32, 8, 8193, 16) == 256 * 32 * 9 * 130 * 4
+    # long sequences are capped at 2048 tokens per split
+    assert kvq.workspace_bytes(256, 32, 8, 8193, 16) == 256 * 32 * 5 * 130 * 4
+    assert kvq.workspace_bytes(256, 32, 8, 8193, 16, pages_per_split=1000) == 256 * 32 * 5 * 130 * 4
 
 
 FAKE = 0x1000  # an aligned, never-dereferenced address
