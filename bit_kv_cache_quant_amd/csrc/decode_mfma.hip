@@ -199,24 +199,34 @@ struct ChunkData {
     uint32_t vs[4];      // value scale (fp16 bits) of group t, token j
 };
 
+// Address of tile (page phys) in a pool: base + phys * stride (wave-uniform).
+__device__ __forceinline__ const uint8_t *tile_addr(const uint8_t *base, uint32_t phys, uint32_t stride) {
+    return base + (uint64_t)phys * stride;
+}
+
+// Loads of one chunk: group t is rows slot0(t) .. slot0(t)+15 of tile t.
 template <int P>
-__device__ __forceinline__ void load_chunk(ChunkData &cd, const uint8_t *kpool, const uint8_t *vpool,
-                                           const int64_t (&tile_off)[4], const int (&slot0)[4], int lane) {
-    const int g = lane >> 4, j = lane & 15;
+__device__ __forceinline__ void load_chunk(ChunkData &cd, const uint8_t *const (&kt)[4], const uint8_t *const (&vt)[4],
+                                           uint32_t koff, uint32_t voff, uint32_t soff) {
+    // Opaque copies: the 32-bit lane offsets are then extended next to the
+    // loads, which lets them take the scalar-base + 32-bit-offset form.
+    asm("" : "+v"(koff), "+v"(voff), "+v"(soff));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint8_t *kt = kpool + tile_off[t];
-        const uint8_t *vt = vpool + tile_off[t];
-        cd.k[t] = stream_load16(kt + (slot0[t] + j) * kCodeBytesPerRow + 16 * g);
-        cd.v[t] = stream_load16(vt + slot0[t] * kCodeBytesPerRow + 16 * lane);
-        cd.ks[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(kt + P * kCodeBytesPerRow + 2 * (slot0[t] + j)));
-        cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(vt + P * kCodeBytesPerRow + 2 * (slot0[t] + j)));
+        constexpr int kScaleBase = P * kCodeBytesPerRow;
+        const int slot0 = (16 * t) % P;
+        cd.k[t] = stream_load16(kt[t] + slot0 * kCodeBytesPerRow + koff);
+        cd.v[t] = stream_load16(vt[t] + slot0 * kCodeBytesPerRow + voff);
+        cd.ks[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(kt[t] + kScaleBase + 2 * slot0 + soff));
+        cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(vt[t] + kScaleBase + 2 * slot0 + soff));
     }
 }
 
 template <int BH, int P>
 __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a) {
-    const int wave = threadIdx.x >> 6;
+    // The wave index is uniform across the wave; saying so keeps everything
+    // derived from it (head, tile addresses) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int j = lane & 15;
@@ -345,23 +355,30 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
 
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
-    const int64_t head_off = (int64_t)hk * a.tile_bytes;
-    const int64_t page_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
+    // Both fit in 32 bits (the host checks num_kv_heads * tile_bytes < 2^31).
+    const uint32_t head_off = (uint32_t)hk * (uint32_t)a.tile_bytes;
+    const uint32_t page_stride = (uint32_t)a.num_kv_heads * (uint32_t)a.tile_bytes;
+    const uint8_t *kbase = kpool + head_off;
+    const uint8_t *vbase = vpool + head_off;
     const int last_rel = p1 - 1 - p0;
 
+    // Per-lane byte offsets inside a 16-token group: key row j, part g;
+    // value bytes 16 lane; scale of token j.
+    const uint32_t koff = j * kCodeBytesPerRow + 16 * g;
+    const uint32_t voff = 16 * lane;
+    const uint32_t soff = 2 * j;
+    // Chunk c starts at page p0 + c * 64 / P (ranges start on chunk boundaries).
     auto load = [&](int c, ChunkData &cd) {
-        int64_t tile_off[4];
-        int slot0[4];
+        const uint8_t *kt[4], *vt[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int tok = tok_begin + c * kChunk + 16 * t;
-            const int rel = min(tok / P - p0, last_rel);        // clamp past the end
-            slot0[t] = tok % P;
+            const int rel = min(c * (kChunk / P) + (16 * t) / P, last_rel);   // clamp past the end
             const int32_t phys = rel < 64 ? __builtin_amdgcn_readlane(my_page_lo, rel)
                                           : __builtin_amdgcn_readlane(my_page_hi, rel - 64);
-            tile_off[t] = (int64_t)phys * page_stride + head_off;
+            kt[t] = tile_addr(kbase, (uint32_t)phys, page_stride);
+            vt[t] = tile_addr(vbase, (uint32_t)phys, page_stride);
         }
-        load_chunk<P>(cd, kpool, vpool, tile_off, slot0, lane);
+        load_chunk<P>(cd, kt, vt, koff, voff, soff);
     };
 
     auto compute = [&](int c, ChunkData &cd) {
