@@ -71,6 +71,8 @@
 //        the operand's bytes with two bit operations each.
 //        D: lane (g, j) gets rows (head g, limbs) for dim 16m + j.
 //   All cache bytes are read with non-temporal 16-byte loads.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -105,6 +107,26 @@ __device__ __forceinline__ float row_max16(float v) {
     v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
     v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
     return v;
+}
+
+// Row max as an integer max (one DPP-fused instruction per step): float
+// order equals signed-integer order of the key b ^ ((b >> 31) & 0x7fffffff)
+// for all non-NaN floats, -inf included.
+__device__ __forceinline__ int row_max16_key(int k) {
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, true));
+    return k;
+}
+__device__ __forceinline__ float row_max16_fast(float v) {
+    const int b = __builtin_bit_cast(int, v);
+    const int k = row_max16_key(b ^ ((b >> 31) & 0x7fffffff));
+    return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff));
+}
+// For v >= 0 (no -0, no NaN) the bits themselves order like the values.
+__device__ __forceinline__ float row_max16_nonneg(float v) {
+    return __builtin_bit_cast(float, row_max16_key(__builtin_bit_cast(int, v)));
 }
 
 __device__ __forceinline__ float row_sum16(float v) {
@@ -158,13 +180,18 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
 
 // D0 2^14 + D1 2^7 + D2 of one (head, limbs 0..2) row group, exact in 32
 // bits (|D0| <= 2^16 for q.k; 0 <= D0 < 64*127*15 for p.v), then one rounding.
+// (Two shift-and-add instructions; the empty asm keeps the compiler from
+// re-associating them into three.)
 __device__ __forceinline__ float limbs_to_float(v4i d) {
-    const int s = (((d[0] << 7) + d[1]) << 7) + d[2];
+    int s = (d[0] << 7) + d[1];
+    asm("" : "+v"(s));
+    s = (s << 7) + d[2];
     return static_cast<float>(s);
 }
 __device__ __forceinline__ float ulimbs_to_float(v4i d) {
-    const uint32_t s = (((static_cast<uint32_t>(d[0]) << 7) + static_cast<uint32_t>(d[1])) << 7) +
-                       static_cast<uint32_t>(d[2]);
+    uint32_t s = (static_cast<uint32_t>(d[0]) << 7) + static_cast<uint32_t>(d[1]);
+    asm("" : "+v"(s));
+    s = (s << 7) + static_cast<uint32_t>(d[2]);
     return static_cast<float>(s);
 }
 
@@ -381,7 +408,9 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         load_chunk<P>(cd, kt, vt, koff, voff, soff);
     };
 
-    auto compute = [&](int c, ChunkData &cd) {
+    // TAIL: the chunk may extend past the range's last token (masked).
+    auto compute = [&](int c, ChunkData &cd, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
         const int T0 = tok_begin + c * kChunk;
         // Values to LDS first (row r = lane / 4, 16-byte part lane % 4): the
         // transposed read-back does not depend on the softmax, so its latency
@@ -402,9 +431,8 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
             split_offset(cd.k[t].w, lo[3], hi[3]);
             v4i d = mfma(qa0, v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]}, qk_init);
             d = mfma(qa1, v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}, d);
-            const bool valid = T0 + 16 * t + j < tok_end;
             const float sc = limbs_to_float(d) * score_mul * half_to_float(cd.ks[t]);
-            z[t] = valid ? sc : -INFINITY;
+            z[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? sc : -INFINITY;
             zmax = fmaxf(zmax, z[t]);
         }
 
@@ -421,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         }
 
         // online softmax for head g (row g)
-        zmax = row_max16(zmax);
+        zmax = row_max16_fast(zmax);
         if (zmax > m_run) {
             const float alpha = exp2f(m_run - zmax);
             l_lane *= alpha;
@@ -435,11 +463,11 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
         for (int t = 0; t < 4; ++t) {
             const float p = exp2f(z[t] - m_run);          // 0 for masked tokens
             l_lane += p;
-            const bool valid = T0 + 16 * t + j < tok_end;
-            pv[t] = valid ? p * half_to_float(cd.vs[t]) : 0.0f;   // masked scales may be garbage
+            // masked tokens: p = 0, but their scales may be garbage
+            pv[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? p * half_to_float(cd.vs[t]) : 0.0f;
             pmax = fmaxf(pmax, pv[t]);
         }
-        pmax = row_max16(pmax);
+        pmax = row_max16_nonneg(pmax);
         int pexp = 0;
         if (pmax > 0.0f) (void)frexpf(pmax, &pexp);        // pv < 2^pexp
         const float pmul = ldexpf(1.0f, 20 - pexp);
@@ -463,9 +491,9 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
             const uint4 *src = reinterpret_cast<const uint4 *>(&sh.pfix[j >> 2][16 * g]);
             const uint4 f0 = src[0], f1 = src[1], f2 = src[2], f3 = src[3];
             const int limb = j & 3;
-            const int shift = 14 - 7 * limb;
-            const uint32_t mask = (limb == 3) ? 0u : 127u;
-            auto L = [&](uint32_t f) { return (f >> (shift & 31)) & mask; };
+            const uint32_t shift = (limb == 3) ? 0u : 14u - 7u * limb;
+            const uint32_t width = (limb == 3) ? 0u : 7u;   // the zero row
+            auto L = [&](uint32_t f) { return __builtin_amdgcn_ubfe(f, shift, width); };
             pa[0] = (int)(L(f0.x) | (L(f0.z) << 8) | (L(f1.x) << 16) | (L(f1.z) << 24));
             pa[1] = (int)(L(f0.y) | (L(f0.w) << 8) | (L(f1.y) << 16) | (L(f1.w) << 24));
             pa[2] = (int)(L(f2.x) | (L(f2.z) << 8) | (L(f3.x) << 16) | (L(f3.z) << 24));
@@ -488,10 +516,16 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     // five waves fit per SIMD and hide each other's memory latency.  (A
     // register double buffer costs two waves per SIMD and its waits were
     // measured to gain nothing.)
-    for (int c = 0; c < nchunks; ++c) {
+    const int nfull = (tok_end - tok_begin) / kChunk;   // chunks with no masked token
+    for (int c = 0; c < nfull; ++c) {
         ChunkData buf;
         load(c, buf);
-        compute(c, buf);
+        compute(c, buf, std::false_type{});
+    }
+    if (nfull < nchunks) {
+        ChunkData buf;
+        load(nfull, buf);
+        compute(nfull, buf, std::true_type{});
     }
 
     // ---- write this range's partial state ----
