@@ -13,12 +13,20 @@
 // repeats it: no multiply-add may be fused unless written as fmaf.
 //
 // Mapping: 16 lanes own one 128-entry vector (one token, one KV head, K or V),
-// 8 consecutive entries per lane, loaded with one 16-byte load; 16 vectors per
-// 256-thread block, consecutive vectors being consecutive (token, head) rows,
-// so a wave reads 1 KiB of contiguous input.  Butterfly spans 1, 2, 4 are done
-// inside a lane, spans 8..64 between lanes (lane distance span/8).  Each lane
-// then produces exactly one 32-bit word of packed codes (its 8 nibbles), so
-// the 16 lanes write the 64 code bytes of the slot with one coalesced store.
+// 8 consecutive entries per lane, loaded with one 16-byte load.  A 256-thread
+// block takes 16 consecutive tokens of one (KV head, K or V): when those tokens
+// are consecutive positions of one sequence (a prefill append) their rows land
+// in consecutive slots of the same tile, so the block's code and scale stores
+// cover whole cache lines.  Butterfly spans 1, 2, 4 are done inside a lane,
+// spans 8..64 between lanes of the 16-lane row (lane distance span/8) with DPP
+// lane moves; the absmax is a DPP row reduction.  Each lane then produces one
+// 32-bit word of packed codes (its 8 nibbles), so the 16 lanes write the 64
+// code bytes of the slot with one coalesced store.
+//
+// Scale.  s32 = m / 7 is computed as q0 = m * r7, e = fma(-q0, 7, m),
+// q = fma(e, r7, q0) with r7 the fp32 value nearest 1/7; this equals the IEEE
+// quotient for every non-negative finite fp32 m (checked exhaustively, all
+// 2^31 - 2^23 values, zero mismatches).
 //
 // Division.  The quotient y / s must be the IEEE-rounded one, because rint of
 // it decides the code.  One correctly rounded reciprocal r = 1 / s is computed
@@ -29,6 +37,8 @@
 // quotient exponent in [2^-5, 2^5) (77 G cases, zero mismatches); smaller
 // quotients round to code 0 and larger ones clamp either way.  (Markstein's
 // correction step; the check replaces the general theorem's preconditions.)
+// Rounding to an integer is done by adding 1.5 * 2^23 (round-half-even at
+// unit spacing); the code is the low nibble of the sum's bits.
 #pragma clang fp contract(off)
 
 #include "kvq_internal.h"
@@ -39,6 +49,8 @@ namespace {
 constexpr int kLanesPerVec = 16;
 constexpr int kVecsPerBlock = 16;
 constexpr int kBlockThreads = kLanesPerVec * kVecsPerBlock;
+constexpr int kRowsPerGroup = 4;                                 // tokens per 16-lane row
+constexpr int kTokensPerBlock = kVecsPerBlock * kRowsPerGroup;   // 64
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
@@ -57,26 +69,47 @@ __device__ __forceinline__ float inv_sqrt_block() {
     else return __builtin_bit_cast(float, 0x3DB504F3u);
 }
 
+// Value of lane (i ^ mask) within this lane's row of 16, for mask 1, 2, 4, 8.
+template <int MASK>
+__device__ __forceinline__ float row_xor(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (MASK == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
+    else if constexpr (MASK == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    else if constexpr (MASK == 4)                                                          // (i ^ 7) ^ 3
+        r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true), 0x1B, 0xF, 0xF, true);
+    else r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);                           // row_ror:8
+    return __builtin_bit_cast(float, r);
+}
+
+// Butterfly span 8 * MASK: the lower-index lane keeps u + v, the other u - v.
+// Written as p + (+-1) y: the product is exact, so this is the same single
+// rounding as y + p (lower lane) or p - y (upper lane).
+template <int MASK>
+__device__ __forceinline__ void cross_span(float (&y)[8], int lane) {
+    const float sgn = (lane & MASK) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float p = row_xor<MASK>(y[r]);
+        y[r] = p + sgn * y[r];
+    }
+}
+
+// Max over the 16 lanes of the row of non-negative floats: their bit patterns
+// order like the values, so an integer max per DPP step.
+__device__ __forceinline__ float row_max_nonneg(float v) {
+    int k = __builtin_bit_cast(int, v);
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, k);
+}
+
+// Rotate and quantize one 128-entry vector held as 8 consecutive entries per
+// lane of a 16-lane row; returns the lane's 8 packed codes and the scale.
 template <int BH>
-__global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs a) {
-    const int lane = threadIdx.x & (kLanesPerVec - 1);
-    const int64_t vec = (int64_t)blockIdx.x * kVecsPerBlock + (threadIdx.x / kLanesPerVec);
-    const int64_t per_tensor = (int64_t)a.num_tokens * a.num_kv_heads;
-    if (vec >= 2 * per_tensor) return;  // the whole 16-lane group leaves together
-    const bool is_v = vec >= per_tensor;
-    const int64_t row = is_v ? vec - per_tensor : vec;
-    const int32_t t = (int32_t)(row / a.num_kv_heads);
-    const int32_t h = (int32_t)(row - (int64_t)t * a.num_kv_heads);
-
-    // Issue the address loads first; their latency overlaps the arithmetic.
-    const int32_t seq = a.token_seq[t];
-    const int32_t pos = a.token_pos[t];
-    const int32_t page = a.page_table[(int64_t)seq * a.max_pages_per_seq + (pos >> a.page_shift)];
-    const int32_t slot = pos & (a.page_size - 1);
-
-    const uint16_t *src = (is_v ? a.v_new : a.k_new) + row * kHeadDim + lane * 8;
-    const uint4 raw = *reinterpret_cast<const uint4 *>(src);
-
+__device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Float16 &s16_out) {
     float y[8];
     y[0] = half_bits_to_float(raw.x);
     y[1] = half_bits_to_float(raw.x >> 16);
@@ -100,18 +133,11 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
                 y[r + span] = u - v;
             }
         }
-        // Spans 8 .. BH/2: the partner entry sits in lane ^ (span / 8).  The
-        // lane holding the lower index keeps u + v, the other keeps u - v,
-        // where u is the lower-index entry (the partner's value there).
-#pragma unroll
-        for (int m = 1; m < BH / 8; m <<= 1) {
-            const bool upper = (lane & m) != 0;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float p = xor_lane16(y[r], m);
-                y[r] = upper ? (p - y[r]) : (y[r] + p);
-            }
-        }
+        // Spans 8 .. BH/2: the partner entry sits in lane ^ (span / 8).
+        if constexpr (BH >= 16) cross_span<1>(y, lane);
+        if constexpr (BH >= 32) cross_span<2>(y, lane);
+        if constexpr (BH >= 64) cross_span<4>(y, lane);
+        if constexpr (BH >= 128) cross_span<8>(y, lane);
         const float c = inv_sqrt_block<BH>();
 #pragma unroll
         for (int r = 0; r < 8; ++r) y[r] = y[r] * c;
@@ -121,10 +147,14 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(y[r]));
-#pragma unroll
-    for (int k = 1; k < kLanesPerVec; k <<= 1) m = fmaxf(m, xor_lane16(m, k));
+    m = row_max_nonneg(m);
 
-    const float s32 = m / 7.0f;                       // IEEE division
+    const float r7 = __builtin_bit_cast(float, 0x3E124925u);   // fp32 nearest 1/7
+    const float m0 = m * r7;
+    float s32 = __builtin_fmaf(__builtin_fmaf(-m0, 7.0f, m), r7, m0);   // == m / 7 (see header)
+    // The empty asm keeps the compiler from folding the fp16 conversion into
+    // the fma (one rounding to fp16 instead of fp32 then fp16: not the same).
+    asm("" : "+v"(s32));
     const _Float16 s16 = static_cast<_Float16>(s32);  // round to nearest even
     const float s = static_cast<float>(s16);
     float sd = s;
@@ -142,17 +172,53 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
         const float e = __builtin_fmaf(-q0, sd, y[r]);
         const float q = __builtin_fmaf(e, rcp, q0);  // == y / s (see header)
         // Clamping to integer bounds commutes with rounding to an integer.
-        const float qc = fminf(fmaxf(q, -8.0f), 7.0f);
-        const int code = static_cast<int>(rintf(qc));
-        word |= (static_cast<uint32_t>(code) & 0xFu) << (4 * r);
+        const float qc = __builtin_amdgcn_fmed3f(q, -8.0f, 7.0f);
+        const uint32_t bits = __builtin_bit_cast(uint32_t, qc + 12582912.0f);   // rint, in the low bits
+        word |= (bits & 0xFu) << (4 * r);
     }
+    s16_out = s16;
+    return word;
+}
 
+// A block covers kTokensPerBlock consecutive tokens of one (KV head, K or V);
+// its 16-lane row g takes tokens base + 16 i + g, i < kRowsPerGroup, so at
+// each step the 16 rows write 16 consecutive tokens.  All loads of a row's
+// tokens are issued before any of them is quantized.
+template <int BH>
+__global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs a) {
+    const int lane = threadIdx.x & (kLanesPerVec - 1);
+    const int group = threadIdx.x / kLanesPerVec;
+    const int32_t base = (int32_t)blockIdx.x * kTokensPerBlock + group;
+    const int32_t h = (int32_t)blockIdx.y;
+    const bool is_v = blockIdx.z != 0;
+    const uint16_t *src_base = (is_v ? a.v_new : a.k_new) + (int64_t)h * kHeadDim + lane * 8;
     uint8_t *pool = static_cast<uint8_t *>(is_v ? a.v_pool : a.k_pool);
-    uint8_t *tile = pool + ((int64_t)page * a.num_kv_heads + h) * a.tile_bytes;
-    *reinterpret_cast<uint32_t *>(tile + slot * kCodeBytesPerRow + lane * 4) = word;
-    if (lane == 0) {
-        *reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot) =
-            __builtin_bit_cast(uint16_t, s16);
+
+    uint4 raw[kRowsPerGroup];
+    int32_t page[kRowsPerGroup], slot[kRowsPerGroup];
+#pragma unroll
+    for (int i = 0; i < kRowsPerGroup; ++i) {
+        const int32_t t = base + kVecsPerBlock * i;
+        if (t < a.num_tokens) {
+            const int32_t seq = a.token_seq[t];
+            const int32_t pos = a.token_pos[t];
+            page[i] = a.page_table[(int64_t)seq * a.max_pages_per_seq + (pos >> a.page_shift)];
+            slot[i] = pos & (a.page_size - 1);
+            raw[i] = *reinterpret_cast<const uint4 *>(src_base + (int64_t)t * a.num_kv_heads * kHeadDim);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerGroup; ++i) {
+        const int32_t t = base + kVecsPerBlock * i;
+        if (t >= a.num_tokens) break;   // uniform across the 16-lane row
+        _Float16 s16;
+        const uint32_t word = quantize_row<BH>(raw[i], lane, s16);
+        uint8_t *tile = pool + ((int64_t)page[i] * a.num_kv_heads + h) * a.tile_bytes;
+        *reinterpret_cast<uint32_t *>(tile + slot[i] * kCodeBytesPerRow + lane * 4) = word;
+        if (lane == 0) {
+            *reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot[i]) =
+                __builtin_bit_cast(uint16_t, s16);
+        }
     }
 }
 
@@ -184,7 +250,7 @@ dim3 grid_for(const AppendArgs &a) {
 }  // namespace
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream) {
-    const dim3 grid = grid_for(a);
+    const dim3 grid((unsigned)((a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock), (unsigned)a.num_kv_heads, 2);
     switch (a.had_block) {
         case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kBlockThreads), 0, stream, a); break;
         case 32: hipLaunchKernelGGL(quant_append_kernel<32>, grid, dim3(kBlockThreads), 0, stream, a); break;
