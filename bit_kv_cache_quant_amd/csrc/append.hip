@@ -37,8 +37,8 @@
 // quotient exponent in [2^-5, 2^5) (77 G cases, zero mismatches); smaller
 // quotients round to code 0 and larger ones clamp either way.  (Markstein's
 // correction step; the check replaces the general theorem's preconditions.)
-// Rounding to an integer is done by adding 1.5 * 2^23 (round-half-even at
-// unit spacing); the code is the low nibble of the sum's bits.
+// Rounding to an integer is done by adding 1.5 * 2^23 + 8 (round-half-even at
+// unit spacing); the low byte of the sum's bits is then code + 8.
 #pragma clang fp contract(off)
 
 #include "kvq_internal.h"
@@ -49,8 +49,8 @@ namespace {
 constexpr int kLanesPerVec = 16;
 constexpr int kVecsPerBlock = 16;
 constexpr int kBlockThreads = kLanesPerVec * kVecsPerBlock;
-constexpr int kRowsPerGroup = 4;                                 // tokens per 16-lane row
-constexpr int kTokensPerBlock = kVecsPerBlock * kRowsPerGroup;   // 64
+constexpr int kRowsPerGroup = 2;                                 // tokens per 16-lane row
+constexpr int kTokensPerBlock = kVecsPerBlock * kRowsPerGroup;   // 32
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
@@ -69,15 +69,16 @@ __device__ __forceinline__ float inv_sqrt_block() {
     else return __builtin_bit_cast(float, 0x3DB504F3u);
 }
 
-// Value of lane (i ^ mask) within this lane's row of 16, for mask 1, 2, 4, 8.
+// Value of lane (i ^ mask) within this lane's row of 16, for mask 1, 2, 4, 8
+// (DPP lane moves; xor 4 uses the LDS crossbar's swizzle, without memory).
 template <int MASK>
 __device__ __forceinline__ float row_xor(float v) {
     const int x = __builtin_bit_cast(int, v);
     int r;
     if constexpr (MASK == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
     else if constexpr (MASK == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-    else if constexpr (MASK == 4)                                                          // (i ^ 7) ^ 3
-        r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true), 0x1B, 0xF, 0xF, true);
+    else if constexpr (MASK == 4)                                                          // no single DPP move:
+        r = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1F);                              // swizzle, xor 4
     else r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);                           // row_ror:8
     return __builtin_bit_cast(float, r);
 }
@@ -106,8 +107,16 @@ __device__ __forceinline__ float row_max_nonneg(float v) {
     return __builtin_bit_cast(float, k);
 }
 
-// Rotate and quantize one 128-entry vector held as 8 consecutive entries per
-// lane of a 16-lane row; returns the lane's 8 packed codes and the scale.
+// Lane <-> entries.  Lane l of a 16-lane row holds the 8 consecutive entries
+// of block e(l) = b0 + 2 b1 + 4 b3 + 8 b2 (b_i the bits of l), so butterfly
+// spans 8, 16, 32, 64 pair lanes l ^ 1, l ^ 2, l ^ 8, l ^ 4: with Bh <= 64
+// every exchange is a single DPP move.
+__device__ __forceinline__ int entry_block(int lane) {
+    return (lane & 3) | ((lane & 8) >> 1) | ((lane & 4) << 1);
+}
+
+// Rotate and quantize one 128-entry vector held as above; returns the lane's
+// 8 packed codes and the scale.
 template <int BH>
 __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Float16 &s16_out) {
     float y[8];
@@ -120,6 +129,10 @@ __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Flo
     y[6] = half_bits_to_float(raw.w);
     y[7] = half_bits_to_float(raw.w >> 16);
 
+    // 1/sqrt(Bh) is a power of two for Bh = 64: then y * c is exact, and
+    // scaling the absmax and the divisor instead of the 128 entries gives the
+    // same numbers (the quotient y c / s equals y / (s / c) exactly).
+    constexpr bool kExactScale = (BH == 64);
     if constexpr (BH > 0) {
         // Spans 1, 2, 4: both entries of a butterfly live in this lane.
 #pragma unroll
@@ -133,14 +146,16 @@ __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Flo
                 y[r + span] = u - v;
             }
         }
-        // Spans 8 .. BH/2: the partner entry sits in lane ^ (span / 8).
+        // Spans 8, 16, 32, 64 (see entry_block).
         if constexpr (BH >= 16) cross_span<1>(y, lane);
         if constexpr (BH >= 32) cross_span<2>(y, lane);
-        if constexpr (BH >= 64) cross_span<4>(y, lane);
-        if constexpr (BH >= 128) cross_span<8>(y, lane);
-        const float c = inv_sqrt_block<BH>();
+        if constexpr (BH >= 64) cross_span<8>(y, lane);
+        if constexpr (BH >= 128) cross_span<4>(y, lane);
+        if constexpr (!kExactScale) {
+            const float c = inv_sqrt_block<BH>();
 #pragma unroll
-        for (int r = 0; r < 8; ++r) y[r] = y[r] * c;
+            for (int r = 0; r < 8; ++r) y[r] = y[r] * c;
+        }
     }
 
     // Token-wise absmax over the 128 entries (exact).
@@ -148,6 +163,7 @@ __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Flo
 #pragma unroll
     for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(y[r]));
     m = row_max_nonneg(m);
+    if constexpr (kExactScale) m = m * inv_sqrt_block<BH>();
 
     const float r7 = __builtin_bit_cast(float, 0x3E124925u);   // fp32 nearest 1/7
     const float m0 = m * r7;
@@ -157,15 +173,25 @@ __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Flo
     asm("" : "+v"(s32));
     const _Float16 s16 = static_cast<_Float16>(s32);  // round to nearest even
     const float s = static_cast<float>(s16);
-    float sd = s;
+    float sd = 0.0f;     // divisor (zero scale: every code is 0)
     float rcp = 0.0f;
     if (s > 0.0f && s <= 65504.0f) {
-        rcp = 1.0f / s;                               // correctly rounded
-    } else {
-        sd = 0.0f;                                    // zero scale: every code is 0
+        // Correctly rounded 1/s: hardware reciprocal (1 ulp) and one Newton
+        // step; equal to IEEE 1/s for every positive finite fp16 s (checked
+        // on the device for all of them).
+        const float r0 = __builtin_amdgcn_rcpf(s);
+        rcp = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+        sd = s;
+        if constexpr (kExactScale) {
+            sd = s * 8.0f;              // s / c, exact
+            rcp = rcp * 0.125f;         // 1 / (s / c), exact
+        }
     }
 
-    uint32_t word = 0;
+    // Codes: exact quotient, clamp, round half to even by adding 1.5 * 2^23 + 8
+    // (the low byte of the sum is then code + 8 in [0, 15]); nibble pairs are
+    // packed, then bytes, and xor 0x88 turns code + 8 into two's complement.
+    uint32_t u[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const float q0 = y[r] * rcp;
@@ -173,11 +199,15 @@ __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Flo
         const float q = __builtin_fmaf(e, rcp, q0);  // == y / s (see header)
         // Clamping to integer bounds commutes with rounding to an integer.
         const float qc = __builtin_amdgcn_fmed3f(q, -8.0f, 7.0f);
-        const uint32_t bits = __builtin_bit_cast(uint32_t, qc + 12582912.0f);   // rint, in the low bits
-        word |= (bits & 0xFu) << (4 * r);
+        u[r] = __builtin_bit_cast(uint32_t, qc + 12582920.0f);
     }
+    uint32_t b[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b[k] = (u[2 * k + 1] << 4) | u[2 * k];   // low byte: the code pair
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);   // bytes: b0.0, b1.0
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);   // bytes: b2.0, b3.0 at 2, 3
     s16_out = s16;
-    return word;
+    return (lo | hi) ^ 0x88888888u;
 }
 
 // A block covers kTokensPerBlock consecutive tokens of one (KV head, K or V);
@@ -191,7 +221,8 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
     const int32_t base = (int32_t)blockIdx.x * kTokensPerBlock + group;
     const int32_t h = (int32_t)blockIdx.y;
     const bool is_v = blockIdx.z != 0;
-    const uint16_t *src_base = (is_v ? a.v_new : a.k_new) + (int64_t)h * kHeadDim + lane * 8;
+    const int eb = entry_block(lane);
+    const uint16_t *src_base = (is_v ? a.v_new : a.k_new) + (int64_t)h * kHeadDim + eb * 8;
     uint8_t *pool = static_cast<uint8_t *>(is_v ? a.v_pool : a.k_pool);
 
     uint4 raw[kRowsPerGroup];
@@ -214,7 +245,7 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
         _Float16 s16;
         const uint32_t word = quantize_row<BH>(raw[i], lane, s16);
         uint8_t *tile = pool + ((int64_t)page[i] * a.num_kv_heads + h) * a.tile_bytes;
-        *reinterpret_cast<uint32_t *>(tile + slot[i] * kCodeBytesPerRow + lane * 4) = word;
+        *reinterpret_cast<uint32_t *>(tile + slot[i] * kCodeBytesPerRow + eb * 4) = word;
         if (lane == 0) {
             *reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot[i]) =
                 __builtin_bit_cast(uint16_t, s16);
