@@ -49,8 +49,7 @@ namespace {
 constexpr int kLanesPerVec = 16;
 constexpr int kVecsPerBlock = 16;
 constexpr int kBlockThreads = kLanesPerVec * kVecsPerBlock;
-constexpr int kRowsPerGroup = 2;                                 // tokens per 16-lane row
-constexpr int kTokensPerBlock = kVecsPerBlock * kRowsPerGroup;   // 32
+constexpr int kTokensPerBlock = kBlockThreads / 4;   // INT4 append: one token per quad
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
@@ -69,100 +68,119 @@ __device__ __forceinline__ float inv_sqrt_block() {
     else return __builtin_bit_cast(float, 0x3DB504F3u);
 }
 
-// Value of lane (i ^ mask) within this lane's row of 16, for mask 1, 2, 4, 8
-// (DPP lane moves; xor 4 uses the LDS crossbar's swizzle, without memory).
+// Quad exchange: the value of lane (i ^ MASK), MASK = 1 or 2, of this quad.
 template <int MASK>
-__device__ __forceinline__ float row_xor(float v) {
-    const int x = __builtin_bit_cast(int, v);
-    int r;
-    if constexpr (MASK == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
-    else if constexpr (MASK == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-    else if constexpr (MASK == 4)                                                          // no single DPP move:
-        r = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1F);                              // swizzle, xor 4
-    else r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);                           // row_ror:8
-    return __builtin_bit_cast(float, r);
+__device__ __forceinline__ float quad_xor(float v) {
+    constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;    // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
 }
 
-// Butterfly span 8 * MASK: the lower-index lane keeps u + v, the other u - v.
-// Written as p + (+-1) y: the product is exact, so this is the same single
-// rounding as y + p (lower lane) or p - y (upper lane).
-template <int MASK>
-__device__ __forceinline__ void cross_span(float (&y)[8], int lane) {
-    const float sgn = (lane & MASK) ? -1.0f : 1.0f;
+// One 128-entry vector (token, KV head, K or V) per quad of lanes.  Lane q of
+// the quad holds the 8-entry chunks c = 4 i + q, i = 0..3 (entries 8c..8c+7)
+// in y[8 i + k]: the quad's four 16-byte loads i cover 64 contiguous bytes
+// each, and butterfly spans 1, 2, 4 (inside a chunk) and 32, 64 (chunk bits
+// 2, 3 = i) stay in the lane; spans 8, 16 (chunk bits 0, 1 = q) pair lanes
+// q ^ 1, q ^ 2 of the quad, one DPP move each.
+template <int BH>
+__device__ __forceinline__ void rotate_chunks(float (&y)[32], int q) {
+    // Spans 1, 2, 4 inside each chunk.
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const float p = row_xor<MASK>(y[r]);
-        y[r] = p + sgn * y[r];
+    for (int span = 1; span < 8; span <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            if (r & span) continue;
+            const float u = y[r];
+            const float v = y[r + span];
+            y[r] = u + v;
+            y[r + span] = u - v;
+        }
+    }
+    // Spans 8, 16: the lower-index lane keeps u + v, the other u - v,
+    // written as p + (+-1) y (the product is exact: one rounding either way).
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {
+        if (8 * m >= BH) break;
+        const float sgn = (q & m) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const float p = (m == 1) ? quad_xor<1>(y[r]) : quad_xor<2>(y[r]);
+            y[r] = p + sgn * y[r];
+        }
+    }
+    // Spans 32, 64: chunk index bits 2, 3 are the register index bits 3, 4.
+#pragma unroll
+    for (int span = 8; span < 32; span <<= 1) {
+        if (4 * span >= BH) break;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            if (r & span) continue;
+            const float u = y[r];
+            const float v = y[r + span];
+            y[r] = u + v;
+            y[r + span] = u - v;
+        }
     }
 }
 
-// Max over the 16 lanes of the row of non-negative floats: their bit patterns
-// order like the values, so an integer max per DPP step.
-__device__ __forceinline__ float row_max_nonneg(float v) {
-    int k = __builtin_bit_cast(int, v);
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, true));
-    return __builtin_bit_cast(float, k);
-}
-
-// Lane <-> entries.  Lane l of a 16-lane row holds the 8 consecutive entries
-// of block e(l) = b0 + 2 b1 + 4 b3 + 8 b2 (b_i the bits of l), so butterfly
-// spans 8, 16, 32, 64 pair lanes l ^ 1, l ^ 2, l ^ 8, l ^ 4: with Bh <= 64
-// every exchange is a single DPP move.
-__device__ __forceinline__ int entry_block(int lane) {
-    return (lane & 3) | ((lane & 8) >> 1) | ((lane & 4) << 1);
-}
-
-// Rotate and quantize one 128-entry vector held as above; returns the lane's
-// 8 packed codes and the scale.
+// A block covers 64 consecutive tokens of one (KV head, K or V): quad g takes
+// token base + g, so consecutive quads write consecutive slots of a page.
 template <int BH>
-__device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Float16 &s16_out) {
-    float y[8];
-    y[0] = half_bits_to_float(raw.x);
-    y[1] = half_bits_to_float(raw.x >> 16);
-    y[2] = half_bits_to_float(raw.y);
-    y[3] = half_bits_to_float(raw.y >> 16);
-    y[4] = half_bits_to_float(raw.z);
-    y[5] = half_bits_to_float(raw.z >> 16);
-    y[6] = half_bits_to_float(raw.w);
-    y[7] = half_bits_to_float(raw.w >> 16);
+__global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs a) {
+    const int q = threadIdx.x & 3;
+    const int32_t t = (int32_t)blockIdx.x * kTokensPerBlock + (int32_t)(threadIdx.x >> 2);
+    if (t >= a.num_tokens) return;  // the whole quad leaves together
+    const int32_t h = (int32_t)blockIdx.y;
+    const bool is_v = blockIdx.z != 0;
+
+    // Issue the address loads first; their latency overlaps the arithmetic.
+    const int32_t seq = a.token_seq[t];
+    const int32_t pos = a.token_pos[t];
+    const int32_t page = a.page_table[(int64_t)seq * a.max_pages_per_seq + (pos >> a.page_shift)];
+    const int32_t slot = pos & (a.page_size - 1);
+
+    const uint4 *src = reinterpret_cast<const uint4 *>((is_v ? a.v_new : a.k_new) +
+                                                       ((int64_t)t * a.num_kv_heads + h) * kHeadDim) + q;
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = src[4 * i];
+
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        y[8 * i + 0] = half_bits_to_float(raw[i].x);
+        y[8 * i + 1] = half_bits_to_float(raw[i].x >> 16);
+        y[8 * i + 2] = half_bits_to_float(raw[i].y);
+        y[8 * i + 3] = half_bits_to_float(raw[i].y >> 16);
+        y[8 * i + 4] = half_bits_to_float(raw[i].z);
+        y[8 * i + 5] = half_bits_to_float(raw[i].z >> 16);
+        y[8 * i + 6] = half_bits_to_float(raw[i].w);
+        y[8 * i + 7] = half_bits_to_float(raw[i].w >> 16);
+    }
 
     // 1/sqrt(Bh) is a power of two for Bh = 64: then y * c is exact, and
     // scaling the absmax and the divisor instead of the 128 entries gives the
     // same numbers (the quotient y c / s equals y / (s / c) exactly).
     constexpr bool kExactScale = (BH == 64);
     if constexpr (BH > 0) {
-        // Spans 1, 2, 4: both entries of a butterfly live in this lane.
-#pragma unroll
-        for (int span = 1; span < 8; span <<= 1) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                if (r & span) continue;
-                const float u = y[r];
-                const float v = y[r + span];
-                y[r] = u + v;
-                y[r + span] = u - v;
-            }
-        }
-        // Spans 8, 16, 32, 64 (see entry_block).
-        if constexpr (BH >= 16) cross_span<1>(y, lane);
-        if constexpr (BH >= 32) cross_span<2>(y, lane);
-        if constexpr (BH >= 64) cross_span<8>(y, lane);
-        if constexpr (BH >= 128) cross_span<4>(y, lane);
+        rotate_chunks<BH>(y, q);
         if constexpr (!kExactScale) {
             const float c = inv_sqrt_block<BH>();
 #pragma unroll
-            for (int r = 0; r < 8; ++r) y[r] = y[r] * c;
+            for (int r = 0; r < 32; ++r) y[r] = y[r] * c;
         }
     }
 
-    // Token-wise absmax over the 128 entries (exact).
+    // Token-wise absmax over the 128 entries (exact): lane, then quad.
     float m = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(y[r]));
-    m = row_max_nonneg(m);
+    for (int r = 0; r < 32; ++r) m = fmaxf(m, fabsf(y[r]));
+    {
+        // non-negative floats order like their bit patterns: integer max
+        int k = __builtin_bit_cast(int, m);
+        k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
+        k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
+        m = __builtin_bit_cast(float, k);
+    }
     if constexpr (kExactScale) m = m * inv_sqrt_block<BH>();
 
     const float r7 = __builtin_bit_cast(float, 0x3E124925u);   // fp32 nearest 1/7
@@ -188,68 +206,35 @@ __device__ __forceinline__ uint32_t quantize_row(const uint4 raw, int lane, _Flo
         }
     }
 
-    // Codes: exact quotient, clamp, round half to even by adding 1.5 * 2^23 + 8
-    // (the low byte of the sum is then code + 8 in [0, 15]); nibble pairs are
-    // packed, then bytes, and xor 0x88 turns code + 8 into two's complement.
-    uint32_t u[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const float q0 = y[r] * rcp;
-        const float e = __builtin_fmaf(-q0, sd, y[r]);
-        const float q = __builtin_fmaf(e, rcp, q0);  // == y / s (see header)
-        // Clamping to integer bounds commutes with rounding to an integer.
-        const float qc = __builtin_amdgcn_fmed3f(q, -8.0f, 7.0f);
-        u[r] = __builtin_bit_cast(uint32_t, qc + 12582920.0f);
-    }
-    uint32_t b[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) b[k] = (u[2 * k + 1] << 4) | u[2 * k];   // low byte: the code pair
-    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);   // bytes: b0.0, b1.0
-    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);   // bytes: b2.0, b3.0 at 2, 3
-    s16_out = s16;
-    return (lo | hi) ^ 0x88888888u;
-}
-
-// A block covers kTokensPerBlock consecutive tokens of one (KV head, K or V);
-// its 16-lane row g takes tokens base + 16 i + g, i < kRowsPerGroup, so at
-// each step the 16 rows write 16 consecutive tokens.  All loads of a row's
-// tokens are issued before any of them is quantized.
-template <int BH>
-__global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs a) {
-    const int lane = threadIdx.x & (kLanesPerVec - 1);
-    const int group = threadIdx.x / kLanesPerVec;
-    const int32_t base = (int32_t)blockIdx.x * kTokensPerBlock + group;
-    const int32_t h = (int32_t)blockIdx.y;
-    const bool is_v = blockIdx.z != 0;
-    const int eb = entry_block(lane);
-    const uint16_t *src_base = (is_v ? a.v_new : a.k_new) + (int64_t)h * kHeadDim + eb * 8;
     uint8_t *pool = static_cast<uint8_t *>(is_v ? a.v_pool : a.k_pool);
-
-    uint4 raw[kRowsPerGroup];
-    int32_t page[kRowsPerGroup], slot[kRowsPerGroup];
+    uint8_t *tile = pool + ((int64_t)page * a.num_kv_heads + h) * a.tile_bytes;
+    uint8_t *row = tile + slot * kCodeBytesPerRow + 4 * q;
 #pragma unroll
-    for (int i = 0; i < kRowsPerGroup; ++i) {
-        const int32_t t = base + kVecsPerBlock * i;
-        if (t < a.num_tokens) {
-            const int32_t seq = a.token_seq[t];
-            const int32_t pos = a.token_pos[t];
-            page[i] = a.page_table[(int64_t)seq * a.max_pages_per_seq + (pos >> a.page_shift)];
-            slot[i] = pos & (a.page_size - 1);
-            raw[i] = *reinterpret_cast<const uint4 *>(src_base + (int64_t)t * a.num_kv_heads * kHeadDim);
+    for (int i = 0; i < 4; ++i) {
+        // Codes of chunk 4 i + q: exact quotient, clamp, round half to even by
+        // adding 1.5 * 2^23 + 8 (the low byte of the sum is code + 8); nibble
+        // pairs, then bytes, then xor 0x88 gives two's complement nibbles.
+        uint32_t u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float yv = y[8 * i + k];
+            const float q0 = yv * rcp;
+            const float e = __builtin_fmaf(-q0, sd, yv);
+            const float qt = __builtin_fmaf(e, rcp, q0);  // == y / s (see header)
+            // Clamping to integer bounds commutes with rounding to an integer.
+            const float qc = __builtin_amdgcn_fmed3f(qt, -8.0f, 7.0f);
+            u[k] = __builtin_bit_cast(uint32_t, qc + 12582920.0f);
         }
+        uint32_t b[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b[k] = (u[2 * k + 1] << 4) | u[2 * k];   // low byte: the code pair
+        const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);   // bytes b0.0, b1.0
+        const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);   // b2.0, b3.0 at bytes 2, 3
+        *reinterpret_cast<uint32_t *>(row + 16 * i) = (lo | hi) ^ 0x88888888u;
     }
-#pragma unroll
-    for (int i = 0; i < kRowsPerGroup; ++i) {
-        const int32_t t = base + kVecsPerBlock * i;
-        if (t >= a.num_tokens) break;   // uniform across the 16-lane row
-        _Float16 s16;
-        const uint32_t word = quantize_row<BH>(raw[i], lane, s16);
-        uint8_t *tile = pool + ((int64_t)page[i] * a.num_kv_heads + h) * a.tile_bytes;
-        *reinterpret_cast<uint32_t *>(tile + slot[i] * kCodeBytesPerRow + eb * 4) = word;
-        if (lane == 0) {
-            *reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot[i]) =
-                __builtin_bit_cast(uint16_t, s16);
-        }
+    if (q == 0) {
+        *reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot) =
+            __builtin_bit_cast(uint16_t, s16);
     }
 }
 

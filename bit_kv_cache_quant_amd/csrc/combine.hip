@@ -13,9 +13,10 @@
 // One wave merges one (sequence, query head): lane t owns dims 2t and 2t+1,
 // so the butterflies of the inverse FWHT are one in-register step (span 1)
 // and lane exchanges (spans 2..64); no LDS and no block barrier on that path.
-// With many splits per sequence (batch 1, long context) four waves share one
-// (sequence, head): each merges every fourth split, and the four partial
-// states are merged once more through LDS.
+// With many splits per sequence (batch 1, long context) 4 or 16 waves share
+// one (sequence, head): each merges every 4th (16th) split, and their partial
+// states are merged once more through LDS.  The merge is latency-bound there
+// (few units), so more waves means fewer dependent load rounds per wave.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -23,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kWideWaves = 16;     // waves per unit for very many splits
 
 __device__ __forceinline__ float wave_max(float v) {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
@@ -76,10 +78,11 @@ __device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh
     *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(o0, o1);
 }
 
-// WIDE = false: 4 units per block, one wave each.  WIDE = true: one unit per
-// block, 4 waves each merging every 4th split.
-template <bool WIDE>
-__global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a, int rotate_back) {
+// NW = 1: 4 units per block, one wave each.  NW = 4 or 16: one unit per block,
+// NW waves each merging every NW-th split.
+template <int NW>
+__global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(DecodeArgs a, int rotate_back) {
+    constexpr bool WIDE = NW > 1;
     const int wave = threadIdx.x >> 6;
     const int t = threadIdx.x & 63;
     const int unit = WIDE ? blockIdx.x : blockIdx.x * kWaves + wave;   // b * num_q_heads + qh
@@ -101,9 +104,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a, int rot
     if constexpr (!WIDE) {
         merge_splits(ml, po, nsplit, 0, 1, t, M, lsum, o0, o1);
     } else {
-        merge_splits(ml, po, nsplit, wave, kWaves, t, M, lsum, o0, o1);
-        __shared__ float sm[kWaves], sl[kWaves];
-        __shared__ float so[kWaves][kHeadDim];
+        merge_splits(ml, po, nsplit, wave, NW, t, M, lsum, o0, o1);
+        __shared__ float sm[NW], sl[NW];
+        __shared__ float so[NW][kHeadDim];
         if (t == 0) {
             sm[wave] = M;
             sl[wave] = lsum;
@@ -112,12 +115,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a, int rot
         so[wave][2 * t + 1] = o1;
         __syncthreads();
         if (wave != 0) return;
-        M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w]);
         lsum = 0.0f;
         o0 = 0.0f;
         o1 = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float f = (sm[w] == -INFINITY) ? 0.0f : exp2f(sm[w] - M);
             lsum = fmaf(sl[w], f, lsum);
             o0 = fmaf(so[w][2 * t], f, o0);
@@ -132,14 +137,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a, int rot
 
 hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream) {
     const int units = a.batch * a.num_q_heads;
+    const int rb = rotate_back ? 1 : 0;
     // Many splits per sequence (long context, small batch): spread each unit's
-    // splits over 4 waves; otherwise one wave per unit.
-    if (a.num_splits >= 32) {
-        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, stream, a,
-                           rotate_back ? 1 : 0);
+    // splits over 4 or 16 waves; otherwise one wave per unit.
+    if (a.num_splits >= 128) {
+        hipLaunchKernelGGL(combine_kernel<kWideWaves>, dim3((unsigned)units), dim3(64 * kWideWaves), 0, stream, a, rb);
+    } else if (a.num_splits >= 32) {
+        hipLaunchKernelGGL(combine_kernel<kWaves>, dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
     } else {
-        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
-                           stream, a, rotate_back ? 1 : 0);
+        hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
+                           stream, a, rb);
     }
     return hipGetLastError();
 }
