@@ -40,10 +40,9 @@
 // chunks of 64 tokens.  A block holds the 4 waves of 4 KV heads of the same
 // sequence and page range: they read adjacent tiles of the same pages (DRAM
 // locality) and share nothing but LDS space.  The grid is ordered
-// page-range-major (blockIdx.y), aligned so that each sequence's last,
-// partial range sits at the highest blockIdx.y: whole ranges are dispatched
-// first and the short remainders last (longest-first), so the launch does not
-// end on a few long ranges.  Ranges are long because every partial result
+// page-range-major (blockIdx.y).  A sequence's chunks are shared out evenly
+// over its ranges (no short remainder range), so the work items of a launch
+// have similar sizes and the launch does not end on a few long ones.  Ranges are long because every partial result
 // written back costs far more than its size in lost read bandwidth (writes
 // interleaved with the streaming reads).
 //
@@ -269,14 +268,18 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     const int L = a.context_lens[b];
     if (L <= 0) return;
     const int npages = (L + P - 1) / P;
-    // Page range s of this sequence.  Ranges are dispatched so that every
-    // sequence's last (partial) range has the highest blockIdx.y: full ranges
-    // start first and the short remainders fill the end of the launch.
+    // Page range s of this sequence: its chunks are shared out evenly over
+    // nsplit_b = ceil(npages / pages_per_split) ranges (no short remainder
+    // range), each a whole number of chunks and at most pages_per_split
+    // pages.  Ranges are dispatched with the sequence's last range at the
+    // highest blockIdx.y.
+    constexpr int kChunkPages = kChunk / P;
+    const int nch_b = (npages + kChunkPages - 1) / kChunkPages;
     const int nsplit_b = (npages + a.pages_per_split - 1) / a.pages_per_split;
     const int s = (int)blockIdx.y - (a.num_splits - nsplit_b);
     if (s < 0) return;
-    const int p0 = s * a.pages_per_split;
-    const int p1 = min(p0 + a.pages_per_split, npages);
+    const int p0 = (s * nch_b / nsplit_b) * kChunkPages;
+    const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
     const int tok_begin = p0 * P;
     const int tok_end = min(p1 * P, L);
     const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
