@@ -65,7 +65,7 @@ def _src_hash(*names):
 
 
 DECODE_KERNEL_SRC = ("decode_mfma.hip",)
-DECODE_KERNEL_NAME = "decode_int4_mfma_kernel<64, 16>"
+DECODE_KERNEL_NAME = "decode_int4_balanced_kernel<64, 16>"
 
 
 def _traffic_from_profile(kernel_hash):

@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+static_assert(kWaves == 4, "the balanced decode's partial layout assumes 4 waves per block");
 constexpr int kWideWaves = 16;     // waves per unit for very many splits
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -36,22 +37,24 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Merge splits s0, s0 + step, ... of one unit: returns (M, l) and o for dims
-// 2t, 2t + 1 (relative to M).
-__device__ __forceinline__ void merge_splits(const float *ml, const float *po, int nsplit, int s0, int step,
-                                             int t, float &M, float &lsum, float &o0, float &o1) {
+// Merge the partial states s0, s0 + step, ... < nsplit of one unit, state s
+// stored at position s * stride: returns (M, l) and o for dims 2t, 2t + 1
+// (relative to M).
+__device__ __forceinline__ void merge_splits(const float *ml, const float *po, int nsplit, int64_t stride, int s0,
+                                             int step, int t, float &M, float &lsum, float &o0, float &o1) {
     float mloc = -INFINITY;
-    for (int s = s0 + t * step; s < nsplit; s += 64 * step) mloc = fmaxf(mloc, ml[2 * s]);
+    for (int s = s0 + t * step; s < nsplit; s += 64 * step) mloc = fmaxf(mloc, ml[2 * s * stride]);
     M = wave_max(mloc);
     float lloc = 0.0f;
-    for (int s = s0 + t * step; s < nsplit; s += 64 * step) lloc = fmaf(ml[2 * s + 1], exp2f(ml[2 * s] - M), lloc);
+    for (int s = s0 + t * step; s < nsplit; s += 64 * step)
+        lloc = fmaf(ml[2 * s * stride + 1], exp2f(ml[2 * s * stride] - M), lloc);
     lsum = wave_sum(lloc);
     o0 = 0.0f;
     o1 = 0.0f;
 #pragma unroll 8
     for (int s = s0; s < nsplit; s += step) {
-        const float w = exp2f(ml[2 * s] - M);
-        const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)s * kHeadDim + 2 * t);
+        const float w = exp2f(ml[2 * s * stride] - M);
+        const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)s * stride * kHeadDim + 2 * t);
         o0 = fmaf(v.x, w, o0);
         o1 = fmaf(v.y, w, o1);
     }
@@ -94,17 +97,40 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
         return;
     }
-    const int npages = (L + a.page_size - 1) >> a.page_shift;
-    const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    const float *ml = a.ws_ml + (int64_t)unit * a.num_splits * 2;
-    const float *po = a.ws_o + (int64_t)unit * a.num_splits * kHeadDim;
+    const int qh = unit - b * a.num_q_heads;
+    int nsplit;
+    int64_t first, stride;
+    if (a.sk_groups > 0) {
+        // Balanced decode: the partial states of (b, qh) come from the ranges
+        // g_first .. g_last that meet sequence b, at positions
+        // ((quad * 4 + wave) * 4 + head) * (sk_groups + batch) + g + b.
+        const int tot = a.sk_prefix[a.batch];
+        const int pb = a.sk_prefix[b], pb1 = a.sk_prefix[b + 1];
+        const int G = balanced_groups(a.sk_min, a.sk_target, tot);
+        const int g_first = (int)((((int64_t)pb + 1) * G - 1) / tot);
+        const int g_last = (int)(((int64_t)pb1 * G - 1) / tot);
+        const int hk = qh / a.group;
+        const int chunk_id = (qh - hk * a.group) / kHeadsPerChunk;
+        const int slot = hk * a.head_chunks + chunk_id;
+        const int local = (slot % kWaves) * kHeadsPerChunk + (qh - hk * a.group) % kHeadsPerChunk;
+        nsplit = g_last - g_first + 1;
+        stride = 1;
+        first = ((int64_t)(slot / kWaves) * kWaves * kHeadsPerChunk + local) * (a.sk_groups + a.batch) + g_first + b;
+    } else {
+        const int npages = (L + a.page_size - 1) >> a.page_shift;
+        nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
+        stride = 1;
+        first = (int64_t)unit * a.num_splits;
+    }
+    const float *ml = a.ws_ml + first * 2;
+    const float *po = a.ws_o + first * kHeadDim;
     const int bh = rotate_back ? a.had_block : 0;
 
     float M, lsum, o0, o1;
     if constexpr (!WIDE) {
-        merge_splits(ml, po, nsplit, 0, 1, t, M, lsum, o0, o1);
+        merge_splits(ml, po, nsplit, stride, 0, 1, t, M, lsum, o0, o1);
     } else {
-        merge_splits(ml, po, nsplit, wave, NW, t, M, lsum, o0, o1);
+        merge_splits(ml, po, nsplit, stride, wave, NW, t, M, lsum, o0, o1);
         __shared__ float sm[NW], sl[NW];
         __shared__ float so[NW][kHeadDim];
         if (t == 0) {
@@ -140,9 +166,10 @@ hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t str
     const int rb = rotate_back ? 1 : 0;
     // Many splits per sequence (long context, small batch): spread each unit's
     // splits over 4 or 16 waves; otherwise one wave per unit.
-    if (a.num_splits >= 128) {
+    const int per_unit = a.sk_groups > 0 ? a.sk_groups / a.batch + 2 : a.num_splits;
+    if (per_unit >= 128) {
         hipLaunchKernelGGL(combine_kernel<kWideWaves>, dim3((unsigned)units), dim3(64 * kWideWaves), 0, stream, a, rb);
-    } else if (a.num_splits >= 32) {
+    } else if (per_unit >= 32) {
         hipLaunchKernelGGL(combine_kernel<kWaves>, dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
     } else {
         hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,

@@ -81,6 +81,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
+// Page-table registers per lane: a range has at most kMaxRangeChunks chunks
+// (balanced mode) or kMaxSplitTokens tokens (split mode), i.e. at most 256
+// pages of 16 tokens.
+constexpr int kPageRegs = 4;
+static_assert(kMaxRangeChunks * kChunkTokens / 16 <= 64 * kPageRegs, "page registers");
+static_assert(kMaxSplitTokens / 16 <= 64 * kPageRegs, "page registers");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = kChunkTokens;  // 64 tokens per chunk
 constexpr int kH = kHeadsPerChunk;    // 4 query heads
@@ -248,52 +254,28 @@ __device__ __forceinline__ void load_chunk(ChunkData &cd, const uint8_t *const (
     }
 }
 
+// One work range: tokens [p0 P, min(p1 P, L)) of sequence b (p0 on a chunk
+// boundary) for head slot (KV head hk, query-head chunk chunk_id).  Writes
+// the partial softmax state of query head qh0 + g to unit u0 + g * head_stride
+// of the workspace (o: kHeadDim floats, then (max, sum) in ws_ml).
 template <int BH, int P>
-__global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a) {
-    // The wave index is uniform across the wave; saying so keeps everything
-    // derived from it (head, tile addresses) in scalar registers.
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh, const int lane, const int b,
+                                             const int hk, const int chunk_id, const int L, const int p0,
+                                             const int p1, const int64_t u0, const int64_t head_stride) {
     const int g = lane >> 4;
     const int j = lane & 15;
-    // blockIdx.x = (sequence, quad of head slots), blockIdx.y = page range;
-    // a head slot is (KV head, chunk of 4 of its query heads).
-    const int head_slots = a.num_kv_heads * a.head_chunks;
-    const int quads = (head_slots + kWaves - 1) / kWaves;
-    const int b = blockIdx.x / quads;
-    const int slot = (blockIdx.x - b * quads) * kWaves + wave;
-    if (slot >= head_slots) return;
-    const int hk = slot / a.head_chunks;
-    const int chunk_id = slot - hk * a.head_chunks;
-    const int L = a.context_lens[b];
-    if (L <= 0) return;
-    const int npages = (L + P - 1) / P;
-    // Page range s of this sequence: its chunks are shared out evenly over
-    // nsplit_b = ceil(npages / pages_per_split) ranges (no short remainder
-    // range), each a whole number of chunks and at most pages_per_split
-    // pages.  Ranges are dispatched with the sequence's last range at the
-    // highest blockIdx.y.
-    constexpr int kChunkPages = kChunk / P;
-    const int nch_b = (npages + kChunkPages - 1) / kChunkPages;
-    const int nsplit_b = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    const int s = (int)blockIdx.y - (a.num_splits - nsplit_b);
-    if (s < 0) return;
-    const int p0 = (s * nch_b / nsplit_b) * kChunkPages;
-    const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
     const int tok_begin = p0 * P;
     const int tok_end = min(p1 * P, L);
     const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
-
-    __shared__ WaveShared shared_all[kWaves];
-    WaveShared &sh = shared_all[wave];
     const int qh0 = hk * a.group + chunk_id * kH;
     const int nheads = min(kH, a.group - chunk_id * kH);
 
-    // Physical pages of this range (at most 128): lane i holds pages p0 + i
-    // and p0 + 64 + i.
+    // Physical pages of this range (at most 64 kPageRegs): lane i holds pages
+    // p0 + 64 r + i.
     const int32_t *pt = a.page_table + (int64_t)b * a.max_pages_per_seq;
-    const int my_page_lo = (p0 + lane < p1) ? pt[p0 + lane] : 0;
-    const int my_page_hi = (p0 + 64 + lane < p1) ? pt[p0 + 64 + lane] : 0;
+    int my_page[kPageRegs];
+#pragma unroll
+    for (int r = 0; r < kPageRegs; ++r) my_page[r] = (p0 + 64 * r + lane < p1) ? pt[p0 + 64 * r + lane] : 0;
 
     // ---- setup: rotated query as fixed-point limbs; row g = head g ----
     float qv[8];
@@ -403,8 +385,10 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int rel = min(c * (kChunk / P) + (16 * t) / P, last_rel);   // clamp past the end
-            const int32_t phys = rel < 64 ? __builtin_amdgcn_readlane(my_page_lo, rel)
-                                          : __builtin_amdgcn_readlane(my_page_hi, rel - 64);
+            int32_t phys = __builtin_amdgcn_readlane(my_page[0], rel & 63);
+#pragma unroll
+            for (int r = 1; r < kPageRegs; ++r)
+                if ((rel >> 6) == r) phys = __builtin_amdgcn_readlane(my_page[r], rel & 63);
             kt[t] = tile_addr(kbase, (uint32_t)phys, page_stride);
             vt[t] = tile_addr(vbase, (uint32_t)phys, page_stride);
         }
@@ -534,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     // ---- write this range's partial state ----
     const float l_row = row_sum16(l_lane);
     if (g < nheads) {
-        const int64_t unit = ((int64_t)b * a.num_q_heads + qh0 + g) * a.num_splits + s;
+        const int64_t unit = u0 + g * head_stride;
         float *dst = a.ws_o + unit * kHeadDim + j;
 #pragma unroll
         for (int m = 0; m < 8; ++m) dst[16 * m] = o_acc[m];
@@ -545,13 +529,171 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     }
 }
 
+
+template <int BH, int P>
+__global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a) {
+    // The wave index is uniform across the wave; saying so keeps everything
+    // derived from it (head, tile addresses) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    // blockIdx.x = (sequence, quad of head slots), blockIdx.y = page range;
+    // a head slot is (KV head, chunk of 4 of its query heads).
+    const int head_slots = a.num_kv_heads * a.head_chunks;
+    const int quads = (head_slots + kWaves - 1) / kWaves;
+    const int b = blockIdx.x / quads;
+    const int slot = (blockIdx.x - b * quads) * kWaves + wave;
+    if (slot >= head_slots) return;
+    const int hk = slot / a.head_chunks;
+    const int chunk_id = slot - hk * a.head_chunks;
+    const int L = a.context_lens[b];
+    if (L <= 0) return;
+    const int npages = (L + P - 1) / P;
+    // Page range s of this sequence: its chunks are shared out evenly over
+    // nsplit_b = ceil(npages / pages_per_split) ranges (no short remainder
+    // range), each a whole number of chunks and at most pages_per_split
+    // pages.  Ranges are dispatched with the sequence's last range at the
+    // highest blockIdx.y.
+    constexpr int kChunkPages = kChunk / P;
+    const int nch_b = (npages + kChunkPages - 1) / kChunkPages;
+    const int nsplit_b = (npages + a.pages_per_split - 1) / a.pages_per_split;
+    const int s = (int)blockIdx.y - (a.num_splits - nsplit_b);
+    if (s < 0) return;
+    const int p0 = (s * nch_b / nsplit_b) * kChunkPages;
+    const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
+    __shared__ WaveShared shared_all[kWaves];
+    const int qh0 = hk * a.group + chunk_id * kH;
+    decode_range<BH, P>(a, shared_all[wave], lane, b, hk, chunk_id, L, p0, p1,
+                        ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
+}
+
+// Balanced INT4 decode: the chunks of all sequences, in sequence order, form
+// one list of TOT chunks that is cut into G equal ranges; block (range gi,
+// head quad q) processes range gi for the 4 head slots of quad q, one
+// partial state per (sequence b it meets, head), stored at position gi + b
+// of that head's (sk_groups + batch) states (so a head's states for one
+// sequence are contiguous).  Every block gets the same
+// amount of cache to stream, whatever the mix of context lengths, so the
+// launch neither waits on a few long work items nor dispatches a second
+// round of them.  Each block first scans the context lengths (batch <=
+// kMaxScanBatch) to find its range.
+template <int BH, int P>
+__global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeArgs a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int B = a.batch;
+    union Shared {
+        struct {
+            int32_t prefix[kMaxScanBatch + 1];
+            int32_t part[kThreads];
+        } scan;
+        WaveShared waves[kWaves];
+    };
+    __shared__ Shared sm;
+
+    // Exclusive prefix sums of the per-sequence chunk counts.
+    if (B <= 64) {
+        // one wave: lane i holds sequence i; shuffle scan, no block barriers
+        if (wave == 0) {
+            const int L = lane < B ? a.context_lens[lane] : 0;
+            const int nch = L > 0 ? (L + kChunk - 1) / kChunk : 0;
+            int inc = nch;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(inc, off);
+                if (lane >= off) inc += v;
+            }
+            if (lane < B) sm.scan.prefix[lane] = inc - nch;
+            if (lane == B - 1) sm.scan.prefix[B] = inc;
+        }
+    } else {
+        const int per = (B + kThreads - 1) / kThreads;
+        const int i0 = threadIdx.x * per;
+        const int i1 = min(i0 + per, B);
+        int local = 0;
+        for (int i = i0; i < i1; ++i) {
+            const int L = a.context_lens[i];
+            local += L > 0 ? (L + kChunk - 1) / kChunk : 0;
+        }
+        sm.scan.part[threadIdx.x] = local;
+        __syncthreads();
+        for (int off = 1; off < kThreads; off <<= 1) {
+            const int v = threadIdx.x >= off ? sm.scan.part[threadIdx.x - off] : 0;
+            __syncthreads();
+            sm.scan.part[threadIdx.x] += v;
+            __syncthreads();
+        }
+        int run = sm.scan.part[threadIdx.x] - local;
+        for (int i = i0; i < i1; ++i) {
+            sm.scan.prefix[i] = run;
+            const int L = a.context_lens[i];
+            run += L > 0 ? (L + kChunk - 1) / kChunk : 0;
+        }
+        if (threadIdx.x == kThreads - 1) sm.scan.prefix[B] = sm.scan.part[kThreads - 1];
+    }
+    __syncthreads();
+    const int tot = __builtin_amdgcn_readfirstlane(sm.scan.prefix[B]);
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i <= B; i += kThreads) a.sk_prefix[i] = sm.scan.prefix[i];
+
+    const int G = balanced_groups(a.sk_min, a.sk_target, tot);
+    const int gi = blockIdx.x / a.quads;
+    const int qd = blockIdx.x - gi * a.quads;
+    const int start = (int)(((int64_t)gi * tot) / G);
+    const int end = (int)(((int64_t)(gi + 1) * tot) / G);
+    // First sequence of the range: the last b with prefix[b] <= start.
+    int b0 = 0;
+    if (tot > 0 && gi < G) {
+        int hi = B;
+        while (hi - b0 > 1) {
+            const int mid = (b0 + hi) >> 1;
+            if (sm.scan.prefix[mid] <= start) b0 = mid;
+            else hi = mid;
+        }
+    }
+    b0 = __builtin_amdgcn_readfirstlane(b0);   // uniform: keep sequence state scalar
+    const int pb0 = __builtin_amdgcn_readfirstlane(sm.scan.prefix[b0]);
+    __syncthreads();   // the scan space becomes the waves' space
+    if (tot == 0 || gi >= G) return;
+
+    const int head_slots = a.num_kv_heads * a.head_chunks;
+    const int slot = qd * kWaves + wave;
+    if (slot >= head_slots) return;
+    const int hk = slot / a.head_chunks;
+    const int chunk_id = slot - hk * a.head_chunks;
+    constexpr int kChunkPages = kChunk / P;
+    int pb = pb0;
+    for (int b = b0; b < B && pb < end; ++b) {
+        const int L = a.context_lens[b];
+        const int nch = L > 0 ? (L + kChunk - 1) / kChunk : 0;
+        const int pb1 = pb + nch;
+        const int c0 = max(start, pb) - pb;
+        const int c1 = min(end, pb1) - pb;
+        if (c0 < c1) {
+            const int npages = (L + P - 1) / P;
+            const int64_t per_head = (int64_t)a.sk_groups + B;   // partial states per head
+            const int64_t u0 = ((int64_t)(qd * kWaves + wave) * kH) * per_head + gi + b;
+            decode_range<BH, P>(a, sm.waves[wave], lane, b, hk, chunk_id, L, c0 * kChunkPages,
+                                min(c1 * kChunkPages, npages), u0, per_head);
+        }
+        pb = pb1;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream) {
     const int quads = (a.num_kv_heads * a.head_chunks + kWaves - 1) / kWaves;
-    const dim3 grid((unsigned)(a.batch * quads), (unsigned)a.num_splits, 1);
+    const bool balanced = a.sk_groups > 0;
+    const dim3 grid = balanced ? dim3((unsigned)(quads * a.sk_groups), 1, 1)
+                               : dim3((unsigned)(a.batch * quads), (unsigned)a.num_splits, 1);
     const dim3 block(kThreads);
-#define KVQ_LAUNCH(BHV, PV) hipLaunchKernelGGL((decode_int4_mfma_kernel<BHV, PV>), grid, block, 0, stream, a)
+#define KVQ_LAUNCH(BHV, PV)                                                                       \
+    do {                                                                                          \
+        if (balanced)                                                                             \
+            hipLaunchKernelGGL((decode_int4_balanced_kernel<BHV, PV>), grid, block, 0, stream, a); \
+        else                                                                                      \
+            hipLaunchKernelGGL((decode_int4_mfma_kernel<BHV, PV>), grid, block, 0, stream, a);     \
+    } while (0)
     if (a.page_size == 16) {
         switch (a.had_block) {
             case 0: KVQ_LAUNCH(0, 16); break;

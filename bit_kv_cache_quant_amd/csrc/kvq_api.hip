@@ -52,6 +52,58 @@ size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, int32_t nsplit) {
     return (size_t)batch * num_q_heads * nsplit * (kHeadDim + 2) * sizeof(float);
 }
 
+// Balanced INT4 decode plan (batch <= kMaxScanBatch).  The chunk total is
+// only known on the device; tot_max = batch * ceil(max_context_len / 64)
+// bounds it, and the launch has enough block groups for any total up to it.
+// Default: between 512 and 1024 blocks over all head quads (two to four per
+// CU), ranges of about 32 chunks in between.  A caller's pages_per_split
+// fixes the number of ranges so that a range holds about that many pages.
+constexpr int32_t kBalancedMinBatch = 16;
+
+struct BalancedPlan {
+    int32_t quads = 0, gmin = 0, gmax = 0, groups = 0;
+    size_t partial_units = 0;   // partial states in the workspace
+};
+
+bool balanced_plan(int32_t batch, int32_t num_kv_heads, int32_t head_chunks, int32_t max_context_len,
+                   int32_t page_size, int32_t pages_per_split, BalancedPlan *pl) {
+    // Few sequences: the split mode already cuts each into equal ranges
+    // (mostly full-length ones), without the scan, the range lookup in the
+    // merge and the balanced kernel's larger register footprint (measured:
+    // 3% slower at batch 8 x 131,072, 8% at batch 1 x 32,768).
+    if (batch < kBalancedMinBatch || batch > kvq::kMaxScanBatch) return false;
+    const int64_t heads_per_quad = (int64_t)kvq::kHeadsPerChunk * 4;   // 4 waves x 4 query heads
+    const int64_t quads = ((int64_t)num_kv_heads * head_chunks + 3) / 4;
+    int64_t tot_max = (int64_t)batch * ((max_context_len + kvq::kChunkTokens - 1) / kvq::kChunkTokens);
+    if (tot_max < 1) tot_max = 1;
+    if (tot_max >= (1ll << 30)) return false;
+    int64_t gmin, gmax;
+    if (pages_per_split <= 0) {
+        gmax = 1024 / quads;
+        if (gmax < 1) gmax = 1;
+        gmin = gmax / 2;
+        if (gmin < 1) gmin = 1;
+    } else {
+        int64_t cpr = ((int64_t)pages_per_split * page_size + kvq::kChunkTokens - 1) / kvq::kChunkTokens;
+        if (cpr < 1) cpr = 1;
+        gmax = gmin = (tot_max + cpr - 1) / cpr;
+    }
+    if (gmax > (1 << 24)) gmax = gmin = 1 << 24;
+    const int64_t groups = kvq::balanced_groups((int32_t)gmin, (int32_t)gmax, (int32_t)tot_max);
+    if (groups * quads > (1ll << 31) - 1) return false;
+    pl->quads = (int32_t)quads;
+    pl->gmin = (int32_t)gmin;
+    pl->gmax = (int32_t)gmax;
+    pl->groups = (int32_t)groups;
+    pl->partial_units = (size_t)quads * (size_t)(groups + batch) * (size_t)heads_per_quad;
+    return true;
+}
+
+size_t balanced_workspace_bytes(const BalancedPlan &pl, int32_t batch) {
+    const size_t floats = pl.partial_units * (kHeadDim + 2);
+    return floats * sizeof(float) + (((size_t)batch + 1) * sizeof(int32_t) + 15) / 16 * 16;
+}
+
 // Timing hook (see kvq_set_decode_phase_event in include/kvq.h).
 void *g_phase_event = nullptr;
 
@@ -164,7 +216,10 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
     if (nsplit > 65535 || (int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
     if (!int4 && batch > 65535) return KVQ_ERR_UNSUPPORTED;   // fp16 kernel: batch is grid z
-    const size_t need = workspace_bytes_for(batch, num_q_heads, nsplit);
+    BalancedPlan bp;
+    const bool balanced = int4 && balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size,
+                                                pages_per_split, &bp);
+    const size_t need = balanced ? balanced_workspace_bytes(bp, batch) : workspace_bytes_for(batch, num_q_heads, nsplit);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (debug_checks_enabled()) {
@@ -180,7 +235,16 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.context_lens = context_lens;
     a.out = out;
     a.ws_o = static_cast<float *>(workspace);
-    a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * nsplit * kHeadDim;
+    if (balanced) {
+        a.ws_ml = a.ws_o + bp.partial_units * kHeadDim;
+        a.sk_prefix = reinterpret_cast<int32_t *>(a.ws_ml + bp.partial_units * 2);
+        a.sk_groups = bp.groups;
+        a.sk_min = bp.gmin;
+        a.sk_target = bp.gmax;
+        a.quads = bp.quads;
+    } else {
+        a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * nsplit * kHeadDim;
+    }
     a.tile_bytes = int4 ? (int64_t)kvq_page_tile_bytes(head_dim, page_size) : (int64_t)page_size * head_dim * 2;
     a.max_pages_per_seq = max_pages_per_seq;
     a.batch = batch;
@@ -295,9 +359,15 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int
         head_dim != kHeadDim || !valid_page_size(page_size) || pages_per_split < 0 || max_context_len < 0)
         return 0;
     int32_t pps = 0, nsplit = 0;
-    choose_split(batch, num_kv_heads, head_chunks_of(num_q_heads, num_kv_heads), max_context_len, page_size,
-                 pages_per_split, &pps, &nsplit);
-    return workspace_bytes_for(batch, num_q_heads, nsplit);
+    const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
+    choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
+    size_t need = workspace_bytes_for(batch, num_q_heads, nsplit);   // fp16 decode (and large batches)
+    BalancedPlan bp;
+    if (balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &bp)) {
+        const size_t nb = balanced_workspace_bytes(bp, batch);
+        if (nb > need) need = nb;
+    }
+    return need;
 }
 
 int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,

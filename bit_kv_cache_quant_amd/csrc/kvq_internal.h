@@ -11,7 +11,9 @@ constexpr int kHeadDim = 128;          // the only supported head dimension
 constexpr int kCodeBytesPerRow = kHeadDim / 2;
 constexpr int kHeadsPerChunk = 4;      // query heads handled together per KV head
 constexpr int kChunkTokens = 64;       // decode processes tokens in chunks of 64
-constexpr int kMaxSplitTokens = 2048;  // longest page range one decode wave takes
+constexpr int kMaxSplitTokens = 2048;  // longest page range one decode wave takes (split mode)
+constexpr int kMaxScanBatch = 4096;    // balanced INT4 decode: largest batch one block scans
+constexpr int kMaxRangeChunks = 64;    // balanced INT4 decode: longest work range, in chunks
 
 struct AppendArgs {
     const uint16_t *k_new;
@@ -52,7 +54,30 @@ struct DecodeArgs {
     int32_t pages_per_split;
     int32_t num_splits;
     float score_scale;         // softmax_scale * log2(e): scores are kept in log2 units
+    // Balanced INT4 decode (sk_groups > 0): the concatenated chunk list of all
+    // sequences is cut into equal ranges, one per block group; partial states
+    // are indexed by (head quad, range + sequence, wave, head).
+    int32_t *sk_prefix;        // [batch + 1] chunk prefix sums (written by the partial kernel)
+    int32_t sk_groups;         // block groups launched per head quad (0: split mode)
+    int32_t sk_min;            // block groups wanted for parallelism
+    int32_t sk_target;         // most block groups wanted
+    int32_t quads;             // head quads (groups of kHeadsPerChunk head slots) per sequence
 };
+
+// Number of ranges the balanced decode cuts `tot` chunks into: ranges of
+// about kPreferredRangeChunks (few partial states to write and merge), but at
+// least gmin ranges (parallelism) and at most gmax, never a range longer than
+// kMaxRangeChunks, never an empty one.  Monotonic in tot.
+constexpr int kPreferredRangeChunks = 32;
+__host__ __device__ inline int32_t balanced_groups(int32_t gmin, int32_t gmax, int32_t tot) {
+    int32_t g = (tot + kPreferredRangeChunks - 1) / kPreferredRangeChunks;
+    if (g < gmin) g = gmin;
+    if (g > gmax) g = gmax;
+    const int32_t gcap = (tot + kMaxRangeChunks - 1) / kMaxRangeChunks;
+    if (g < gcap) g = gcap;
+    if (g > tot) g = tot;
+    return g < 1 ? 1 : g;
+}
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_append_fp16(const AppendArgs &a, hipStream_t stream);

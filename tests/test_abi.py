@@ -46,19 +46,56 @@ def test_status_strings_and_tile_bytes():
     assert kvq.page_tile_bytes(128, 8) == 0
 
 
+def _split_bytes(batch, hq, hkv, ctx, P, pps=0):
+    """Split-mode workspace (fp16 decode, and INT4 for batches above 4096)."""
+    npages = max(1, -(-ctx // P))
+    chunks = -(-(hq // hkv) // 4)
+    if pps <= 0:
+        items = batch * hkv * chunks
+        want = 1 if items >= 2048 else -(-2048 // items)
+        pps = -(-npages // want)
+    pps = max(1, min(pps, 2048 // P))
+    cp = 64 // P
+    pps = -(-pps // cp) * cp
+    return batch * hq * (-(-npages // pps)) * 130 * 4
+
+
+def _balanced_bytes(batch, hq, hkv, ctx, P, pps=0):
+    """Balanced INT4 decode workspace (16 <= batch <= 4096): quads x (groups +
+    batch) x 16 partial states of 130 floats, then batch + 1 int32 prefix sums
+    (16-byte padded)."""
+    if batch < 16 or batch > 4096:
+        return 0
+    quads = -(-(hkv * -(-(hq // hkv) // 4)) // 4)
+    tot_max = max(1, batch * (-(-ctx // 64)))
+    if pps <= 0:
+        gmax = max(1, 1024 // quads)
+        gmin = max(1, gmax // 2)
+    else:
+        cpr = max(1, -(-(pps * P) // 64))
+        gmax = gmin = -(-tot_max // cpr)
+    g = min(max(-(-tot_max // 32), gmin), gmax)       # ranges of ~32 chunks within [gmin, gmax]
+    groups = max(1, min(max(g, -(-tot_max // 64)), tot_max))
+    units = quads * (groups + batch) * 16
+    return units * 130 * 4 + -(-((batch + 1) * 4) // 16) * 16
+
+
 def test_workspace_query():
-    # 1 sequence, ctx 256, P 16 -> 16 pages; a split is a whole number of
-    # 64-token chunks (4 pages of 16, 2 of 32)
-    n = kvq.workspace_bytes(1, 32, 8, 256, 16)
-    assert n == 1 * 32 * 4 * (128 + 2) * 4
-    assert kvq.workspace_bytes(1, 32, 8, 256, 16, pages_per_split=4) == 32 * 4 * 130 * 4
-    assert kvq.workspace_bytes(1, 32, 8, 256, 16, pages_per_split=1) == 32 * 4 * 130 * 4
-    assert kvq.workspace_bytes(1, 32, 8, 256, 32, pages_per_split=1) == 32 * 4 * 130 * 4
+    # the larger of the two layouts (one workspace serves INT4 and fp16 calls)
+    for args, pps in [((1, 32, 8, 256, 16), 0), ((1, 32, 8, 256, 16), 4), ((1, 32, 8, 256, 16), 1),
+                      ((1, 32, 8, 256, 32), 1), ((256, 32, 8, 8193, 16), 0), ((256, 32, 8, 8193, 16), 1000),
+                      ((8, 32, 8, 131072, 32), 0), ((3, 32, 8, 129, 16), 0), ((1, 8, 8, 300, 16), 0),
+                      ((2, 32, 8, 256, 16), 4), ((16, 32, 8, 256, 16), 4), ((4096, 32, 8, 64, 16), 0),
+                      ((4097, 32, 8, 64, 16), 0)]:
+        want = max(_split_bytes(*args, pps), _balanced_bytes(*args, pps))
+        assert kvq.workspace_bytes(*args, pages_per_split=pps) == want, (args, pps)
+    # hand-checked values: ctx 256 at P 16 is 4 chunks
+    assert _split_bytes(1, 32, 8, 256, 16) == 1 * 32 * 4 * 130 * 4
+    assert _balanced_bytes(16, 32, 8, 256, 16, 4) == 2 * (64 + 16) * 16 * 130 * 4 + 80
+    # long sequences: split mode caps a split at 2048 tokens
+    assert _split_bytes(256, 32, 8, 8193, 16) == 256 * 32 * 5 * 130 * 4
     assert kvq.workspace_bytes(0, 32, 8, 256, 16) == 0
     assert kvq.workspace_bytes(1, 30, 8, 256, 16) == 0      # Hq not a multiple of Hkv
-    # long sequences are capped at 2048 tokens per split
-    assert kvq.workspace_bytes(256, 32, 8, 8193, 16) == 256 * 32 * 5 * 130 * 4
-    assert kvq.workspace_bytes(256, 32, 8, 8193, 16, pages_per_split=1000) == 256 * 32 * 5 * 130 * 4
 
 
 FAKE = 0x1000  # an aligned, never-dereferenced address

@@ -71,6 +71,24 @@ def test_decode_gqa_groups(dev, group):
     _assert_close(got, want)
 
 
+@pytest.mark.parametrize("pages_per_split,group", [(0, 4), (4, 4), (9, 4), (0, 1), (3, 8), (5, 2)])
+def test_decode_ranges_cross_sequences(dev, pages_per_split, group):
+    """Many short, ragged sequences (some empty): with batches of 16 or more
+    the decode cuts the concatenated chunks of all sequences into equal
+    ranges, so a range can end inside one sequence and run on into the next
+    ones; small pages_per_split values force ranges of one or two chunks."""
+    r = np.random.default_rng(123)
+    lens = [int(x) for x in r.integers(0, 260, size=37)]
+    lens[3] = 0
+    lens[4] = 0
+    lens[20] = 1
+    hkv = 8 if group <= 4 else 2
+    w = wl.small(len(lens), lens, 64, 16, cfg_id=150 + group, num_kv_heads=hkv, num_q_heads=hkv * group)
+    got, want, _ = _int4_case(w, dev, pages_per_split=pages_per_split)
+    _assert_close(got, want)
+    assert np.all(got[3] == 0) and np.all(got[4] == 0)
+
+
 def test_decode_split_invariance(dev):
     lens = [700, 1500, 33]
     w = wl.small(len(lens), lens, 128, 16, cfg_id=90)
