@@ -106,8 +106,9 @@ size_t kvq_page_tile_bytes(int32_t head_dim, int32_t page_size);
  *      (all codes 0 when s is 0);
  *   4. the D/2 code bytes and s are written to slot token_pos[t] % page_size
  *      of physical page page_table[token_seq[t]][token_pos[t] / page_size].
- * The results are bit-exact with that definition.  No other byte of either
- * pool changes.
+ * The results are bit-exact with that definition for finite inputs (inf and
+ * NaN entries are outside the contract).  No other byte of either pool
+ * changes.
  *
  *   k_new, v_new          fp16 [num_tokens][num_kv_heads][head_dim]
  *   token_seq, token_pos  int32 [num_tokens]
@@ -124,8 +125,11 @@ int kv_quant_append(const uint16_t *k_new, const uint16_t *v_new,
 
 /*
  * Workspace size for the decode entry points: partial softmax states of the
- * split-K reduction, fp32.  `pages_per_split` = 0 lets the library choose
- * (the same choice the decode call makes for the same arguments).
+ * split-K reduction (fp32) plus, for batches of 16 to 4096, the prefix sums
+ * of the sequences' chunk counts.  The size covers both ways of splitting, so
+ * one workspace serves the INT4 and the fp16 decode.  `pages_per_split` = 0
+ * lets the library choose (the same choice the decode call makes for the same
+ * arguments).
  */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
@@ -144,10 +148,14 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   z_j = softmax_scale * (q' . k_j), w = softmax(z) over j < L,
  *   out[b][qh] = R (sum_j w_j v_j).
  * L <= 0 gives a zero row.  had_block must be the value the cache was
- * written with (0 = no rotation).  The work is split over page ranges
- * ("split-K"); partial softmax states go to `workspace` and a second kernel
- * merges them, so the result does not depend on the split beyond fp32
- * rounding.
+ * written with (0 = no rotation).  Every context_lens[b] must be at most
+ * max_context_len (not checked unless KVQ_CHECK=1).  The work is split over
+ * page ranges ("split-K"): for batches of 16 to 4096 sequences the chunks
+ * (64 tokens) of all sequences are cut into equal ranges, which may run from
+ * one sequence into the next; otherwise each sequence is cut into equal
+ * ranges of at most 2048 tokens.  Partial softmax states go to `workspace`
+ * and a second kernel merges them, so the result does not depend on the
+ * split beyond fp32 rounding.
  *
  *   q              fp16 [batch][num_q_heads][head_dim]
  *   k_pool, v_pool uint8 [num_pages][num_kv_heads][tile]
@@ -155,8 +163,9 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   context_lens   int32 [batch]
  *   out            fp32 [batch][num_q_heads][head_dim]
  *   workspace      >= paged_decode_attn_workspace_bytes(...) bytes of device memory
- *   pages_per_split  0 = library's choice, else the number of pages per split,
- *                  rounded up to whole 64-token chunks and capped at 2048 tokens
+ *   pages_per_split  0 = library's choice, else about this many pages per
+ *                  range (whole 64-token chunks; per-sequence ranges are
+ *                  capped at 2048 tokens, batch-wide ranges at 64 chunks)
  * batch == 0 is a no-op returning KVQ_OK.
  */
 int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
@@ -182,7 +191,8 @@ int kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
 /*
  * paged_decode_attn_fp16 — baseline decode over fp16 pools: the same
  * computation as paged_decode_attn_int4 with unquantized keys and values and
- * no rotation.  Same arguments as paged_decode_attn_int4 without had_block.
+ * no rotation.  Same arguments as paged_decode_attn_int4 without had_block;
+ * it always splits each sequence on its own (never across sequences).
  */
 int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                            int64_t num_pages, const int32_t *page_table,
