@@ -63,12 +63,15 @@
 //        1 KiB of LDS; lane (g, j) reads back the 16 tokens of group g for
 //        head j/4 and keeps limb j%4 (A operand of p.v).
 //   p.v  B (values): lane column j = dim 16m + j of MFMA m, k-slots = the
-//        16 tokens of group g.  Values are loaded like keys, 16 bytes per
-//        lane (1 KiB per instruction), written to LDS, and read back with
-//        gfx950's transposed 4-bit LDS read (ds_read_b64_tr_b4): one read
+//        16 tokens of group g.  Values go from HBM straight into LDS
+//        (global_load_lds_dwordx4, 1 KiB per instruction) and are read back
+//        with gfx950's transposed 4-bit LDS read (ds_read_b64_tr_b4): one read
 //        gives a lane one dim of 16 tokens as 16 nibbles, which split into
 //        the operand's bytes with two bit operations each.
 //        D: lane (g, j) gets rows (head g, limbs) for dim 16m + j.
+//   Pipelining: chunk c + 1 loads while chunk c computes, its values into
+//        the second LDS buffer, its keys and scales into registers once chunk
+//        c's have been used.
 //   All cache bytes are read with non-temporal 16-byte loads.
 #include <type_traits>
 
@@ -200,17 +203,35 @@ __device__ __forceinline__ float ulimbs_to_float(v4i d) {
     return static_cast<float>(s);
 }
 
-// Value codes of one chunk pass through LDS to be read back transposed: one
-// 16-token group is 16 rows of 64 code bytes, stored with an 80-byte row
-// pitch so that the 16 lanes of a transposed read (one 8-byte word from each
-// of the group's 16 rows) hit distinct banks.
-constexpr int kVRowPitch = 80;
-constexpr int kVGroupStride = 16 * kVRowPitch;
+// Value codes go from HBM straight to LDS (global_load_lds_dwordx4: lane l
+// of the instruction deposits its 16 bytes at 16 l of a 1 KiB block), two
+// chunks deep, and are read back transposed.  One 16-token group is one 1 KiB
+// block: 16 rows of 64 code bytes, row n's 16-byte piece p stored in slot
+// 4n + (p ^ ((n >> 2) & 3)).  A transposed read (one 8-byte word from each of
+// the group's 16 rows) then touches 32 distinct banks; the groups start at
+// 0, 1152, 2176 and 3328 bytes, so that the two groups read in the same pass
+// (0 and 1, 2 and 3) lie 128 bytes apart modulo 256 and use the other 32.
+constexpr int kVGroupBytes = 1024;
+__host__ __device__ constexpr int vgroup_off(int t) { return t * kVGroupBytes + 128 * ((t + 1) >> 1); }
+constexpr int kVBufBytes = vgroup_off(3) + kVGroupBytes;     // 4352
+static_assert(vgroup_off(1) >= kVGroupBytes && vgroup_off(2) >= vgroup_off(1) + kVGroupBytes &&
+              vgroup_off(3) >= vgroup_off(2) + kVGroupBytes, "value groups overlap");
+constexpr int kPfixPitch = kChunk + 4;                          // dwords per head row
 
-struct WaveShared {
-    uint32_t qlimb[kH][4][2][4][4];   // [head][limb][parity][lane group][dword]
-    uint32_t pfix[kH][kChunk];        // fixed-point P of the current chunk
-    uint8_t vtile[4 * kVGroupStride]; // value codes of the current chunk
+// LDS of one wave, in two arrays of their own so that the compiler can tell
+// the value loads' destination apart from the P hand-off (and waits for the
+// value loads only before reading values):
+//   value space: two chunks of value codes, vbuf[2][kVBufBytes]; at set-up
+//                it holds the query limbs, qlimb[kH][4][2][4][4]
+//                ([head][limb][parity][lane group][dword]);
+//   P space:     fixed-point P of the current chunk, pfix[kH][kPfixPitch].
+struct alignas(16) WaveValues {
+    uint8_t vbuf[2][kVBufBytes];
+};
+typedef uint32_t QLimbs[kH][4][2][4][4];
+static_assert(sizeof(QLimbs) <= sizeof(WaveValues), "query limbs");
+struct alignas(16) WavePfix {
+    uint32_t pfix[kH][kPfixPitch];
 };
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -226,7 +247,6 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
 // Raw cache bytes of one chunk, as loaded.
 struct ChunkData {
     uint4 k[4];          // keys: group t, token j, dims 32g..32g+31
-    uint4 v[4];          // values: group t, bytes 16*lane .. 16*lane+15 of its 1 KiB of codes
     uint32_t ks[4];      // key scale (fp16 bits) of group t, token j
     uint32_t vs[4];      // value scale (fp16 bits) of group t, token j
 };
@@ -236,30 +256,12 @@ __device__ __forceinline__ const uint8_t *tile_addr(const uint8_t *base, uint32_
     return base + (uint64_t)phys * stride;
 }
 
-// Loads of one chunk: group t is rows slot0(t) .. slot0(t)+15 of tile t.
-template <int P>
-__device__ __forceinline__ void load_chunk(ChunkData &cd, const uint8_t *const (&kt)[4], const uint8_t *const (&vt)[4],
-                                           uint32_t koff, uint32_t voff, uint32_t soff) {
-    // Opaque copies: the 32-bit lane offsets are then extended next to the
-    // loads, which lets them take the scalar-base + 32-bit-offset form.
-    asm("" : "+v"(koff), "+v"(voff), "+v"(soff));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        constexpr int kScaleBase = P * kCodeBytesPerRow;
-        const int slot0 = (16 * t) % P;
-        cd.k[t] = stream_load16(kt[t] + slot0 * kCodeBytesPerRow + koff);
-        cd.v[t] = stream_load16(vt[t] + slot0 * kCodeBytesPerRow + voff);
-        cd.ks[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(kt[t] + kScaleBase + 2 * slot0 + soff));
-        cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(vt[t] + kScaleBase + 2 * slot0 + soff));
-    }
-}
-
 // One work range: tokens [p0 P, min(p1 P, L)) of sequence b (p0 on a chunk
 // boundary) for head slot (KV head hk, query-head chunk chunk_id).  Writes
 // the partial softmax state of query head qh0 + g to unit u0 + g * head_stride
 // of the workspace (o: kHeadDim floats, then (max, sum) in ws_ml).
 template <int BH, int P>
-__device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh, const int lane, const int b,
+__device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv, WavePfix &sp, const int lane, const int b,
                                              const int hk, const int chunk_id, const int L, const int p0,
                                              const int p1, const int64_t u0, const int64_t head_stride) {
     const int g = lane >> 4;
@@ -276,6 +278,8 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
     int my_page[kPageRegs];
 #pragma unroll
     for (int r = 0; r < kPageRegs; ++r) my_page[r] = (p0 + 64 * r + lane < p1) ? pt[p0 + 64 * r + lane] : 0;
+    // wait for the page numbers here, not inside the chunk loop
+    asm volatile("" ::"v"(my_page[0]), "v"(my_page[1]), "v"(my_page[2]), "v"(my_page[3]));
 
     // ---- setup: rotated query as fixed-point limbs; row g = head g ----
     float qv[8];
@@ -325,6 +329,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
     if (amax > 0.0f) (void)frexpf(amax, &qexp);      // amax < 2^qexp
     const float qmul = ldexpf(1.0f, 20 - qexp);
     int lsum[4] = {0, 0, 0, 0};
+    QLimbs &qlimb = *reinterpret_cast<QLimbs *>(&sv);
     {
         uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]; limb 3 stays 0
 #pragma unroll
@@ -340,8 +345,8 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
         // dim 8j + k sits at lane group j/4, slot 4 (j%4) + k/2 of parity k%2
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sh.qlimb[g][r][0][j >> 2][j & 3] = w[r][0];
-            sh.qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
+            qlimb[g][r][0][j >> 2][j & 3] = w[r][0];
+            qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
         }
     }
     v4i qk_init;    // rows (head g, limbs 0..2, zero row): -8 sum_d L, offset-binary keys
@@ -352,13 +357,17 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
     wave_lds_sync();
     v4i qa0, qa1;   // A operands: row (head j/4, limb j%4), k-slots of group g
     {
-        const uint4 e0 = *reinterpret_cast<const uint4 *>(&sh.qlimb[j >> 2][j & 3][0][g][0]);
-        const uint4 e1 = *reinterpret_cast<const uint4 *>(&sh.qlimb[j >> 2][j & 3][1][g][0]);
+        const uint4 e0 = *reinterpret_cast<const uint4 *>(&qlimb[j >> 2][j & 3][0][g][0]);
+        const uint4 e1 = *reinterpret_cast<const uint4 *>(&qlimb[j >> 2][j & 3][1][g][0]);
         qa0 = v4i{(int)e0.x, (int)e0.y, (int)e0.z, (int)e0.w};
         qa1 = v4i{(int)e1.x, (int)e1.y, (int)e1.z, (int)e1.w};
     }
+    // The query limbs share LDS with the value buffers: their reads must have
+    // completed before the first value load can land there.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::"v"(qa0), "v"(qa1) : "memory");
 
-    // ---- main loop: chunk c computed while chunk c+1 loads ----
+    // ---- main loop state ----
     float m_run = -INFINITY;     // running max (log2 units) of head g, uniform in row g
     float l_lane = 0.0f;         // this lane's part of the running sum
     float o_acc[8];              // head g, dims 16m + j
@@ -375,13 +384,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
     const int last_rel = p1 - 1 - p0;
 
     // Per-lane byte offsets inside a 16-token group: key row j, part g;
-    // value bytes 16 lane; scale of token j.
+    // value piece for LDS slot lane (row lane / 4, swizzled piece); scale of token j.
     const uint32_t koff = j * kCodeBytesPerRow + 16 * g;
-    const uint32_t voff = 16 * lane;
+    const uint32_t voff = 64 * (lane >> 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
     const uint32_t soff = 2 * j;
+    constexpr int kScaleBase = P * kCodeBytesPerRow;
+    struct TileAddrs { const uint8_t *kt[4], *vt[4]; };
     // Chunk c starts at page p0 + c * 64 / P (ranges start on chunk boundaries).
-    auto load = [&](int c, ChunkData &cd) {
-        const uint8_t *kt[4], *vt[4];
+    auto addrs = [&](int c, TileAddrs &ta) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int rel = min(c * (kChunk / P) + (16 * t) / P, last_rel);   // clamp past the end
@@ -389,22 +399,66 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
 #pragma unroll
             for (int r = 1; r < kPageRegs; ++r)
                 if ((rel >> 6) == r) phys = __builtin_amdgcn_readlane(my_page[r], rel & 63);
-            kt[t] = tile_addr(kbase, (uint32_t)phys, page_stride);
-            vt[t] = tile_addr(vbase, (uint32_t)phys, page_stride);
+            ta.kt[t] = tile_addr(kbase, (uint32_t)phys, page_stride);
+            ta.vt[t] = tile_addr(vbase, (uint32_t)phys, page_stride);
         }
-        load_chunk<P>(cd, kt, vt, koff, voff, soff);
+    };
+    // Opaque copies of the lane offsets: they are then extended next to the
+    // loads, which lets them take the scalar-base + 32-bit-offset form.
+    auto load_v = [&](const TileAddrs &ta, int buf) {
+        uint32_t vo = voff;
+        asm("" : "+v"(vo));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            __builtin_amdgcn_global_load_lds((const void *)(ta.vt[t] + ((16 * t) % P) * kCodeBytesPerRow + vo),
+                                             (__attribute__((address_space(3))) void *)&sv.vbuf[buf][vgroup_off(t)],
+                                             16, 0, 2 /* nt */);
+    };
+    auto load_k = [&](const TileAddrs &ta, ChunkData &cd) {
+        uint32_t ko = koff, so = soff;
+        asm("" : "+v"(ko), "+v"(so));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int slot0 = (16 * t) % P;
+            cd.k[t] = stream_load16(ta.kt[t] + slot0 * kCodeBytesPerRow + ko);
+            cd.ks[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.kt[t] + kScaleBase + 2 * slot0 + so));
+        }
+    };
+    auto load_vs = [&](const TileAddrs &ta, ChunkData &cd) {
+        uint32_t so = soff;
+        asm("" : "+v"(so));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int slot0 = (16 * t) % P;
+            cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.vt[t] + kScaleBase + 2 * slot0 + so));
+        }
     };
 
     // TAIL: the chunk may extend past the range's last token (masked).
-    auto compute = [&](int c, ChunkData &cd, auto tail) {
+    auto compute = [&](int c, ChunkData &cd, auto tail, auto pf) {
         constexpr bool TAIL = decltype(tail)::value;
+        constexpr bool PF = decltype(pf)::value;   // prefetch chunk c + 1
         const int T0 = tok_begin + c * kChunk;
-        // Values to LDS first (row r = lane / 4, 16-byte part lane % 4): the
-        // transposed read-back does not depend on the softmax, so its latency
-        // overlaps the q.k work.
+        const int vb = c & 1;
+        // Value columns by transposed 4-bit LDS reads: lane (g, n) points at
+        // the 8-byte word m (dims 16m..16m+15) of token n of group g, and lane
+        // (g, i) receives dim 16m + i of the 16 tokens (token n in nibble n).
+        uint2 vt[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            *reinterpret_cast<uint4 *>(&sh.vtile[t * kVGroupStride + (lane >> 2) * kVRowPitch + 16 * (lane & 3)]) = cd.v[t];
+        for (int m = 0; m < 8; ++m) {
+            const v2i r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(
+                &sv.vbuf[vb][vgroup_off(g) + 16 * (4 * j + ((m >> 1) ^ ((j >> 2) & 3))) + 8 * (m & 1)]));
+            vt[m] = make_uint2(static_cast<uint32_t>(r.x), static_cast<uint32_t>(r.y));
+        }
+
+        // (the reads come before the next chunk's value loads are issued: the
+        // compiler cannot tell the two value buffers apart and waits for every
+        // value load in flight before reading either)
+        TileAddrs ta;
+        if constexpr (PF) {
+            addrs(c + 1, ta);
+            load_v(ta, vb ^ 1);
+        }
 
         // q.k: z[t] = score of head g, token 16t + j (log2 units)
         float z[4];
@@ -422,18 +476,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
             z[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? sc : -INFINITY;
             zmax = fmaxf(zmax, z[t]);
         }
-
-        // Value columns by transposed 4-bit LDS reads: lane (g, n) points at
-        // the 8-byte word m (dims 16m..16m+15) of token n of group g, and lane
-        // (g, i) receives dim 16m + i of the 16 tokens (token n in nibble n).
-        wave_lds_sync();
-        uint2 vt[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const v2i r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(
-                &sh.vtile[g * kVGroupStride + j * kVRowPitch + 8 * m]));
-            vt[m] = make_uint2(static_cast<uint32_t>(r.x), static_cast<uint32_t>(r.y));
-        }
+        if constexpr (PF) load_k(ta, cd);
 
         // online softmax for head g (row g)
         zmax = row_max16_fast(zmax);
@@ -454,6 +497,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
             pv[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? p * half_to_float(cd.vs[t]) : 0.0f;
             pmax = fmaxf(pmax, pv[t]);
         }
+        if constexpr (PF) load_vs(ta, cd);
         pmax = row_max16_nonneg(pmax);
         int pexp = 0;
         if (pmax > 0.0f) (void)frexpf(pmax, &pexp);        // pv < 2^pexp
@@ -463,7 +507,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t F = static_cast<uint32_t>(fmaf(pv[t], pmul, 0.5f));
-            sh.pfix[g][16 * t + j] = F;
+            sp.pfix[g][16 * t + j] = F;
             fsum += static_cast<float>(F);
         }
         // Values enter as offset-binary codes u = c + 8, so sum_t F_t c_t =
@@ -475,7 +519,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
         // dword 0 = tokens 0,2,4,6; 1 = 1,3,5,7; 2 = 8,10,12,14; 3 = 9,11,13,15.
         v4i pa;
         {
-            const uint4 *src = reinterpret_cast<const uint4 *>(&sh.pfix[j >> 2][16 * g]);
+            const uint4 *src = reinterpret_cast<const uint4 *>(&sp.pfix[j >> 2][16 * g]);
             const uint4 f0 = src[0], f1 = src[1], f2 = src[2], f3 = src[3];
             const int limb = j & 3;
             const uint32_t shift = (limb == 3) ? 0u : 14u - 7u * limb;
@@ -499,21 +543,22 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveShared &sh
         }
     };
 
-    // Load then compute, one chunk at a time: with the footprint this small,
-    // five waves fit per SIMD and hide each other's memory latency.  (A
-    // register double buffer costs two waves per SIMD and its waits were
-    // measured to gain nothing.)
+    // Chunk c + 1 loads while chunk c computes: values into the other LDS
+    // buffer (issued first), keys and scales into registers once chunk c's
+    // have been used.  Every chunk before the last is full.
     const int nfull = (tok_end - tok_begin) / kChunk;   // chunks with no masked token
-    for (int c = 0; c < nfull; ++c) {
-        ChunkData buf;
-        load(c, buf);
-        compute(c, buf, std::false_type{});
+    ChunkData buf;
+    if (nchunks > 0) {
+        TileAddrs ta;
+        addrs(0, ta);
+        load_v(ta, 0);
+        load_k(ta, buf);
+        load_vs(ta, buf);
     }
-    if (nfull < nchunks) {
-        ChunkData buf;
-        load(nfull, buf);
-        compute(nfull, buf, std::true_type{});
-    }
+    int c = 0;
+    for (; c + 1 < nchunks; ++c) compute(c, buf, std::false_type{}, std::true_type{});
+    if (c < nfull) compute(c, buf, std::false_type{}, std::false_type{});
+    else if (c < nchunks) compute(c, buf, std::true_type{}, std::false_type{});
 
     // ---- write this range's partial state ----
     const float l_row = row_sum16(l_lane);
@@ -560,9 +605,10 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     if (s < 0) return;
     const int p0 = (s * nch_b / nsplit_b) * kChunkPages;
     const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
-    __shared__ WaveShared shared_all[kWaves];
+    __shared__ WaveValues values[kWaves];
+    __shared__ WavePfix pfix[kWaves];
     const int qh0 = hk * a.group + chunk_id * kH;
-    decode_range<BH, P>(a, shared_all[wave], lane, b, hk, chunk_id, L, p0, p1,
+    decode_range<BH, P>(a, values[wave], pfix[wave], lane, b, hk, chunk_id, L, p0, p1,
                         ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
 }
 
@@ -586,9 +632,10 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
             int32_t prefix[kMaxScanBatch + 1];
             int32_t part[kThreads];
         } scan;
-        WaveShared waves[kWaves];
+        WaveValues waves[kWaves];
     };
     __shared__ Shared sm;
+    __shared__ WavePfix pfix[kWaves];
 
     // Exclusive prefix sums of the per-sequence chunk counts.
     if (B <= 64) {
@@ -672,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
             const int npages = (L + P - 1) / P;
             const int64_t per_head = (int64_t)a.sk_groups + B;   // partial states per head
             const int64_t u0 = ((int64_t)(qd * kWaves + wave) * kH) * per_head + gi + b;
-            decode_range<BH, P>(a, sm.waves[wave], lane, b, hk, chunk_id, L, c0 * kChunkPages,
+            decode_range<BH, P>(a, sm.waves[wave], pfix[wave], lane, b, hk, chunk_id, L, c0 * kChunkPages,
                                 min(c1 * kChunkPages, npages), u0, per_head);
         }
         pb = pb1;
