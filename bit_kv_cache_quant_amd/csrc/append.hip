@@ -12,16 +12,16 @@
 // This file is therefore compiled with -ffp-contract=off, and the pragma below
 // repeats it: no multiply-add may be fused unless written as fmaf.
 //
-// Mapping: 16 lanes own one 128-entry vector (one token, one KV head, K or V),
-// 8 consecutive entries per lane, loaded with one 16-byte load.  A 256-thread
-// block takes 16 consecutive tokens of one (KV head, K or V): when those tokens
-// are consecutive positions of one sequence (a prefill append) their rows land
-// in consecutive slots of the same tile, so the block's code and scale stores
-// cover whole cache lines.  Butterfly spans 1, 2, 4 are done inside a lane,
-// spans 8..64 between lanes of the 16-lane row (lane distance span/8) with DPP
-// lane moves; the absmax is a DPP row reduction.  Each lane then produces one
-// 32-bit word of packed codes (its 8 nibbles), so the 16 lanes write the 64
-// code bytes of the slot with one coalesced store.
+// Mapping: a quad of lanes owns one 128-entry vector (one token, one KV head,
+// K or V); lane q holds the 8-entry chunks 4 i + q (four 16-byte loads).  A
+// 256-thread block takes 64 consecutive tokens of one (KV head, K or V): when
+// those are consecutive positions of one sequence (a prefill append) their
+// rows land in consecutive slots of the same tiles, so the block's code and
+// scale stores cover whole cache lines.  Butterfly span 1 is done while the
+// fp16 input is widened, spans 2, 4, 32, 64 inside a lane, spans 8 and 16
+// between lanes of the quad with DPP operands; the absmax is a DPP quad
+// reduction.  The quad's code words are regrouped through LDS so that each
+// lane stores 16 contiguous bytes of its row.
 //
 // Scale.  s32 = m / 7 is computed as q0 = m * r7, e = fma(-q0, 7, m),
 // q = fma(e, r7, q0) with r7 the fp32 value nearest 1/7; this equals the IEEE
@@ -40,6 +40,8 @@
 // Rounding to an integer is done by adding 1.5 * 2^23 + 8 (round-half-even at
 // unit spacing); the low byte of the sum's bits is then code + 8.
 #pragma clang fp contract(off)
+
+#include <type_traits>
 
 #include "kvq_internal.h"
 
@@ -75,17 +77,74 @@ __device__ __forceinline__ float quad_xor(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
 }
 
+// Span-1 butterfly of two fp16 entries packed in one word, straight from the
+// fp16 bits: (x0 + x1, x0 - x1) in fp32 with one rounding each, via the
+// mixed-precision fma (fp16 operands widened exactly, x0 * 1 + x1 and
+// x1 * -1 + x0): two instructions instead of two conversions and two adds.
+__device__ __forceinline__ void widen_span1(uint32_t w, float &y0, float &y1) {
+    asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(y0) : "v"(w));
+    asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(y1) : "v"(w));
+}
+
+// Butterfly across lanes q and q ^ MASK of the quad, as y += c * y_partner
+// with c = +1 in the lower lane and -1 in the upper one: one fused
+// multiply-add with a DPP operand per entry (the product is exact, so it is
+// the same single rounding as the add or the subtraction).  The upper lane
+// gets the negated result, y_upper - y_lower = -(y_lower - y_upper); the
+// caller tracks that sign per lane.  (The s_nop gives the two wait states a
+// DPP read of a just-written register needs.)
+template <int MASK>
+__device__ __forceinline__ void quad_butterfly8(float &y0, float &y1, float &y2, float &y3, float &y4, float &y5,
+                                                float &y6, float &y7, float c) {
+    if constexpr (MASK == 1) {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(y0), "+v"(y1), "+v"(y2), "+v"(y3), "+v"(y4), "+v"(y5), "+v"(y6), "+v"(y7)
+            : "v"(c));
+    } else {
+        static_assert(MASK == 2, "quad lane distance 1 or 2");
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(y0), "+v"(y1), "+v"(y2), "+v"(y3), "+v"(y4), "+v"(y5), "+v"(y6), "+v"(y7)
+            : "v"(c));
+    }
+}
+
 // One 128-entry vector (token, KV head, K or V) per quad of lanes.  Lane q of
 // the quad holds the 8-entry chunks c = 4 i + q, i = 0..3 (entries 8c..8c+7)
 // in y[8 i + k]: the quad's four 16-byte loads i cover 64 contiguous bytes
 // each, and butterfly spans 1, 2, 4 (inside a chunk) and 32, 64 (chunk bits
 // 2, 3 = i) stay in the lane; spans 8, 16 (chunk bits 0, 1 = q) pair lanes
-// q ^ 1, q ^ 2 of the quad, one DPP move each.
+// q ^ 1, q ^ 2 of the quad.  Span 1 is done while widening the fp16 input.
+// Returns the sign F (+1 or -1) of this lane's results: y holds F times the
+// transform (the lane-pair butterflies leave the upper lane's values negated;
+// every later step is linear, so one sign per lane describes them all).
 template <int BH>
-__device__ __forceinline__ void rotate_chunks(float (&y)[32], int q) {
-    // Spans 1, 2, 4 inside each chunk.
+__device__ __forceinline__ float rotate_chunks(const uint4 (&raw)[4], float (&y)[32], int q) {
 #pragma unroll
-    for (int span = 1; span < 8; span <<= 1) {
+    for (int i = 0; i < 4; ++i) {
+        widen_span1(raw[i].x, y[8 * i + 0], y[8 * i + 1]);
+        widen_span1(raw[i].y, y[8 * i + 2], y[8 * i + 3]);
+        widen_span1(raw[i].z, y[8 * i + 4], y[8 * i + 5]);
+        widen_span1(raw[i].w, y[8 * i + 6], y[8 * i + 7]);
+    }
+    // Spans 2, 4 inside each chunk.
+#pragma unroll
+    for (int span = 2; span < 8; span <<= 1) {
 #pragma unroll
         for (int r = 0; r < 32; ++r) {
             if (r & span) continue;
@@ -95,18 +154,18 @@ __device__ __forceinline__ void rotate_chunks(float (&y)[32], int q) {
             y[r + span] = u - v;
         }
     }
-    // Spans 8, 16: the lower-index lane keeps u + v, the other u - v,
-    // written as p + (+-1) y (the product is exact: one rounding either way).
+    // Spans 8 (lanes q, q ^ 1), then 16 (lanes q, q ^ 2).  After the first,
+    // lanes with q & 1 hold negated values; in the second both partners carry
+    // the same sign, so c = -1 again marks the upper lane, which flips its sign.
+    static_assert(BH >= 32, "the lane-pair spans 8 and 16 are always part of the transform");
+    const float c1 = (q & 1) ? -1.0f : 1.0f;
+    const float c2 = (q & 2) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int m = 1; m <= 2; m <<= 1) {
-        if (8 * m >= BH) break;
-        const float sgn = (q & m) ? -1.0f : 1.0f;
+    for (int i = 0; i < 32; i += 8)
+        quad_butterfly8<1>(y[i], y[i + 1], y[i + 2], y[i + 3], y[i + 4], y[i + 5], y[i + 6], y[i + 7], c1);
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const float p = (m == 1) ? quad_xor<1>(y[r]) : quad_xor<2>(y[r]);
-            y[r] = p + sgn * y[r];
-        }
-    }
+    for (int i = 0; i < 32; i += 8)
+        quad_butterfly8<2>(y[i], y[i + 1], y[i + 2], y[i + 3], y[i + 4], y[i + 5], y[i + 6], y[i + 7], c2);
     // Spans 32, 64: chunk index bits 2, 3 are the register index bits 3, 4.
 #pragma unroll
     for (int span = 8; span < 32; span <<= 1) {
@@ -120,6 +179,7 @@ __device__ __forceinline__ void rotate_chunks(float (&y)[32], int q) {
             y[r + span] = u - v;
         }
     }
+    return c1 * c2;
 }
 
 // A block covers 64 consecutive tokens of one (KV head, K or V): quad g takes
@@ -145,24 +205,25 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
     for (int i = 0; i < 4; ++i) raw[i] = src[4 * i];
 
     float y[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        y[8 * i + 0] = half_bits_to_float(raw[i].x);
-        y[8 * i + 1] = half_bits_to_float(raw[i].x >> 16);
-        y[8 * i + 2] = half_bits_to_float(raw[i].y);
-        y[8 * i + 3] = half_bits_to_float(raw[i].y >> 16);
-        y[8 * i + 4] = half_bits_to_float(raw[i].z);
-        y[8 * i + 5] = half_bits_to_float(raw[i].z >> 16);
-        y[8 * i + 6] = half_bits_to_float(raw[i].w);
-        y[8 * i + 7] = half_bits_to_float(raw[i].w >> 16);
-    }
-
     // 1/sqrt(Bh) is a power of two for Bh = 64: then y * c is exact, and
     // scaling the absmax and the divisor instead of the 128 entries gives the
     // same numbers (the quotient y c / s equals y / (s / c) exactly).
     constexpr bool kExactScale = (BH == 64);
-    if constexpr (BH > 0) {
-        rotate_chunks<BH>(y, q);
+    float sign = 1.0f;   // y holds sign times the rotated vector
+    if constexpr (BH == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[8 * i + 0] = half_bits_to_float(raw[i].x);
+            y[8 * i + 1] = half_bits_to_float(raw[i].x >> 16);
+            y[8 * i + 2] = half_bits_to_float(raw[i].y);
+            y[8 * i + 3] = half_bits_to_float(raw[i].y >> 16);
+            y[8 * i + 4] = half_bits_to_float(raw[i].z);
+            y[8 * i + 5] = half_bits_to_float(raw[i].z >> 16);
+            y[8 * i + 6] = half_bits_to_float(raw[i].w);
+            y[8 * i + 7] = half_bits_to_float(raw[i].w >> 16);
+        }
+    } else {
+        sign = rotate_chunks<BH>(raw, y, q);
         if constexpr (!kExactScale) {
             const float c = inv_sqrt_block<BH>();
 #pragma unroll
@@ -204,34 +265,61 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
             sd = s * 8.0f;              // s / c, exact
             rcp = rcp * 0.125f;         // 1 / (s / c), exact
         }
+        // Dividing the sign-carrying entries by the sign-carrying divisor
+        // gives the quotients of the true ones, exactly (IEEE division and
+        // these steps are odd in the divisor).
+        sd *= sign;
+        rcp *= sign;
     }
+    // With s a normal fp16 value (or 0) |y / s| <= 7 (1 + 2^-11) < 7.5, so
+    // every code lies in [-7, 7] without clamping; only a subnormal scale
+    // (an absmax below 7 * 2^-14) needs the clamp, and a wave takes the
+    // clamping path only if one of its vectors has one.
+    const bool no_clamp = __all(!(s > 0.0f && s < 6.103515625e-05f));
 
     uint8_t *pool = static_cast<uint8_t *>(is_v ? a.v_pool : a.k_pool);
     uint8_t *tile = pool + ((int64_t)page * a.num_kv_heads + h) * a.tile_bytes;
-    uint8_t *row = tile + slot * kCodeBytesPerRow + 4 * q;
+    // The quad's code words pass through LDS so that each lane stores 16
+    // contiguous bytes of the row: lane q holds words q, q + 4, q + 8, q + 12
+    // (chunks 4 i + q) and stores words 4 q .. 4 q + 3, and a wave's store
+    // covers its 16 rows as whole cache lines.
+    __shared__ __attribute__((aligned(16))) uint32_t words[kTokensPerBlock][kCodeBytesPerRow / 4];
+    uint32_t *my_words = words[threadIdx.x >> 2];
+    auto quantize_store = [&](auto clamp) {
+        constexpr bool kClamp = decltype(clamp)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // Codes of chunk 4 i + q: exact quotient, clamp, round half to even by
-        // adding 1.5 * 2^23 + 8 (the low byte of the sum is code + 8); nibble
-        // pairs, then bytes, then xor 0x88 gives two's complement nibbles.
-        uint32_t u[8];
+        for (int i = 0; i < 4; ++i) {
+            // Codes of chunk 4 i + q: exact quotient, clamp, round half to even
+            // by adding 1.5 * 2^23 + 8 (the low byte of the sum is code + 8);
+            // nibble pairs, then bytes, then xor 0x88 gives two's complement
+            // nibbles.
+            uint32_t u[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float yv = y[8 * i + k];
-            const float q0 = yv * rcp;
-            const float e = __builtin_fmaf(-q0, sd, yv);
-            const float qt = __builtin_fmaf(e, rcp, q0);  // == y / s (see header)
-            // Clamping to integer bounds commutes with rounding to an integer.
-            const float qc = __builtin_amdgcn_fmed3f(qt, -8.0f, 7.0f);
-            u[k] = __builtin_bit_cast(uint32_t, qc + 12582920.0f);
+            for (int k = 0; k < 8; ++k) {
+                const float yv = y[8 * i + k];
+                const float q0 = yv * rcp;
+                const float e = __builtin_fmaf(-q0, sd, yv);
+                float qt = __builtin_fmaf(e, rcp, q0);  // == y / s (see header)
+                // Clamping to integer bounds commutes with rounding to an integer.
+                if constexpr (kClamp) qt = __builtin_amdgcn_fmed3f(qt, -8.0f, 7.0f);
+                u[k] = __builtin_bit_cast(uint32_t, qt + 12582920.0f);
+            }
+            uint32_t b[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) b[k] = (u[2 * k + 1] << 4) | u[2 * k];   // low byte: the code pair
+            const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);   // bytes b0.0, b1.0
+            const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);   // b2.0, b3.0 at bytes 2, 3
+            my_words[4 * i + q] = (lo | hi) ^ 0x88888888u;
         }
-        uint32_t b[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) b[k] = (u[2 * k + 1] << 4) | u[2 * k];   // low byte: the code pair
-        const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);   // bytes b0.0, b1.0
-        const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);   // b2.0, b3.0 at bytes 2, 3
-        *reinterpret_cast<uint32_t *>(row + 16 * i) = (lo | hi) ^ 0x88888888u;
-    }
+        // the quad's lanes are in one wave: a wave-level LDS ordering suffices
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        *reinterpret_cast<uint4 *>(tile + slot * kCodeBytesPerRow + 16 * q) =
+            *reinterpret_cast<const uint4 *>(&my_words[4 * q]);
+    };
+    if (no_clamp) quantize_store(std::false_type{});
+    else quantize_store(std::true_type{});
     if (q == 0) {
         *reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot) =
             __builtin_bit_cast(uint16_t, s16);
