@@ -153,6 +153,12 @@ __device__ __forceinline__ int row_sum16_i(int v) {
     return v;
 }
 
+// 2^x with the hardware exponential alone (v_exp_f32, about 1 ulp): the
+// softmax arguments are <= 0, and where the exact result would be an fp32
+// denormal (x < -126) this may give 0 instead, a weight below 2^-126 of the
+// largest one.  -inf gives 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Orders LDS traffic between the lanes of one wave (no cross-wave sharing).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -481,7 +487,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
         // online softmax for head g (row g)
         zmax = row_max16_fast(zmax);
         if (zmax > m_run) {
-            const float alpha = exp2f(m_run - zmax);
+            const float alpha = fast_exp2(m_run - zmax);
             l_lane *= alpha;
 #pragma unroll
             for (int m = 0; m < 8; ++m) o_acc[m] *= alpha;
@@ -491,7 +497,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
         float pmax = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float p = exp2f(z[t] - m_run);          // 0 for masked tokens
+            const float p = fast_exp2(z[t] - m_run);      // 0 for masked tokens
             l_lane += p;
             // masked tokens: p = 0, but their scales may be garbage
             pv[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? p * half_to_float(cd.vs[t]) : 0.0f;
@@ -503,16 +509,17 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
         if (pmax > 0.0f) (void)frexpf(pmax, &pexp);        // pv < 2^pexp
         const float pmul = ldexpf(1.0f, 20 - pexp);
         const float pback = ldexpf(1.0f, pexp - 20);
-        float fsum = 0.0f;   // sum of this lane's fixed-point P (exact: < 2^23)
+        int fsum = 0;   // sum of this lane's fixed-point P (exact: < 2^23)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t F = static_cast<uint32_t>(fmaf(pv[t], pmul, 0.5f));
             sp.pfix[g][16 * t + j] = F;
-            fsum += static_cast<float>(F);
+            fsum += static_cast<int>(F);
         }
         // Values enter as offset-binary codes u = c + 8, so sum_t F_t c_t =
-        // sum_t F_t u_t - 8 sum_t F_t; the second term is one number per head.
-        const float corr = 8.0f * pback * row_sum16(fsum);
+        // sum_t F_t u_t - 8 sum_t F_t; the second term is one number per head
+        // (its integer sum is exact: 64 values below 2^21).
+        const float corr = 8.0f * pback * static_cast<float>(row_sum16_i(fsum));
         wave_lds_sync();
         // A operand of p.v: row (head j/4, limb j%4; limb 3 is zero), tokens
         // of group g in the k-slot order of the transposed value words:
