@@ -212,6 +212,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="main workload only (no extra measurements)")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only the append bandwidth measurement (65,536 tokens in one call), one JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB streaming kernel (counter calibration under rocprofv3 --pmc)")
@@ -229,6 +231,11 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kvq.lib()
+
+    if args.append_only:
+        print(json.dumps({"append": append_measurements(dev, iters=args.steps, warmup=args.warmup,
+                                                        with_decode_time=False)}), flush=True)
+        return 0
 
     if args.calibrate_copy:
         # a plain streaming kernel of known traffic: reads 1 GiB, writes 1 GiB
@@ -365,14 +372,14 @@ def main(argv=None):
     return 0
 
 
-def extra_measurements(dev, args):
-    import numpy as np
+def append_measurements(dev, iters=20, warmup=3, with_decode_time=True):
+    """Append bandwidth: 256 sequences x 256 consecutive tokens in one call
+    (Hadamard block 64 and no rotation), and (with_decode_time) the
+    decode-time append of one token for each of 256 sequences."""
     import torch
     import bit_kv_cache_quant_amd as kvq
     import workloads as wl
     ex = {}
-
-    # Append bandwidth: 256 sequences x 256 consecutive tokens in one call.
     w = wl.c2_stream()
     tb = kvq.page_tile_bytes(w.head_dim, w.page_size)
     kp = torch.zeros((w.num_pages, w.num_kv_heads, tb), dtype=torch.uint8, device=dev)
@@ -384,10 +391,14 @@ def extra_measurements(dev, args):
     T = int(w.append_seq.size)
     nb = append_bytes(T, w.num_kv_heads)
     for bh in (64, 0):
-        ms, med = time_calls(lambda: kvq.kv_quant_append(k, v, seq, pos, pt, kp, vp, w.page_size, bh), 20, 3)
+        ms, med = time_calls(lambda: kvq.kv_quant_append(k, v, seq, pos, pt, kp, vp, w.page_size, bh), iters, warmup)
         ex[f"append_65536tok_bh{bh}"] = {"ms": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
                                          "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
                                          "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    if not with_decode_time:
+        del kp, vp, k, v
+        torch.cuda.empty_cache()
+        return ex
     # decode-time append (1 token per sequence)
     w2 = wl.c2()
     k2, v2 = w2.append_rows(0, dev)
@@ -397,6 +408,15 @@ def extra_measurements(dev, args):
     ex["append_256x1tok_bh64"] = {"ms": round(ms, 5), "tokens_per_s": round(256 / (ms * 1e-3), 1)}
     del kp, vp, k, v
     torch.cuda.empty_cache()
+    return ex
+
+
+def extra_measurements(dev, args):
+    import numpy as np
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
+    ex = append_measurements(dev)
 
     # Rotation on vs off: batch 8 x 131,072 context, page size 32.
     rot = {}
