@@ -1,13 +1,12 @@
-// Paged decode attention on the vector ALUs: split-K partial kernel for the
-// INT4 cache and for the fp16 baseline cache.
+// Paged decode attention on the vector ALUs over the fp16 baseline cache:
+// split-K partial kernel.  (The INT4 cache has its own matrix-core kernel,
+// decode_mfma.hip; this file's earlier INT4 variant was retired.)
 //
 // Method source: "KVキャッシュを4ビットへ — SAW-INT4とシステムを踏まえたINT4量子化",
-// sections "KVキャッシュこそが本当のボトルネックである理由" (attention reads the
-// whole paged cache each decode step; fused attention over paged blocks) and
-// "回転のトリック — ブロック対角アダマール" (R = H/sqrt(Bh) is orthogonal and its
-// own inverse, so rotating the query once replaces un-rotating every key:
-// (R q).(R k) = q.k, and the weighted sum of rotated values is rotated back
-// after the merge, in the combine kernel).
+// section "KVキャッシュこそが本当のボトルネックである理由" (attention reads the
+// whole paged cache each decode step; fused attention over paged blocks).  The
+// baseline cache holds unrotated fp16 keys and values, so there is no
+// rotation here.
 //
 // Work item: (split s, KV head h and a chunk of up to 4 of its query heads,
 // sequence b); 256 threads = 4 waves; wave w walks pages p0+w, p0+w+4, ...
@@ -40,35 +39,6 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 __device__ __forceinline__ float xor16(float v, int mask) { return __shfl_xor(v, mask, 16); }
 
-// In-place block FWHT of a 128-vector spread as 8 entries per lane over 16
-// lanes (entry 8*lane + r), times 1/sqrt(bh).  Query rotation only: any
-// butterfly order is fine here since the result is compared with a tolerance.
-__device__ __forceinline__ void rotate_lane8(float (&y)[8], int lane, int bh) {
-    if (bh <= 0) return;
-#pragma unroll
-    for (int span = 1; span < 8; span <<= 1) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (r & span) continue;
-            const float u = y[r], v = y[r + span];
-            y[r] = u + v;
-            y[r + span] = u - v;
-        }
-    }
-    for (int m = 1; m < bh / 8; m <<= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float p = xor16(y[r], m);
-            y[r] = upper ? (p - y[r]) : (y[r] + p);
-        }
-    }
-    const float c = rsqrtf(static_cast<float>(bh));
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] *= c;
-}
-
-template <bool INT4>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) {
     const int s = blockIdx.x;
     const int hk = blockIdx.y / a.head_chunks;
@@ -103,7 +73,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 #pragma unroll
             for (int r = 0; r < 8; ++r) qr[i][r] = 0.0f;
         }
-        if (INT4) rotate_lane8(qr[i], lane, a.had_block);
 #pragma unroll
         for (int r = 0; r < 8; ++r) qr[i][r] *= a.score_scale;
     }
@@ -126,35 +95,22 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
         const uint8_t *vtile = static_cast<const uint8_t *>(a.v_pool) + (phys * a.num_kv_heads + hk) * a.tile_bytes;
         for (int j = row; j < ntok; j += 4) {
             float kx[8], vx[8];
-            float ks = 1.0f, vs = 1.0f;
-            if constexpr (INT4) {
-                const uint32_t kw = *reinterpret_cast<const uint32_t *>(ktile + j * kCodeBytesPerRow + lane * 4);
-                const uint32_t vw = *reinterpret_cast<const uint32_t *>(vtile + j * kCodeBytesPerRow + lane * 4);
-                ks = half_to_float(*reinterpret_cast<const uint16_t *>(ktile + P * kCodeBytesPerRow + 2 * j));
-                vs = half_to_float(*reinterpret_cast<const uint16_t *>(vtile + P * kCodeBytesPerRow + 2 * j));
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    kx[r] = static_cast<float>(static_cast<int>(((kw >> (4 * r)) & 0xFu) ^ 8u) - 8);
-                    vx[r] = static_cast<float>(static_cast<int>(((vw >> (4 * r)) & 0xFu) ^ 8u) - 8);
-                }
-            } else {
-                const uint4 kr = *reinterpret_cast<const uint4 *>(ktile + ((int64_t)j * kHeadDim + lane * 8) * 2);
-                const uint4 vr = *reinterpret_cast<const uint4 *>(vtile + ((int64_t)j * kHeadDim + lane * 8) * 2);
-                kx[0] = half_to_float(kr.x); kx[1] = half_to_float(kr.x >> 16);
-                kx[2] = half_to_float(kr.y); kx[3] = half_to_float(kr.y >> 16);
-                kx[4] = half_to_float(kr.z); kx[5] = half_to_float(kr.z >> 16);
-                kx[6] = half_to_float(kr.w); kx[7] = half_to_float(kr.w >> 16);
-                vx[0] = half_to_float(vr.x); vx[1] = half_to_float(vr.x >> 16);
-                vx[2] = half_to_float(vr.y); vx[3] = half_to_float(vr.y >> 16);
-                vx[4] = half_to_float(vr.z); vx[5] = half_to_float(vr.z >> 16);
-                vx[6] = half_to_float(vr.w); vx[7] = half_to_float(vr.w >> 16);
-            }
+            const uint4 kr = *reinterpret_cast<const uint4 *>(ktile + ((int64_t)j * kHeadDim + lane * 8) * 2);
+            const uint4 vr = *reinterpret_cast<const uint4 *>(vtile + ((int64_t)j * kHeadDim + lane * 8) * 2);
+            kx[0] = half_to_float(kr.x); kx[1] = half_to_float(kr.x >> 16);
+            kx[2] = half_to_float(kr.y); kx[3] = half_to_float(kr.y >> 16);
+            kx[4] = half_to_float(kr.z); kx[5] = half_to_float(kr.z >> 16);
+            kx[6] = half_to_float(kr.w); kx[7] = half_to_float(kr.w >> 16);
+            vx[0] = half_to_float(vr.x); vx[1] = half_to_float(vr.x >> 16);
+            vx[2] = half_to_float(vr.y); vx[3] = half_to_float(vr.y >> 16);
+            vx[4] = half_to_float(vr.z); vx[5] = half_to_float(vr.z >> 16);
+            vx[6] = half_to_float(vr.w); vx[7] = half_to_float(vr.w >> 16);
 #pragma unroll
             for (int i = 0; i < kH; ++i) {
                 float dot = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) dot = fmaf(qr[i][r], kx[r], dot);
-                const float z = row_sum16(dot) * ks;
+                const float z = row_sum16(dot);
                 if (z > m_run[i]) {
                     const float alpha = exp2f(m_run[i] - z);
                     l_run[i] *= alpha;
@@ -164,9 +120,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
                 }
                 const float pw = exp2f(z - m_run[i]);
                 l_run[i] += pw;
-                const float w = pw * vs;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) o[i][r] = fmaf(w, vx[r], o[i][r]);
+                #pragma unroll
+                for (int r = 0; r < 8; ++r) o[i][r] = fmaf(pw, vx[r], o[i][r]);
             }
         }
     }
@@ -215,13 +170,8 @@ dim3 decode_grid(const DecodeArgs &a) {
 
 }  // namespace
 
-hipError_t launch_decode_int4(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_partial_kernel<true>, decode_grid(a), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_decode_fp16(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_partial_kernel<false>, decode_grid(a), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_partial_kernel, decode_grid(a), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

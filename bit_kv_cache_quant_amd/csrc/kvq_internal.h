@@ -81,7 +81,6 @@ __host__ __device__ inline int32_t balanced_groups(int32_t gmin, int32_t gmax, i
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_append_fp16(const AppendArgs &a, hipStream_t stream);
-hipError_t launch_decode_int4(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fp16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream);
