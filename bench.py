@@ -140,21 +140,31 @@ def build_fp16_cache(w, dev, layer=0):
 
 
 def time_calls(fn, iters, warmup):
-    """Mean GPU time (ms) of fn() over iters calls, events around each call."""
+    """GPU time (ms) of fn(): the mean over iters calls issued back to back
+    between two events (no host gaps between the calls), and the median of
+    iters calls timed one by one with events around each."""
     import torch
     for _ in range(warmup):
         fn()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    mean = a.elapsed_time(b) / iters
     evs = []
     for _ in range(iters):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         fn()
-        b.record()
-        evs.append((a, b))
+        e1.record()
+        evs.append((e0, e1))
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
-    return sum(ts) / len(ts), ts[len(ts) // 2]
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return mean, ts[len(ts) // 2]
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -405,7 +415,8 @@ def append_measurements(dev, iters=20, warmup=3, with_decode_time=True):
     s2 = torch.as_tensor(w2.append_seq, device=dev)
     p2 = torch.as_tensor(w2.append_pos, device=dev)
     ms, med = time_calls(lambda: kvq.kv_quant_append(k2, v2, s2, p2, pt, kp, vp, 16, 64), 50, 5)
-    ex["append_256x1tok_bh64"] = {"ms": round(ms, 5), "tokens_per_s": round(256 / (ms * 1e-3), 1)}
+    ex["append_256x1tok_bh64"] = {"ms": round(ms, 5), "tokens_per_s": round(256 / (ms * 1e-3), 1),
+                                  "single_call_median_ms": round(med, 5)}
     del kp, vp, k, v
     torch.cuda.empty_cache()
     return ex
