@@ -210,8 +210,9 @@ __device__ __forceinline__ float ulimbs_to_float(v4i d) {
 }
 
 // Value codes go from HBM straight to LDS (global_load_lds_dwordx4: lane l
-// of the instruction deposits its 16 bytes at 16 l of a 1 KiB block), two
-// chunks deep, and are read back transposed.  One 16-token group is one 1 KiB
+// of the instruction deposits its 16 bytes at 16 l of a 1 KiB block) and are
+// read back transposed; a chunk's reads come first in its compute step, so
+// the next chunk's values can load into the same buffer right after them.  One 16-token group is one 1 KiB
 // block: 16 rows of 64 code bytes, row n's 16-byte piece p stored in slot
 // 4n + (p ^ ((n >> 2) & 3)).  A transposed read (one 8-byte word from each of
 // the group's 16 rows) then touches 32 distinct banks; the groups start at
@@ -224,20 +225,26 @@ static_assert(vgroup_off(1) >= kVGroupBytes && vgroup_off(2) >= vgroup_off(1) + 
               vgroup_off(3) >= vgroup_off(2) + kVGroupBytes, "value groups overlap");
 constexpr int kPfixPitch = kChunk + 4;                          // dwords per head row
 
-// LDS of one wave, in two arrays of their own so that the compiler can tell
-// the value loads' destination apart from the P hand-off (and waits for the
-// value loads only before reading values):
-//   value space: two chunks of value codes, vbuf[2][kVBufBytes]; at set-up
-//                it holds the query limbs, qlimb[kH][4][2][4][4]
+// LDS of one wave, in arrays of their own so that the compiler can tell the
+// value loads' destination apart from the rest (and waits for the value
+// loads only before reading values):
+//   value space: one chunk of value codes, vbuf[kVBufBytes]; at set-up it
+//                holds the query limbs, qlimb[kH][4][2][4][4]
 //                ([head][limb][parity][lane group][dword]);
-//   P space:     fixed-point P of the current chunk, pfix[kH][kPfixPitch].
+//   P space:     fixed-point P of the current chunk, pfix[kH][kPfixPitch];
+//   held state:  (balanced decode) one partial state kept back until the end
+//                of the wave's range, lane-private: 8 output floats, max, sum.
 struct alignas(16) WaveValues {
-    uint8_t vbuf[2][kVBufBytes];
+    uint8_t vbuf[kVBufBytes];
 };
 typedef uint32_t QLimbs[kH][4][2][4][4];
 static_assert(sizeof(QLimbs) <= sizeof(WaveValues), "query limbs");
 struct alignas(16) WavePfix {
     uint32_t pfix[kH][kPfixPitch];
+};
+struct alignas(16) WaveHeld {
+    float4 o[2][64];     // [half][lane]: o[4 h .. 4 h + 3]
+    float2 ml[64];       // [lane]: (max, sum)
 };
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -262,14 +269,38 @@ __device__ __forceinline__ const uint8_t *tile_addr(const uint8_t *base, uint32_
     return base + (uint64_t)phys * stride;
 }
 
+// Partial softmax state of one work range, as lane (g, j) holds it: head g,
+// dims 16 m + j of the unnormalised output, running max and sum (log2 units).
+struct PartialState {
+    float o[8];
+    float m, l;
+};
+
+// Writes the state of query head qh0 + g to unit u0 + g * head_stride of the
+// workspace (o: kHeadDim floats, then (max, sum) in ws_ml).
+__device__ __forceinline__ void write_partial(const DecodeArgs &a, const PartialState &st, const int lane,
+                                              const int nheads, const int64_t u0, const int64_t head_stride) {
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    if (g < nheads) {
+        const int64_t unit = u0 + g * head_stride;
+        float *dst = a.ws_o + unit * kHeadDim + j;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dst[16 * m] = st.o[m];
+        if (j == 0) {
+            a.ws_ml[unit * 2 + 0] = st.m;
+            a.ws_ml[unit * 2 + 1] = st.l;
+        }
+    }
+}
+
 // One work range: tokens [p0 P, min(p1 P, L)) of sequence b (p0 on a chunk
-// boundary) for head slot (KV head hk, query-head chunk chunk_id).  Writes
-// the partial softmax state of query head qh0 + g to unit u0 + g * head_stride
-// of the workspace (o: kHeadDim floats, then (max, sum) in ws_ml).
+// boundary) for head slot (KV head hk, query-head chunk chunk_id); returns
+// its partial softmax state.
 template <int BH, int P>
-__device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv, WavePfix &sp, const int lane, const int b,
-                                             const int hk, const int chunk_id, const int L, const int p0,
-                                             const int p1, const int64_t u0, const int64_t head_stride) {
+__device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveValues &sv, WavePfix &sp,
+                                                     const int lane, const int b, const int hk,
+                                                     const int chunk_id, const int L, const int p0, const int p1) {
     const int g = lane >> 4;
     const int j = lane & 15;
     const int tok_begin = p0 * P;
@@ -411,13 +442,13 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
     };
     // Opaque copies of the lane offsets: they are then extended next to the
     // loads, which lets them take the scalar-base + 32-bit-offset form.
-    auto load_v = [&](const TileAddrs &ta, int buf) {
+    auto load_v = [&](const TileAddrs &ta) {
         uint32_t vo = voff;
         asm("" : "+v"(vo));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             __builtin_amdgcn_global_load_lds((const void *)(ta.vt[t] + ((16 * t) % P) * kCodeBytesPerRow + vo),
-                                             (__attribute__((address_space(3))) void *)&sv.vbuf[buf][vgroup_off(t)],
+                                             (__attribute__((address_space(3))) void *)&sv.vbuf[vgroup_off(t)],
                                              16, 0, 2 /* nt */);
     };
     auto load_k = [&](const TileAddrs &ta, ChunkData &cd) {
@@ -445,7 +476,6 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
         constexpr bool TAIL = decltype(tail)::value;
         constexpr bool PF = decltype(pf)::value;   // prefetch chunk c + 1
         const int T0 = tok_begin + c * kChunk;
-        const int vb = c & 1;
         // Value columns by transposed 4-bit LDS reads: lane (g, n) points at
         // the 8-byte word m (dims 16m..16m+15) of token n of group g, and lane
         // (g, i) receives dim 16m + i of the 16 tokens (token n in nibble n).
@@ -453,17 +483,18 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const v2i r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(
-                &sv.vbuf[vb][vgroup_off(g) + 16 * (4 * j + ((m >> 1) ^ ((j >> 2) & 3))) + 8 * (m & 1)]));
+                &sv.vbuf[vgroup_off(g) + 16 * (4 * j + ((m >> 1) ^ ((j >> 2) & 3))) + 8 * (m & 1)]));
             vt[m] = make_uint2(static_cast<uint32_t>(r.x), static_cast<uint32_t>(r.y));
         }
 
-        // (the reads come before the next chunk's value loads are issued: the
-        // compiler cannot tell the two value buffers apart and waits for every
-        // value load in flight before reading either)
+        // The next chunk's values then load into the same buffer: once these
+        // reads have completed (they also come first because the compiler
+        // waits for every value load in flight before any read of the buffer).
         TileAddrs ta;
         if constexpr (PF) {
             addrs(c + 1, ta);
-            load_v(ta, vb ^ 1);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the reads above are done
+            load_v(ta);
         }
 
         // q.k: z[t] = score of head g, token 16t + j (log2 units)
@@ -558,7 +589,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
     if (nchunks > 0) {
         TileAddrs ta;
         addrs(0, ta);
-        load_v(ta, 0);
+        load_v(ta);
         load_k(ta, buf);
         load_vs(ta, buf);
     }
@@ -567,18 +598,12 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, WaveValues &sv
     if (c < nfull) compute(c, buf, std::false_type{}, std::false_type{});
     else if (c < nchunks) compute(c, buf, std::true_type{}, std::false_type{});
 
-    // ---- write this range's partial state ----
-    const float l_row = row_sum16(l_lane);
-    if (g < nheads) {
-        const int64_t unit = u0 + g * head_stride;
-        float *dst = a.ws_o + unit * kHeadDim + j;
+    PartialState st;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) dst[16 * m] = o_acc[m];
-        if (j == 0) {
-            a.ws_ml[unit * 2 + 0] = m_run;
-            a.ws_ml[unit * 2 + 1] = l_row;
-        }
-    }
+    for (int m = 0; m < 8; ++m) st.o[m] = o_acc[m];
+    st.m = m_run;
+    st.l = row_sum16(l_lane);
+    return st;
 }
 
 
@@ -615,8 +640,9 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     __shared__ WaveValues values[kWaves];
     __shared__ WavePfix pfix[kWaves];
     const int qh0 = hk * a.group + chunk_id * kH;
-    decode_range<BH, P>(a, values[wave], pfix[wave], lane, b, hk, chunk_id, L, p0, p1,
-                        ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
+    const PartialState st = decode_range<BH, P>(a, values[wave], pfix[wave], lane, b, hk, chunk_id, L, p0, p1);
+    write_partial(a, st, lane, min(kH, a.group - chunk_id * kH),
+                  ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
 }
 
 // Balanced INT4 decode: the chunks of all sequences, in sequence order, form
@@ -643,6 +669,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
     };
     __shared__ Shared sm;
     __shared__ WavePfix pfix[kWaves];
+    __shared__ WaveHeld held[kWaves];
 
     // Exclusive prefix sums of the per-sequence chunk counts.
     if (B <= 64) {
@@ -715,6 +742,16 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
     const int hk = slot / a.head_chunks;
     const int chunk_id = slot - hk * a.head_chunks;
     constexpr int kChunkPages = kChunk / P;
+    // A range's first partial state, when more pieces follow it, is held in
+    // LDS and written back with the last one at the end of the range: a write
+    // in the middle of the stream of cache reads was measured to cost several
+    // times its size in lost read bandwidth.  (A third piece of one range, rare,
+    // is written at once.)
+    const int nheads = min(kH, a.group - chunk_id * kH);
+    const int64_t per_head = (int64_t)a.sk_groups + B;   // partial states per head
+    const int64_t unit_base = ((int64_t)(qd * kWaves + wave) * kH) * per_head + gi;
+    int64_t held_u0 = -1;
+    WaveHeld &hw = held[wave];
     int pb = pb0;
     for (int b = b0; b < B && pb < end; ++b) {
         const int L = a.context_lens[b];
@@ -724,12 +761,29 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
         const int c1 = min(end, pb1) - pb;
         if (c0 < c1) {
             const int npages = (L + P - 1) / P;
-            const int64_t per_head = (int64_t)a.sk_groups + B;   // partial states per head
-            const int64_t u0 = ((int64_t)(qd * kWaves + wave) * kH) * per_head + gi + b;
-            decode_range<BH, P>(a, sm.waves[wave], pfix[wave], lane, b, hk, chunk_id, L, c0 * kChunkPages,
-                                min(c1 * kChunkPages, npages), u0, per_head);
+            const PartialState st = decode_range<BH, P>(a, sm.waves[wave], pfix[wave], lane, b, hk, chunk_id, L,
+                                                        c0 * kChunkPages, min(c1 * kChunkPages, npages));
+            if (pb1 < end && held_u0 < 0) {
+                // lane-private slots: the lane that writes one reads it back
+                hw.o[0][lane] = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+                hw.o[1][lane] = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+                hw.ml[lane] = make_float2(st.m, st.l);
+                held_u0 = unit_base + b;
+            } else {
+                write_partial(a, st, lane, nheads, unit_base + b, per_head);
+            }
         }
         pb = pb1;
+    }
+    if (held_u0 >= 0) {
+        PartialState st;
+        const float4 o0 = hw.o[0][lane], o1 = hw.o[1][lane];
+        const float2 ml = hw.ml[lane];
+        st.o[0] = o0.x; st.o[1] = o0.y; st.o[2] = o0.z; st.o[3] = o0.w;
+        st.o[4] = o1.x; st.o[5] = o1.y; st.o[6] = o1.z; st.o[7] = o1.w;
+        st.m = ml.x;
+        st.l = ml.y;
+        write_partial(a, st, lane, nheads, held_u0, per_head);
     }
 }
 
