@@ -52,7 +52,7 @@ def _split_bytes(batch, hq, hkv, ctx, P, pps=0):
     chunks = -(-(hq // hkv) // 4)
     if pps <= 0:
         items = batch * hkv * chunks
-        want = 1 if items >= 2048 else -(-2048 // items)
+        want = 1 if items >= 1024 else -(-1024 // items)
         pps = -(-npages // want)
     pps = max(1, min(pps, 2048 // P))
     cp = 64 // P
