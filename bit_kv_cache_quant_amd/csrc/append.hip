@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kBlockThreads) void append_fp16_kernel(AppendArgs a
     const uint4 raw = *reinterpret_cast<const uint4 *>((is_v ? a.v_new : a.k_new) + row * kHeadDim + lane * 8);
     uint16_t *pool = static_cast<uint16_t *>(is_v ? a.v_pool : a.k_pool);
     uint16_t *dst = pool + (((int64_t)page * a.num_kv_heads + h) * a.page_size + slot) * kHeadDim + lane * 8;
-    *reinterpret_cast<uint4 *>(dst) = raw;
+    __builtin_nontemporal_store(v4u{raw.x, raw.y, raw.z, raw.w}, reinterpret_cast<v4u *>(dst));   // as the INT4 codes
 }
 
 dim3 grid_for(const AppendArgs &a) {
