@@ -228,9 +228,10 @@ constexpr int kPfixPitch = kChunk + 4;                          // dwords per he
 // LDS of one wave, in arrays of their own so that the compiler can tell the
 // value loads' destination apart from the rest (and waits for the value
 // loads only before reading values):
-//   value space: one chunk of value codes, vbuf[kVBufBytes]; at set-up it
-//                holds the query limbs, qlimb[kH][4][2][4][4]
-//                ([head][limb][parity][lane group][dword]);
+//   value space: one chunk of value codes, vbuf[kVBufBytes];
+//   query space: the query limbs, qlimb[kH][4][2][4][4]
+//                ([head][limb][parity][lane group][dword]), written and read
+//                at set-up while the range's first chunk already loads;
 //   P space:     fixed-point P of the current chunk, pfix[kH][kPfixPitch];
 //   held state:  (balanced decode) one partial state kept back until the end
 //                of the wave's range, lane-private: 8 output floats, max, sum.
@@ -238,7 +239,9 @@ struct alignas(16) WaveValues {
     uint8_t vbuf[kVBufBytes];
 };
 typedef uint32_t QLimbs[kH][4][2][4][4];
-static_assert(sizeof(QLimbs) <= sizeof(WaveValues), "query limbs");
+struct alignas(16) WaveQuery {
+    QLimbs qlimb;
+};
 struct alignas(16) WavePfix {
     uint32_t pfix[kH][kPfixPitch];
 };
@@ -299,7 +302,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, const Partial
 // its partial softmax state.
 template <int BH, int P>
 __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveValues &sv, WavePfix &sp,
-                                                     const int lane, const int b, const int hk,
+                                                     WaveQuery &sq, const int lane, const int b, const int hk,
                                                      const int chunk_id, const int L, const int p0, const int p1) {
     const int g = lane >> 4;
     const int j = lane & 15;
@@ -315,101 +318,14 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     int my_page[kPageRegs];
 #pragma unroll
     for (int r = 0; r < kPageRegs; ++r) my_page[r] = (p0 + 64 * r + lane < p1) ? pt[p0 + 64 * r + lane] : 0;
+    // The query (lane (g, j) holds dims 8j..8j+7 of head g) loads with the page
+    // numbers, ahead of the first chunk's loads: the counter of loads in
+    // flight drains in order, so the set-up's wait for it leaves those alone.
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (g < nheads)
+        raw = *reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * a.num_q_heads + qh0 + g) * kHeadDim + 8 * j);
     // wait for the page numbers here, not inside the chunk loop
     asm volatile("" ::"v"(my_page[0]), "v"(my_page[1]), "v"(my_page[2]), "v"(my_page[3]));
-
-    // ---- setup: rotated query as fixed-point limbs; row g = head g ----
-    float qv[8];
-    {
-        const int hq = g;  // lane (g, j) holds dims 8j..8j+7 of head g
-        if (hq < nheads) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(
-                a.q + ((int64_t)b * a.num_q_heads + qh0 + hq) * kHeadDim + 8 * j);
-            qv[0] = half_to_float(raw.x); qv[1] = half_to_float(raw.x >> 16);
-            qv[2] = half_to_float(raw.y); qv[3] = half_to_float(raw.y >> 16);
-            qv[4] = half_to_float(raw.z); qv[5] = half_to_float(raw.z >> 16);
-            qv[6] = half_to_float(raw.w); qv[7] = half_to_float(raw.w >> 16);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) qv[r] = 0.0f;
-        }
-        if constexpr (BH > 0) {
-#pragma unroll
-            for (int span = 1; span < 8; span <<= 1) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    if (r & span) continue;
-                    const float u = qv[r], v = qv[r + span];
-                    qv[r] = u + v;
-                    qv[r + span] = u - v;
-                }
-            }
-#pragma unroll
-            for (int m = 1; m < BH / 8; m <<= 1) {
-                const bool upper = (j & m) != 0;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float p = __shfl_xor(qv[r], m, 16);
-                    qv[r] = upper ? (p - qv[r]) : (qv[r] + p);
-                }
-            }
-            const float c = rsqrtf(static_cast<float>(BH));
-#pragma unroll
-            for (int r = 0; r < 8; ++r) qv[r] *= c;
-        }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(qv[r]));
-    amax = row_max16(amax);
-    int qexp = 0;
-    if (amax > 0.0f) (void)frexpf(amax, &qexp);      // amax < 2^qexp
-    const float qmul = ldexpf(1.0f, 20 - qexp);
-    int lsum[4] = {0, 0, 0, 0};
-    QLimbs &qlimb = *reinterpret_cast<QLimbs *>(&sv);
-    {
-        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]; limb 3 stays 0
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int X = static_cast<int>(rintf(qv[k] * qmul));
-            const int limb[3] = {X >> 14, (X >> 7) & 127, X & 127};
-#pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                lsum[r] += limb[r];
-                w[r][k & 1] |= (static_cast<uint32_t>(limb[r]) & 0xFFu) << (8 * (k >> 1));
-            }
-        }
-        // dim 8j + k sits at lane group j/4, slot 4 (j%4) + k/2 of parity k%2
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            qlimb[g][r][0][j >> 2][j & 3] = w[r][0];
-            qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
-        }
-    }
-    v4i qk_init;    // rows (head g, limbs 0..2, zero row): -8 sum_d L, offset-binary keys
-#pragma unroll
-    for (int r = 0; r < 3; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
-    qk_init[3] = 0;
-    const float score_mul = ldexpf(a.score_scale, qexp - 20);   // head g
-    wave_lds_sync();
-    v4i qa0, qa1;   // A operands: row (head j/4, limb j%4), k-slots of group g
-    {
-        const uint4 e0 = *reinterpret_cast<const uint4 *>(&qlimb[j >> 2][j & 3][0][g][0]);
-        const uint4 e1 = *reinterpret_cast<const uint4 *>(&qlimb[j >> 2][j & 3][1][g][0]);
-        qa0 = v4i{(int)e0.x, (int)e0.y, (int)e0.z, (int)e0.w};
-        qa1 = v4i{(int)e1.x, (int)e1.y, (int)e1.z, (int)e1.w};
-    }
-    // The query limbs share LDS with the value buffers: their reads must have
-    // completed before the first value load can land there.
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    asm volatile("" ::"v"(qa0), "v"(qa1) : "memory");
-
-    // ---- main loop state ----
-    float m_run = -INFINITY;     // running max (log2 units) of head g, uniform in row g
-    float l_lane = 0.0f;         // this lane's part of the running sum
-    float o_acc[8];              // head g, dims 16m + j
-#pragma unroll
-    for (int m = 0; m < 8; ++m) o_acc[m] = 0.0f;
 
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
@@ -470,6 +386,104 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.vt[t] + kScaleBase + 2 * slot0 + so));
         }
     };
+
+    // The range's first chunk starts loading before the set-up below, whose
+    // latency (query load, rotation, LDS round trip) it then hides.
+    const int nfull = (tok_end - tok_begin) / kChunk;   // chunks with no masked token
+    ChunkData buf;
+    if (nchunks > 0) {
+        TileAddrs ta;
+        addrs(0, ta);
+        load_v(ta);
+        load_k(ta, buf);
+        load_vs(ta, buf);
+    }
+
+    // ---- setup: rotated query as fixed-point limbs; row g = head g ----
+    float qv[8];
+    {
+        if (g < nheads) {
+            qv[0] = half_to_float(raw.x); qv[1] = half_to_float(raw.x >> 16);
+            qv[2] = half_to_float(raw.y); qv[3] = half_to_float(raw.y >> 16);
+            qv[4] = half_to_float(raw.z); qv[5] = half_to_float(raw.z >> 16);
+            qv[6] = half_to_float(raw.w); qv[7] = half_to_float(raw.w >> 16);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) qv[r] = 0.0f;
+        }
+        if constexpr (BH > 0) {
+#pragma unroll
+            for (int span = 1; span < 8; span <<= 1) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    if (r & span) continue;
+                    const float u = qv[r], v = qv[r + span];
+                    qv[r] = u + v;
+                    qv[r + span] = u - v;
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < BH / 8; m <<= 1) {
+                const bool upper = (j & m) != 0;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float p = __shfl_xor(qv[r], m, 16);
+                    qv[r] = upper ? (p - qv[r]) : (qv[r] + p);
+                }
+            }
+            const float c = rsqrtf(static_cast<float>(BH));
+#pragma unroll
+            for (int r = 0; r < 8; ++r) qv[r] *= c;
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(qv[r]));
+    amax = row_max16(amax);
+    int qexp = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &qexp);      // amax < 2^qexp
+    const float qmul = ldexpf(1.0f, 20 - qexp);
+    int lsum[4] = {0, 0, 0, 0};
+    QLimbs &qlimb = sq.qlimb;
+    {
+        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]; limb 3 stays 0
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int X = static_cast<int>(rintf(qv[k] * qmul));
+            const int limb[3] = {X >> 14, (X >> 7) & 127, X & 127};
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                lsum[r] += limb[r];
+                w[r][k & 1] |= (static_cast<uint32_t>(limb[r]) & 0xFFu) << (8 * (k >> 1));
+            }
+        }
+        // dim 8j + k sits at lane group j/4, slot 4 (j%4) + k/2 of parity k%2
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            qlimb[g][r][0][j >> 2][j & 3] = w[r][0];
+            qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
+        }
+    }
+    v4i qk_init;    // rows (head g, limbs 0..2, zero row): -8 sum_d L, offset-binary keys
+#pragma unroll
+    for (int r = 0; r < 3; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
+    qk_init[3] = 0;
+    const float score_mul = ldexpf(a.score_scale, qexp - 20);   // head g
+    wave_lds_sync();
+    v4i qa0, qa1;   // A operands: row (head j/4, limb j%4), k-slots of group g
+    {
+        const uint4 e0 = *reinterpret_cast<const uint4 *>(&qlimb[j >> 2][j & 3][0][g][0]);
+        const uint4 e1 = *reinterpret_cast<const uint4 *>(&qlimb[j >> 2][j & 3][1][g][0]);
+        qa0 = v4i{(int)e0.x, (int)e0.y, (int)e0.z, (int)e0.w};
+        qa1 = v4i{(int)e1.x, (int)e1.y, (int)e1.z, (int)e1.w};
+    }
+
+    // ---- main loop state ----
+    float m_run = -INFINITY;     // running max (log2 units) of head g, uniform in row g
+    float l_lane = 0.0f;         // this lane's part of the running sum
+    float o_acc[8];              // head g, dims 16m + j
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o_acc[m] = 0.0f;
 
     // TAIL: the chunk may extend past the range's last token (masked).
     auto compute = [&](int c, ChunkData &cd, auto tail, auto pf) {
@@ -581,18 +595,10 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
         }
     };
 
-    // Chunk c + 1 loads while chunk c computes: values into the other LDS
-    // buffer (issued first), keys and scales into registers once chunk c's
-    // have been used.  Every chunk before the last is full.
-    const int nfull = (tok_end - tok_begin) / kChunk;   // chunks with no masked token
-    ChunkData buf;
-    if (nchunks > 0) {
-        TileAddrs ta;
-        addrs(0, ta);
-        load_v(ta);
-        load_k(ta, buf);
-        load_vs(ta, buf);
-    }
+    // Chunk c + 1 loads while chunk c computes: values into the same LDS
+    // buffer once chunk c's have been read back, keys and scales into
+    // registers once chunk c's have been used.  Every chunk before the last
+    // is full.
     int c = 0;
     for (; c + 1 < nchunks; ++c) compute(c, buf, std::false_type{}, std::true_type{});
     if (c < nfull) compute(c, buf, std::false_type{}, std::false_type{});
@@ -639,8 +645,9 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
     const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
     __shared__ WaveValues values[kWaves];
     __shared__ WavePfix pfix[kWaves];
+    __shared__ WaveQuery query[kWaves];
     const int qh0 = hk * a.group + chunk_id * kH;
-    const PartialState st = decode_range<BH, P>(a, values[wave], pfix[wave], lane, b, hk, chunk_id, L, p0, p1);
+    const PartialState st = decode_range<BH, P>(a, values[wave], pfix[wave], query[wave], lane, b, hk, chunk_id, L, p0, p1);
     write_partial(a, st, lane, min(kH, a.group - chunk_id * kH),
                   ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
 }
@@ -669,6 +676,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
     };
     __shared__ Shared sm;
     __shared__ WavePfix pfix[kWaves];
+    __shared__ WaveQuery query[kWaves];
     __shared__ WaveHeld held[kWaves];
 
     // Exclusive prefix sums of the per-sequence chunk counts.
@@ -761,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
         const int c1 = min(end, pb1) - pb;
         if (c0 < c1) {
             const int npages = (L + P - 1) / P;
-            const PartialState st = decode_range<BH, P>(a, sm.waves[wave], pfix[wave], lane, b, hk, chunk_id, L,
+            const PartialState st = decode_range<BH, P>(a, sm.waves[wave], pfix[wave], query[wave], lane, b, hk, chunk_id, L,
                                                         c0 * kChunkPages, min(c1 * kChunkPages, npages));
             if (pb1 < end && held_u0 < 0) {
                 // lane-private slots: the lane that writes one reads it back
