@@ -84,12 +84,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-// Page-table registers per lane: a range has at most kMaxRangeChunks chunks
-// (balanced mode) or kMaxSplitTokens tokens (split mode), i.e. at most 256
-// pages of 16 tokens.
-constexpr int kPageRegs = 4;
-static_assert(kMaxRangeChunks * kChunkTokens / 16 <= 64 * kPageRegs, "page registers");
-static_assert(kMaxSplitTokens / 16 <= 64 * kPageRegs, "page registers");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = kChunkTokens;  // 64 tokens per chunk
 constexpr int kH = kHeadsPerChunk;    // 4 query heads
@@ -312,20 +306,13 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     const int qh0 = hk * a.group + chunk_id * kH;
     const int nheads = min(kH, a.group - chunk_id * kH);
 
-    // Physical pages of this range (at most 64 kPageRegs): lane i holds pages
-    // p0 + 64 r + i.
-    const int32_t *pt = a.page_table + (int64_t)b * a.max_pages_per_seq;
-    int my_page[kPageRegs];
-#pragma unroll
-    for (int r = 0; r < kPageRegs; ++r) my_page[r] = (p0 + 64 * r + lane < p1) ? pt[p0 + 64 * r + lane] : 0;
-    // The query (lane (g, j) holds dims 8j..8j+7 of head g) loads with the page
-    // numbers, ahead of the first chunk's loads: the counter of loads in
-    // flight drains in order, so the set-up's wait for it leaves those alone.
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (g < nheads)
-        raw = *reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * a.num_q_heads + qh0 + g) * kHeadDim + 8 * j);
-    // wait for the page numbers here, not inside the chunk loop
-    asm volatile("" ::"v"(my_page[0]), "v"(my_page[1]), "v"(my_page[2]), "v"(my_page[3]));
+    // The query (lane (g, j) holds dims 8j..8j+7 of head g) loads first, ahead
+    // of the first chunk's loads: the counter of loads in flight drains in
+    // order, so the set-up's wait for it leaves those alone.
+    // (Unconditional, from a valid head, so that the wait for it is exact;
+    // rows beyond the group's heads are zeroed below.)
+    const uint4 raw = *reinterpret_cast<const uint4 *>(
+        a.q + ((int64_t)b * a.num_q_heads + qh0 + min(g, nheads - 1)) * kHeadDim + 8 * j);
 
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
@@ -335,6 +322,17 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     const uint8_t *kbase = kpool + head_off;
     const uint8_t *vbase = vpool + head_off;
     const int last_rel = p1 - 1 - p0;
+    // Page numbers of the range, read with scalar loads (the table is not
+    // written during the call), one chunk ahead of the loads that use them.
+    const __attribute__((address_space(4))) int32_t *pages =
+        (const __attribute__((address_space(4))) int32_t *)(a.page_table + (int64_t)b * a.max_pages_per_seq + p0);
+    struct PageSet { int32_t p[4]; };   // physical page of each 16-token group of a chunk
+    auto fetch_pages = [&](int c) {
+        PageSet ps;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ps.p[t] = pages[min(c * (kChunk / P) + (16 * t) / P, last_rel)];   // clamp past the end
+        return ps;
+    };
 
     // Per-lane byte offsets inside a 16-token group: key row j, part g;
     // value piece for LDS slot lane (row lane / 4, swizzled piece); scale of token j.
@@ -344,16 +342,11 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     constexpr int kScaleBase = P * kCodeBytesPerRow;
     struct TileAddrs { const uint8_t *kt[4], *vt[4]; };
     // Chunk c starts at page p0 + c * 64 / P (ranges start on chunk boundaries).
-    auto addrs = [&](int c, TileAddrs &ta) {
+    auto addrs = [&](const PageSet &ps, TileAddrs &ta) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int rel = min(c * (kChunk / P) + (16 * t) / P, last_rel);   // clamp past the end
-            int32_t phys = __builtin_amdgcn_readlane(my_page[0], rel & 63);
-#pragma unroll
-            for (int r = 1; r < kPageRegs; ++r)
-                if ((rel >> 6) == r) phys = __builtin_amdgcn_readlane(my_page[r], rel & 63);
-            ta.kt[t] = tile_addr(kbase, (uint32_t)phys, page_stride);
-            ta.vt[t] = tile_addr(vbase, (uint32_t)phys, page_stride);
+            ta.kt[t] = tile_addr(kbase, (uint32_t)ps.p[t], page_stride);
+            ta.vt[t] = tile_addr(vbase, (uint32_t)ps.p[t], page_stride);
         }
     };
     // Opaque copies of the lane offsets: they are then extended next to the
@@ -391,9 +384,15 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     // latency (query load, rotation, LDS round trip) it then hides.
     const int nfull = (tok_end - tok_begin) / kChunk;   // chunks with no masked token
     ChunkData buf;
+    PageSet pages_next;   // pages of the chunk whose loads are issued next
     if (nchunks > 0) {
         TileAddrs ta;
-        addrs(0, ta);
+        addrs(fetch_pages(0), ta);
+        pages_next = fetch_pages(1);
+        // Wait for the query here, with the page numbers: once value loads
+        // into LDS are in flight the compiler waits for every load before
+        // using any.
+        asm volatile("" ::"v"(raw.x), "v"(raw.y), "v"(raw.z), "v"(raw.w));
         load_v(ta);
         load_k(ta, buf);
         load_vs(ta, buf);
@@ -490,6 +489,11 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
         constexpr bool TAIL = decltype(tail)::value;
         constexpr bool PF = decltype(pf)::value;   // prefetch chunk c + 1
         const int T0 = tok_begin + c * kChunk;
+        // This chunk's values were loaded into the buffer by DMA, which the
+        // vector-memory counter tracks; wait for it explicitly (vmcnt(0))
+        // rather than trust the compiler to see the DMA write and these reads
+        // as the same memory (it does not always).
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         // Value columns by transposed 4-bit LDS reads: lane (g, n) points at
         // the 8-byte word m (dims 16m..16m+15) of token n of group g, and lane
         // (g, i) receives dim 16m + i of the 16 tokens (token n in nibble n).
@@ -506,7 +510,8 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
         // waits for every value load in flight before any read of the buffer).
         TileAddrs ta;
         if constexpr (PF) {
-            addrs(c + 1, ta);
+            addrs(pages_next, ta);
+            pages_next = fetch_pages(c + 2);
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the reads above are done
             load_v(ta);
         }
