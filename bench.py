@@ -285,17 +285,17 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, events around each kernel phase
-    evs = []
+    # Timed region: K steps.  The only events in it are the two around the
+    # partial kernel (the roofline's launch duration); each event adds a
+    # marker to the stream, so the append and merge phases are timed in a
+    # second pass of K steps after it, with events at every phase boundary.
+    def make_events(n):
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n)) for _ in range(args.steps)]
+        for e in evs:
+            e[-1].record()                # instantiate; the library re-records the decode-phase one
+        return evs
     kvq.set_decode_phase_event(None)
-    phase = []
-    for _ in range(args.steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        em = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        em.record()                       # instantiate; re-recorded by the library
-        phase.append((e0, e1, em, e2))
+    bracket = make_events(2)              # (before the partial kernel, after it)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -303,20 +303,30 @@ def main(argv=None):
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        e0, e1, em, e2 = phase[i]
+        e1, em = bracket[i]
         kvq.set_decode_phase_event(em)
-        e0.record()
         step(ev=(e1,))
-        e2.record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     kvq.set_decode_phase_event(None)
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
+    t_partial = [e1.elapsed_time(em) for e1, em in bracket]
+
+    # phase pass (not timed as a whole): append, partial, merge
+    phase = make_events(4)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e0, e1, e2, em = phase[i]
+        kvq.set_decode_phase_event(em)
+        e0.record()
+        step(ev=(e1,))
+        e2.record()
+    torch.cuda.synchronize()
+    kvq.set_decode_phase_event(None)
     t_append = [p[0].elapsed_time(p[1]) for p in phase]
-    t_partial = [p[1].elapsed_time(p[2]) for p in phase]
-    t_combine = [p[2].elapsed_time(p[3]) for p in phase]
+    t_combine = [p[3].elapsed_time(p[2]) for p in phase]
     mean = lambda xs: sum(xs) / len(xs)
 
     dbytes = decode_bytes(w)
@@ -356,6 +366,8 @@ def main(argv=None):
             "append_tokens_per_s": round(w.batch / (mean(t_append) * 1e-3), 1),
             "decode_ms": round(mean(t_partial) + mean(t_combine), 5),
             "append_ms": round(mean(t_append), 5),
+            "phase_times": "partial kernel: events in the timed region; append and merge: a second pass of "
+                           "the same K steps with events at every phase boundary",
             "host_wall_s": round(wall, 4),
         },
         "roofline": {

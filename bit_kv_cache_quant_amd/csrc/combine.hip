@@ -81,31 +81,64 @@ __device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh
     *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(o0, o1);
 }
 
+// Merge of a unit with at most kFewSplits partial states (the common case
+// with many sequences): lane t loads the (M, l) pair of split t while every
+// lane loads its two dims of every split's o, all in one round of loads (an
+// index past the last split is clamped and its weight is zero); the maxima
+// and sums then come from lane reads, with no cross-lane reduction.
+constexpr int kFewSplits = 8;
+__device__ __forceinline__ void merge_few(const float *ml, const float *po, int nsplit, int t, float &lsum,
+                                          float &o0, float &o1) {
+    const int mine = min(t, nsplit - 1);
+    const float2 mlt = *reinterpret_cast<const float2 *>(ml + 2 * mine);
+    float2 v[kFewSplits];
+#pragma unroll
+    for (int k = 0; k < kFewSplits; ++k)
+        v[k] = *reinterpret_cast<const float2 *>(po + (int64_t)min(k, nsplit - 1) * kHeadDim + 2 * t);
+    float mk[kFewSplits];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFewSplits; ++k) {
+        mk[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlt.x), k));
+        if (k < nsplit) M = fmaxf(M, mk[k]);
+    }
+    lsum = 0.0f;
+    o0 = 0.0f;
+    o1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kFewSplits; ++k) {
+        const float w = k < nsplit ? exp2f(mk[k] - M) : 0.0f;
+        lsum = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlt.y), k)), w, lsum);
+        o0 = fmaf(v[k].x, w, o0);
+        o1 = fmaf(v[k].y, w, o1);
+    }
+}
+
 // NW = 1: 4 units per block, one wave each.  NW = 4 or 16: one unit per block,
 // NW waves each merging every NW-th split.
 template <int NW>
 __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(DecodeArgs a, int rotate_back) {
     constexpr bool WIDE = NW > 1;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loads below
     const int t = threadIdx.x & 63;
     const int unit = WIDE ? blockIdx.x : blockIdx.x * kWaves + wave;   // b * num_q_heads + qh
     if (unit >= a.batch * a.num_q_heads) return;
     const int b = unit / a.num_q_heads;
     float *out = a.out + (int64_t)unit * kHeadDim;
-    const int L = a.context_lens[b];
-    if (L <= 0) {
-        if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
-        return;
-    }
     const int qh = unit - b * a.num_q_heads;
     int nsplit;
-    int64_t first, stride;
+    int64_t first;
     if (a.sk_groups > 0) {
         // Balanced decode: the partial states of (b, qh) come from the ranges
         // g_first .. g_last that meet sequence b, at positions
-        // ((quad * 4 + wave) * 4 + head) * (sk_groups + batch) + g + b.
+        // ((quad * 4 + wave) * 4 + head) * (sk_groups + batch) + g + b.  A
+        // sequence with no chunks (context length <= 0) has none.
         const int tot = a.sk_prefix[a.batch];
         const int pb = a.sk_prefix[b], pb1 = a.sk_prefix[b + 1];
+        if (pb1 == pb || tot <= 0) {   // (tot > 0 whenever pb1 > pb: the test only orders the loads)
+            if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
+            return;
+        }
         const int G = balanced_groups(a.sk_min, a.sk_target, tot);
         const int g_first = (int)((((int64_t)pb + 1) * G - 1) / tot);
         const int g_last = (int)(((int64_t)pb1 * G - 1) / tot);
@@ -114,12 +147,15 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         const int slot = hk * a.head_chunks + chunk_id;
         const int local = (slot % kWaves) * kHeadsPerChunk + (qh - hk * a.group) % kHeadsPerChunk;
         nsplit = g_last - g_first + 1;
-        stride = 1;
         first = ((int64_t)(slot / kWaves) * kWaves * kHeadsPerChunk + local) * (a.sk_groups + a.batch) + g_first + b;
     } else {
+        const int L = a.context_lens[b];
+        if (L <= 0) {
+            if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
+            return;
+        }
         const int npages = (L + a.page_size - 1) >> a.page_shift;
         nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-        stride = 1;
         first = (int64_t)unit * a.num_splits;
     }
     const float *ml = a.ws_ml + first * 2;
@@ -128,9 +164,10 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
 
     float M, lsum, o0, o1;
     if constexpr (!WIDE) {
-        merge_splits(ml, po, nsplit, stride, 0, 1, t, M, lsum, o0, o1);
+        if (nsplit <= kFewSplits) merge_few(ml, po, nsplit, t, lsum, o0, o1);
+        else merge_splits(ml, po, nsplit, 1, 0, 1, t, M, lsum, o0, o1);
     } else {
-        merge_splits(ml, po, nsplit, stride, wave, NW, t, M, lsum, o0, o1);
+        merge_splits(ml, po, nsplit, 1, wave, NW, t, M, lsum, o0, o1);
         __shared__ float sm[NW], sl[NW];
         __shared__ float so[NW][kHeadDim];
         if (t == 0) {
