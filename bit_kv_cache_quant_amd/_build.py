@@ -20,9 +20,9 @@ OBJDIR = os.path.join(HERE, "_build")
 SOURCES = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
-    "decode_valu.hip": [],
     # MFMA results straight into VGPRs (no accumulator-register copies)
     "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_f16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "combine.hip": [],
 }
 

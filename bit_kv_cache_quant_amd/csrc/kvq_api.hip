@@ -58,7 +58,7 @@ size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, int32_t nsplit) {
     return (size_t)batch * num_q_heads * nsplit * (kHeadDim + 2) * sizeof(float);
 }
 
-// Balanced INT4 decode plan (batch <= kMaxScanBatch).  The chunk total is
+// Balanced decode plan (batch <= kMaxScanBatch).  The chunk total is
 // only known on the device; tot_max = batch * ceil(max_context_len / 64)
 // bounds it, and the launch has enough block groups for any total up to it.
 // Default: between 512 and 1024 blocks over all head quads (two to four per
@@ -221,10 +221,8 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     int32_t pps = 0, nsplit = 0;
     choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
     if (nsplit > 65535 || (int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
-    if (!int4 && batch > 65535) return KVQ_ERR_UNSUPPORTED;   // fp16 kernel: batch is grid z
     BalancedPlan bp;
-    const bool balanced = int4 && balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size,
-                                                pages_per_split, &bp);
+    const bool balanced = balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &bp);
     const size_t need = balanced ? balanced_workspace_bytes(bp, batch) : workspace_bytes_for(batch, num_q_heads, nsplit);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -367,7 +365,7 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int
     int32_t pps = 0, nsplit = 0;
     const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
     choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
-    size_t need = workspace_bytes_for(batch, num_q_heads, nsplit);   // fp16 decode (and large batches)
+    size_t need = workspace_bytes_for(batch, num_q_heads, nsplit);   // split mode
     BalancedPlan bp;
     if (balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &bp)) {
         const size_t nb = balanced_workspace_bytes(bp, batch);

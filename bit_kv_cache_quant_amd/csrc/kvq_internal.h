@@ -12,8 +12,8 @@ constexpr int kCodeBytesPerRow = kHeadDim / 2;
 constexpr int kHeadsPerChunk = 4;      // query heads handled together per KV head
 constexpr int kChunkTokens = 64;       // decode processes tokens in chunks of 64
 constexpr int kMaxSplitTokens = 2048;  // longest page range one decode wave takes (split mode)
-constexpr int kMaxScanBatch = 4096;    // balanced INT4 decode: largest batch one block scans
-constexpr int kMaxRangeChunks = 64;    // balanced INT4 decode: longest work range, in chunks
+constexpr int kMaxScanBatch = 4096;    // balanced decode: largest batch one block scans
+constexpr int kMaxRangeChunks = 64;    // balanced decode: longest work range, in chunks
 
 struct AppendArgs {
     const uint16_t *k_new;
@@ -54,7 +54,7 @@ struct DecodeArgs {
     int32_t pages_per_split;
     int32_t num_splits;
     float score_scale;         // softmax_scale * log2(e): scores are kept in log2 units
-    // Balanced INT4 decode (sk_groups > 0): the concatenated chunk list of all
+    // Balanced decode (sk_groups > 0): the concatenated chunk list of all
     // sequences is cut into equal ranges, one per block group; partial states
     // are indexed by (head quad, range + sequence, wave, head).
     int32_t *sk_prefix;        // [batch + 1] chunk prefix sums (written by the partial kernel)

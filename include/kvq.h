@@ -191,8 +191,8 @@ int kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
 /*
  * paged_decode_attn_fp16 — baseline decode over fp16 pools: the same
  * computation as paged_decode_attn_int4 with unquantized keys and values and
- * no rotation.  Same arguments as paged_decode_attn_int4 without had_block;
- * it always splits each sequence on its own (never across sequences).
+ * no rotation.  Same arguments, split and workspace as paged_decode_attn_int4
+ * without had_block.
  */
 int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                            int64_t num_pages, const int32_t *page_table,

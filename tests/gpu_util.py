@@ -35,10 +35,17 @@ def int4_pools(w: wl.Workload, device, seed: int = 0):
     return canary(shape, 100 + seed, device), canary(shape, 200 + seed, device)
 
 
-def fp16_pools(w: wl.Workload, device):
+def fp16_pools(w: wl.Workload, device, poison: bool = False):
+    """fp16 pools, zero, or (poison) every element a NaN / infinity bit
+    pattern, so that slots no append writes hold values a decode must never
+    let into its result."""
     shape = (w.num_pages, w.num_kv_heads, w.page_size, wl.HEAD_DIM)
     k = torch.zeros(shape, dtype=torch.float16, device=device)
-    return k, torch.zeros_like(k)
+    v = torch.zeros_like(k)
+    if poison:
+        k.view(torch.int16).fill_(0x7E00)          # quiet NaN
+        v.view(torch.int16).fill_(0x7C00)          # +infinity
+    return k, v
 
 
 def prefill(w: wl.Workload, layer: int, device, kp, vp, had_block: int, fp16: bool = False,

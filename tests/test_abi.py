@@ -47,7 +47,7 @@ def test_status_strings_and_tile_bytes():
 
 
 def _split_bytes(batch, hq, hkv, ctx, P, pps=0):
-    """Split-mode workspace (fp16 decode, and INT4 for batches above 4096)."""
+    """Split-mode workspace (batches below 16 or above 4096)."""
     npages = max(1, -(-ctx // P))
     chunks = -(-(hq // hkv) // 4)
     if pps <= 0:
@@ -61,7 +61,7 @@ def _split_bytes(batch, hq, hkv, ctx, P, pps=0):
 
 
 def _balanced_bytes(batch, hq, hkv, ctx, P, pps=0):
-    """Balanced INT4 decode workspace (16 <= batch <= 4096): quads x (groups +
+    """Balanced decode workspace (16 <= batch <= 4096): quads x (groups +
     batch) x 16 partial states of 130 floats, then batch + 1 int32 prefix sums
     (16-byte padded)."""
     if batch < 16 or batch > 4096:

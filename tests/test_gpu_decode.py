@@ -106,21 +106,70 @@ def test_decode_split_invariance(dev):
         assert np.max(np.abs(o - got)) <= bound
 
 
-def test_decode_fp16_baseline(dev):
-    lens = [0, 1, 17, 300, 64]
-    w = wl.small(len(lens), lens, 0, 16, cfg_id=95)
-    kp, vp = fp16_pools(w, dev)
+def _fp16_case(w: wl.Workload, dev, layer=0, pages_per_split=0, poison=False):
+    kp, vp = fp16_pools(w, dev, poison=poison)
     hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
-    prefill(w, 0, dev, kp, vp, 0, fp16=True, host_pools=(hk, hv))
-    append_step(w, 0, dev, kp, vp, 0, fp16=True, host_pools=(hk, hv))
-    q = w.query(0, dev)
-    out = kvq.paged_decode_attn_fp16(q, kp, vp, torch.as_tensor(w.page_table, device=dev),
-                                     torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, w.page_size,
-                                     w.softmax_scale, int(max(lens)))
+    say(f"fp16 prefill {w.name} B={w.batch} P={w.page_size} poison={poison}")
+    prefill(w, layer, dev, kp, vp, 0, fp16=True, host_pools=(hk, hv))
+    append_step(w, layer, dev, kp, vp, 0, fp16=True, host_pools=(hk, hv))
+    assert np.array_equal(kp.cpu().numpy().view(np.uint16), hk.view(np.uint16)), "fp16 K pool differs"
+    assert np.array_equal(vp.cpu().numpy().view(np.uint16), hv.view(np.uint16)), "fp16 V pool differs"
+    q = w.query(layer, dev)
+    pt = torch.as_tensor(w.table(layer), device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    maxctx = int(max(w.context_lens.max(), 0))
+    say(f"fp16 decode {w.name} B={w.batch} maxctx={maxctx} pps={pages_per_split}")
+    out = kvq.paged_decode_attn_fp16(q, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.softmax_scale, maxctx,
+                                     pages_per_split=pages_per_split)
     torch.cuda.synchronize()
-    want = oracle.paged_decode_attn_fp16(q.cpu().numpy(), hk, hv, w.page_table, w.context_lens, w.num_kv_heads,
-                                         w.page_size, w.softmax_scale)
-    _assert_close(out.cpu().numpy(), want)
+    want = oracle.paged_decode_attn_fp16(q.cpu().numpy(), hk, hv, w.table(layer), w.context_lens,
+                                         w.num_kv_heads, w.page_size, w.softmax_scale)
+    return out.cpu().numpy(), want
+
+
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_decode_fp16_baseline(dev, page_size):
+    """Ragged lengths (empty, one token, tails of every kind) with unwritten
+    slots poisoned with NaN keys and infinite values: masked tokens must not
+    reach the result."""
+    lens = [0, 1, 17, 300, 64, 31, 32, 33, 95]
+    w = wl.small(len(lens), lens, 0, page_size, cfg_id=95 + page_size)
+    got, want = _fp16_case(w, dev, poison=True)
+    _assert_close(got, want)
+    assert np.all(got[0] == 0), "a zero-length sequence gives a zero row"
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_fp16_gqa_groups(dev, group):
+    lens = [50, 200, 17]
+    w = wl.small(len(lens), lens, 0, 16, cfg_id=180 + group, num_kv_heads=2, num_q_heads=2 * group)
+    got, want = _fp16_case(w, dev)
+    _assert_close(got, want)
+
+
+@pytest.mark.parametrize("pages_per_split,page_size", [(0, 16), (4, 16), (1, 16), (0, 32), (2, 32)])
+def test_decode_fp16_ranges_cross_sequences(dev, pages_per_split, page_size):
+    """Batches of 16 or more: the fp16 decode uses the INT4 kernel's batch-wide
+    ranges, which run from one sequence into the next."""
+    r = np.random.default_rng(321)
+    lens = [int(x) for x in r.integers(0, 300, size=29)]
+    lens[5] = 0
+    lens[6] = 1
+    w = wl.small(len(lens), lens, 0, page_size, cfg_id=190 + page_size + pages_per_split)
+    got, want = _fp16_case(w, dev, pages_per_split=pages_per_split, poison=True)
+    _assert_close(got, want)
+    assert np.all(got[5] == 0)
+
+
+def test_decode_fp16_split_invariance(dev):
+    lens = [700, 1500, 33]
+    w = wl.small(len(lens), lens, 0, 16, cfg_id=93)
+    got, want = _fp16_case(w, dev)
+    _assert_close(got, want)
+    for pps in (1, 3, 7, 200):
+        o, _ = _fp16_case(w, dev, pages_per_split=pps)
+        bound = 1e-5 * max(1.0, float(np.max(np.abs(got))))
+        assert np.max(np.abs(o - got)) <= bound
 
 
 def test_decode_rotation_off_matches_naive_oracle(dev):
