@@ -16,8 +16,10 @@
 // K or V); lane q holds the 8-entry chunks 4 i + q (four 16-byte loads).  A
 // 256-thread block takes 64 consecutive tokens of one (KV head, K or V): when
 // those are consecutive positions of one sequence (a prefill append) their
-// rows land in consecutive slots of the same tiles, so the block's code and
-// scale stores cover whole cache lines.  Butterfly span 1 is done while the
+// rows land in consecutive slots of the same pages, so the block's code and
+// scale stores cover whole cache lines.  Page layout (include/kvq.h): the
+// code rows of KV heads 0..Hkv-1 ([P][64] bytes each), then the scales of
+// heads 0..Hkv-1 ([P] fp16 each).  Butterfly span 1 is done while the
 // fp16 input is widened, spans 2, 4, 32, 64 inside a lane, spans 8 and 16
 // between lanes of the quad with DPP operands; the absmax is a DPP quad
 // reduction.  The quad's code words are regrouped through LDS so that each
@@ -280,7 +282,10 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
     const bool no_clamp = __all(!(s > 0.0f && s < 6.103515625e-05f));
 
     uint8_t *pool = static_cast<uint8_t *>(is_v ? a.v_pool : a.k_pool);
-    uint8_t *tile = pool + ((int64_t)page * a.num_kv_heads + h) * a.tile_bytes;
+    uint8_t *page_base = pool + (int64_t)page * a.num_kv_heads * a.tile_bytes;
+    uint8_t *code_row = page_base + ((int64_t)h * a.page_size + slot) * kCodeBytesPerRow;
+    uint8_t *scale_at = page_base + (int64_t)a.num_kv_heads * a.page_size * kCodeBytesPerRow +
+                        ((int64_t)h * a.page_size + slot) * 2;
     // The quad's code words pass through LDS so that each lane stores 16
     // contiguous bytes of the row: lane q holds words q, q + 4, q + 8, q + 12
     // (chunks 4 i + q) and stores words 4 q .. 4 q + 3, and a wave's store
@@ -322,13 +327,13 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
         // tokens, where normally cached stores disturb the input stream.
         const uint4 w4 = *reinterpret_cast<const uint4 *>(&my_words[4 * q]);
         __builtin_nontemporal_store(v4u{w4.x, w4.y, w4.z, w4.w},
-                                    reinterpret_cast<v4u *>(tile + slot * kCodeBytesPerRow + 16 * q));
+                                    reinterpret_cast<v4u *>(code_row + 16 * q));
     };
     if (no_clamp) quantize_store(std::false_type{});
     else quantize_store(std::true_type{});
     if (q == 0) {
         __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, s16),   // non-temporal, as the codes
-                                    reinterpret_cast<uint16_t *>(tile + a.page_size * kCodeBytesPerRow + 2 * slot));
+                                    reinterpret_cast<uint16_t *>(scale_at));
     }
 }
 

@@ -257,9 +257,22 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
 // Raw cache bytes of one chunk, as loaded.
 struct ChunkData {
     uint4 k[4];          // keys: group t, token j, dims 32g..32g+31
-    uint32_t ks[4];      // key scale (fp16 bits) of group t, token j
-    uint32_t vs[4];      // value scale (fp16 bits) of group t, token j
+    uint32_t ks;         // key scale (fp16 bits) of group g, token j
+    uint32_t vs;         // value scale (fp16 bits) of group g, token j
 };
+
+// x held by lane (row r, j) of each row of 16 lanes -> y[t] = x of lane
+// (t, j), in every row: one v_permlane16_swap pairs rows (0,1) and (2,3),
+// two v_permlane32_swap pair the halves.
+__device__ __forceinline__ void rows_broadcast(uint32_t x, uint32_t (&y)[4]) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);       // rows r & ~1, r | 1
+    const auto e = __builtin_amdgcn_permlane32_swap(r[0], r[0], false, false);  // rows 0, 2
+    const auto o = __builtin_amdgcn_permlane32_swap(r[1], r[1], false, false);  // rows 1, 3
+    y[0] = e[0];
+    y[1] = o[0];
+    y[2] = e[1];
+    y[3] = o[1];
+}
 
 // Address of tile (page phys) in a pool: base + phys * stride (wave-uniform).
 __device__ __forceinline__ const uint8_t *tile_addr(const uint8_t *base, uint32_t phys, uint32_t stride) {
@@ -316,11 +329,16 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
 
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
-    // Both fit in 32 bits (the host checks num_kv_heads * tile_bytes < 2^31).
-    const uint32_t head_off = (uint32_t)hk * (uint32_t)a.tile_bytes;
+    // A page holds the code rows of every KV head ([P][64] bytes each), then
+    // every head's scales ([P] fp16 each); all fit in 32 bits (the host
+    // checks num_kv_heads * tile_bytes < 2^31).
     const uint32_t page_stride = (uint32_t)a.num_kv_heads * (uint32_t)a.tile_bytes;
-    const uint8_t *kbase = kpool + head_off;
-    const uint8_t *vbase = vpool + head_off;
+    const uint32_t code_off = (uint32_t)hk * (uint32_t)(P * kCodeBytesPerRow);
+    const uint32_t scale_off = (uint32_t)a.num_kv_heads * (uint32_t)(P * kCodeBytesPerRow) + (uint32_t)hk * (2 * P);
+    const uint8_t *kbase = kpool + code_off;
+    const uint8_t *vbase = vpool + code_off;
+    const uint8_t *ksbase = kpool + scale_off;
+    const uint8_t *vsbase = vpool + scale_off;
     const int last_rel = p1 - 1 - p0;
     // Page numbers of the range, read with scalar loads (the table is not
     // written during the call), one chunk ahead of the loads that use them.
@@ -335,12 +353,16 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     };
 
     // Per-lane byte offsets inside a 16-token group: key row j, part g;
-    // value piece for LDS slot lane (row lane / 4, swizzled piece); scale of token j.
+    // value piece for LDS slot lane (row lane / 4, swizzled piece); scale of
+    // token j of group g (the scales of a chunk are two loads, one per
+    // tensor, of 64 distinct tokens, then broadcast across the lane rows).
     const uint32_t koff = j * kCodeBytesPerRow + 16 * g;
     const uint32_t voff = 64 * (lane >> 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t soff = 2 * j;
-    constexpr int kScaleBase = P * kCodeBytesPerRow;
-    struct TileAddrs { const uint8_t *kt[4], *vt[4]; };
+    const uint32_t soff = 2 * ((16 * g) % P + j);
+    struct TileAddrs {
+        const uint8_t *kt[4], *vt[4];   // tile of group t (wave-uniform)
+        const uint8_t *ks, *vs;         // this lane's scale (group g, token j)
+    };
     // Chunk c starts at page p0 + c * 64 / P (ranges start on chunk boundaries).
     auto addrs = [&](const PageSet &ps, TileAddrs &ta) {
 #pragma unroll
@@ -348,6 +370,16 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             ta.kt[t] = tile_addr(kbase, (uint32_t)ps.p[t], page_stride);
             ta.vt[t] = tile_addr(vbase, (uint32_t)ps.p[t], page_stride);
         }
+        // page of group g, selected with bit masks (an indexed pick would go
+        // through scratch memory)
+        int32_t m1 = -(g & 1), m2 = -((g >> 1) & 1);
+        uint32_t so = soff;
+        asm("" : "+v"(so), "+v"(m1), "+v"(m2));
+        const int32_t p01 = ps.p[0] ^ (m1 & (ps.p[0] ^ ps.p[1]));
+        const int32_t p23 = ps.p[2] ^ (m1 & (ps.p[2] ^ ps.p[3]));
+        const int32_t mine = p01 ^ (m2 & (p01 ^ p23));
+        ta.ks = tile_addr(ksbase, (uint32_t)mine, page_stride) + so;
+        ta.vs = tile_addr(vsbase, (uint32_t)mine, page_stride) + so;
     };
     // Opaque copies of the lane offsets: they are then extended next to the
     // loads, which lets them take the scalar-base + 32-bit-offset form.
@@ -361,23 +393,14 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
                                              16, 0, 2 /* nt */);
     };
     auto load_k = [&](const TileAddrs &ta, ChunkData &cd) {
-        uint32_t ko = koff, so = soff;
-        asm("" : "+v"(ko), "+v"(so));
+        uint32_t ko = koff;
+        asm("" : "+v"(ko));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int slot0 = (16 * t) % P;
-            cd.k[t] = stream_load16(ta.kt[t] + slot0 * kCodeBytesPerRow + ko);
-            cd.ks[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.kt[t] + kScaleBase + 2 * slot0 + so));
-        }
+        for (int t = 0; t < 4; ++t) cd.k[t] = stream_load16(ta.kt[t] + ((16 * t) % P) * kCodeBytesPerRow + ko);
+        cd.ks = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.ks));
     };
     auto load_vs = [&](const TileAddrs &ta, ChunkData &cd) {
-        uint32_t so = soff;
-        asm("" : "+v"(so));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int slot0 = (16 * t) % P;
-            cd.vs[t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.vt[t] + kScaleBase + 2 * slot0 + so));
-        }
+        cd.vs = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(ta.vs));
     };
 
     // The range's first chunk starts loading before the set-up below, whose
@@ -517,6 +540,8 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
         }
 
         // q.k: z[t] = score of head g, token 16t + j (log2 units)
+        uint32_t ks[4];   // key scale of token 16t + j
+        rows_broadcast(cd.ks, ks);
         float z[4];
         float zmax = -INFINITY;
 #pragma unroll
@@ -528,7 +553,7 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             split_offset(cd.k[t].w, lo[3], hi[3]);
             v4i d = mfma(qa0, v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]}, qk_init);
             d = mfma(qa1, v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}, d);
-            const float sc = limbs_to_float(d) * score_mul * half_to_float(cd.ks[t]);
+            const float sc = limbs_to_float(d) * score_mul * half_to_float(ks[t]);
             z[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? sc : -INFINITY;
             zmax = fmaxf(zmax, z[t]);
         }
@@ -543,6 +568,8 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             for (int m = 0; m < 8; ++m) o_acc[m] *= alpha;
             m_run = zmax;
         }
+        uint32_t vs[4];   // value scale of token 16t + j
+        rows_broadcast(cd.vs, vs);
         float pv[4];
         float pmax = 0.0f;
 #pragma unroll
@@ -550,7 +577,7 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             const float p = fast_exp2(z[t] - m_run);      // 0 for masked tokens
             l_lane += p;
             // masked tokens: p = 0, but their scales may be garbage
-            pv[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? p * half_to_float(cd.vs[t]) : 0.0f;
+            pv[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? p * half_to_float(vs[t]) : 0.0f;
             pmax = fmaxf(pmax, pv[t]);
         }
         if constexpr (PF) load_vs(ta, cd);

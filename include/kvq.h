@@ -58,10 +58,18 @@
  *                   pos / page_size, slot pos % page_size.
  *   INT4 pools:     uint8 [num_pages][num_kv_heads][tile], one pool for K and
  *                   one for V, tile = page_size*head_dim/2 + 2*page_size bytes
- *                   (1056 for P=16, 2112 for P=32): first page_size rows of
- *                   head_dim/2 code bytes (two's-complement nibbles, element
- *                   2j in the low nibble of byte j), then page_size
- *                   little-endian fp16 scales.
+ *                   (1056 for P=16, 2112 for P=32), the share of one
+ *                   (page, KV head).  One page (num_kv_heads * tile bytes)
+ *                   holds first the code rows of KV heads 0..num_kv_heads-1,
+ *                   page_size rows of head_dim/2 bytes per head (two's-
+ *                   complement nibbles, element 2j in the low nibble of byte
+ *                   j), then the scales of heads 0..num_kv_heads-1, page_size
+ *                   little-endian fp16 per head:
+ *                     code row (h, slot) at  (h * page_size + slot) * head_dim/2
+ *                     scale    (h, slot) at  num_kv_heads * page_size * head_dim/2
+ *                                            + (h * page_size + slot) * 2
+ *                   (every head's codes start on a 1 KiB boundary of the page
+ *                   and the scales of 4 heads share one 128-byte line).
  *   fp16 pools:     fp16 [num_pages][num_kv_heads][page_size][head_dim].
  */
 #ifndef KVQ_H
@@ -85,8 +93,9 @@ enum {
 /* Static, human-readable text for a status code (host function). */
 const char *kvq_status_string(int status);
 
-/* Bytes of one (page, KV head) INT4 tile: page_size*head_dim/2 + 2*page_size.
- * Returns 0 for unsupported arguments. */
+/* Bytes of one (page, KV head) share of an INT4 pool:
+ * page_size*head_dim/2 + 2*page_size (a page is num_kv_heads of these; see
+ * Layouts).  Returns 0 for unsupported arguments. */
 size_t kvq_page_tile_bytes(int32_t head_dim, int32_t page_size);
 
 /*

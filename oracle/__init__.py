@@ -139,7 +139,8 @@ def tile_bytes(head_dim: int, page_size: int) -> int:
 
 def kv_quant_append(k_new, v_new, token_seq, token_pos, page_table, k_pool, v_pool,
                     had_block: int, page_size: int) -> None:
-    """In-place append into uint8 pools [num_pages][Hkv][tile]."""
+    """In-place append into uint8 pools [num_pages][Hkv][tile] (Hkv * tile bytes
+    per page: the code rows of every head, then every head's scales)."""
     k = _as(k_new, np.float16).view(np.uint16)
     v = _as(v_new, np.float16).view(np.uint16)
     T, hkv, d = k.shape
@@ -219,17 +220,20 @@ def dequantize_pool(pool: np.ndarray, page_table, context_len: int, seq: int, he
     pt = _as(page_table, np.int32)
     out = np.zeros((context_len, head_dim), np.float64)
     half = head_dim // 2
+    hkv = pool.shape[1]
     for j in range(context_len):
         page = int(pt[seq, j // page_size])
         slot = j % page_size
-        tile = pool[page, head]
-        row = tile[slot * half:(slot + 1) * half]
+        pg = pool[page].reshape(-1)       # codes of heads 0..hkv-1, then their scales
+        c0 = (head * page_size + slot) * half
+        row = pg[c0:c0 + half]
         lo = (row & 0xF).astype(np.int32)
         hi = (row >> 4).astype(np.int32)
         codes = np.empty(head_dim, np.int32)
         codes[0::2] = np.where(lo >= 8, lo - 16, lo)
         codes[1::2] = np.where(hi >= 8, hi - 16, hi)
-        sb = tile[page_size * half + 2 * slot: page_size * half + 2 * slot + 2]
+        s0 = hkv * page_size * half + (head * page_size + slot) * 2
+        sb = pg[s0:s0 + 2]
         s = float(np.frombuffer(bytes(sb), dtype="<f2")[0])
         out[j] = codes * s
     return out

@@ -234,15 +234,25 @@ int kvq_oracle_quantize_vector(const uint16_t *x, int d, int bh,
 /* ------------------------------------------------------------------------ */
 /* Paged layout ([EXPL] "KVキャッシュこそが..." names the paged layout; the  */
 /* fused-kernel figure appends each token into a paged block).               */
-/* Reading: per (physical page, KV head) one tile of                          */
-/*   codes[P][D/2] bytes followed by scales[P] little-endian fp16;            */
-/* tiles ordered [page][head]; separate pools for K and V.                   */
+/* Reading (the pages fix no byte layout): one physical page of a pool holds */
+/* the code rows of KV heads 0..Hkv-1 ([P][D/2] bytes each), then the scales */
+/* of heads 0..Hkv-1 ([P] little-endian fp16 each): Hkv * tile bytes, with   */
+/* tile = P*D/2 + 2P the share of one (page, head); separate pools for K    */
+/* and V.                                                                    */
 /* The page table is int32 [batch][max_pages_per_seq], logical page ->       */
 /* physical page; token position pos of sequence b lives in logical page     */
 /* pos / P at slot pos % P.                                                  */
 /* ------------------------------------------------------------------------ */
 
 static int64_t tile_bytes(int d, int p) { return (int64_t)p * (d / 2) + 2 * (int64_t)p; }
+
+/* Offsets inside one page of an INT4 pool: the code row and the scale of
+ * (KV head h, slot). */
+static int64_t code_offset(int d, int p, int h, int slot) { return ((int64_t)h * p + slot) * (d / 2); }
+static int64_t scale_offset(int hkv, int d, int p, int h, int slot)
+{
+    return (int64_t)hkv * p * (d / 2) + ((int64_t)h * p + slot) * 2;
+}
 
 int64_t kvq_oracle_tile_bytes(int d, int p) { return tile_bytes(d, p); }
 
@@ -283,16 +293,15 @@ int kvq_oracle_kv_quant_append(const uint16_t *k_new, const uint16_t *v_new,
             for (int which = 0; which < 2; which++) {
                 const uint16_t *src = (which == 0 ? k_new : v_new) +
                                       ((int64_t)t * num_kv_heads + h) * head_dim;
-                uint8_t *tile = (which == 0 ? k_pool : v_pool) +
-                                (page * num_kv_heads + h) * tb;
+                uint8_t *pg = (which == 0 ? k_pool : v_pool) + page * num_kv_heads * tb;
                 uint16_t s16;
                 if (kvq_oracle_quantize_vector(src, head_dim, had_block,
-                                               tile + (int64_t)slot * (head_dim / 2),
+                                               pg + code_offset(head_dim, page_size, h, slot),
                                                &s16) != ORACLE_OK) {
                     bad = 1;
                     continue;
                 }
-                uint8_t *sp = tile + (int64_t)page_size * (head_dim / 2) + 2 * slot;
+                uint8_t *sp = pg + scale_offset(num_kv_heads, head_dim, page_size, h, slot);
                 sp[0] = (uint8_t)(s16 & 0xFF);
                 sp[1] = (uint8_t)(s16 >> 8);
             }
@@ -335,12 +344,13 @@ int kvq_oracle_kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
 /* A context length <= 0 gives a zero output row.                             */
 /* ------------------------------------------------------------------------ */
 
-static double dequant(const uint8_t *tile, int d, int p, int slot, int i)
+/* Element i of (KV head h, slot) of one page pg of an INT4 pool. */
+static double dequant(const uint8_t *pg, int hkv, int h, int d, int p, int slot, int i)
 {
-    uint8_t byte = tile[(int64_t)slot * (d / 2) + i / 2];
+    uint8_t byte = pg[code_offset(d, p, h, slot) + i / 2];
     int nib = (i & 1) ? (byte >> 4) : (byte & 0xF);
     int code = (nib & 8) ? nib - 16 : nib;
-    const uint8_t *sp = tile + (int64_t)p * (d / 2) + 2 * slot;
+    const uint8_t *sp = pg + scale_offset(hkv, d, p, h, slot);
     uint16_t s16 = (uint16_t)(sp[0] | (sp[1] << 8));
     return (double)code * (double)kvq_oracle_f16_to_f32(s16);
 }
@@ -393,8 +403,8 @@ static void fetch_paged(const void *vctx, int j, int which, double *out)
         for (int i = 0; i < c->d; i++) out[i] = (double)kvq_oracle_f16_to_f32(row[i]);
     } else {
         const uint8_t *pool = which == 0 ? c->k_pool : c->v_pool;
-        const uint8_t *tile = pool + (page * c->hkv + c->kvh) * tile_bytes(c->d, c->p);
-        for (int i = 0; i < c->d; i++) out[i] = dequant(tile, c->d, c->p, slot, i);
+        const uint8_t *pg = pool + page * c->hkv * tile_bytes(c->d, c->p);
+        for (int i = 0; i < c->d; i++) out[i] = dequant(pg, c->hkv, c->kvh, c->d, c->p, slot, i);
     }
 }
 

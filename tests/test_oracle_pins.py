@@ -360,9 +360,11 @@ def test_append_under_permuted_page_table_matches_vector_quantizer():
         for h in range(hkv):
             for pool, src in ((kp, k), (vp, v)):
                 codes, s16 = oracle.quantize_vector(src[t, h], 64)
-                tile = pool[page, h]
-                assert np.array_equal(tile[slot * 64:(slot + 1) * 64], codes)
-                assert int(tile[P * 64 + 2 * slot]) | (int(tile[P * 64 + 2 * slot + 1]) << 8) == s16
+                pg = pool[page].reshape(-1)          # codes of both heads, then their scales
+                c0 = (h * P + slot) * 64
+                s0 = hkv * P * 64 + (h * P + slot) * 2
+                assert np.array_equal(pg[c0:c0 + 64], codes)
+                assert int(pg[s0]) | (int(pg[s0 + 1]) << 8) == s16
 
 
 def test_append_rejects_out_of_range_page():
