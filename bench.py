@@ -224,6 +224,8 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="main workload only (no extra measurements)")
     ap.add_argument("--append-only", action="store_true",
                     help="only the append bandwidth measurement (65,536 tokens in one call), one JSON line")
+    ap.add_argument("--fp16-only", action="store_true",
+                    help="only the fp16 baseline decode on the main workload, one JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB streaming kernel (counter calibration under rocprofv3 --pmc)")
@@ -245,6 +247,10 @@ def main(argv=None):
     if args.append_only:
         print(json.dumps({"append": append_measurements(dev, iters=args.steps, warmup=args.warmup,
                                                         with_decode_time=False)}), flush=True)
+        return 0
+    if args.fp16_only:
+        print(json.dumps({"decode_fp16_c4": fp16_measurement(dev, iters=args.steps, warmup=args.warmup)}),
+              flush=True)
         return 0
 
     if args.calibrate_copy:
@@ -481,7 +487,17 @@ def extra_measurements(dev, args):
     del caches
     torch.cuda.empty_cache()
 
-    # fp16 baseline on the main workload.
+    ex["decode_fp16_c4"] = fp16_measurement(dev, iters=10, warmup=2)
+    return ex
+
+
+def fp16_measurement(dev, iters, warmup):
+    """The fp16 baseline decode on the main workload (batch 256, fp16 pools):
+    whole call (partial kernel + merge) and the partial kernel alone (HIP
+    events recorded around it through the library's timing hook)."""
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
     w = wl.c4()
     kp, vp, pt = build_fp16_cache(w, dev)
     q = w.query(0, dev)
@@ -489,14 +505,30 @@ def extra_measurements(dev, args):
     maxctx = int(w.context_lens.max())
     out = torch.empty((w.batch, 32, 128), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.workspace_bytes(w.batch, 32, 8, maxctx, 16), dtype=torch.uint8, device=dev)
-    ms, med = time_calls(lambda: kvq.paged_decode_attn_fp16(q, kp, vp, pt, cl, 8, 16, w.softmax_scale, maxctx,
-                                                            out=out, workspace=ws), 10, 2)
+    call = lambda: kvq.paged_decode_attn_fp16(q, kp, vp, pt, cl, 8, 16, w.softmax_scale, maxctx,
+                                              out=out, workspace=ws)
+    ms, med = time_calls(call, iters, warmup)
+    # partial kernel alone: an event before the call and the library's event after the kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for _, em in evs:
+        em.record()
+    torch.cuda.synchronize()
+    for e0, em in evs:
+        kvq.set_decode_phase_event(em)
+        e0.record()
+        call()
+    torch.cuda.synchronize()
+    kvq.set_decode_phase_event(None)
+    part = sum(e0.elapsed_time(em) for e0, em in evs) / iters
     nb = decode_bytes(w, int4=False)
-    ex["decode_fp16_c4"] = {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
-                            "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    res = {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+           "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+           "partial_kernel_ms": round(part, 5),
+           "partial_kernel_GBps": round(nb / (part * 1e-3) / 1e9, 2),
+           "partial_kernel_pct_of_hbm_peak": round(100 * nb / (part * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
     del kp, vp
     torch.cuda.empty_cache()
-    return ex
+    return res
 
 
 if __name__ == "__main__":
