@@ -64,7 +64,7 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-DECODE_KERNEL_SRC = ("decode_mfma.hip",)
+DECODE_KERNEL_SRC = ("decode_mfma.hip", "decode_common.h")
 DECODE_KERNEL_NAME = "decode_int4_balanced_kernel<64, 16>"
 
 

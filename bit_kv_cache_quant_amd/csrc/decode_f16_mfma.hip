@@ -43,21 +43,20 @@
 //   registers once this step's keys have been used.
 #include <type_traits>
 
-#include "kvq_internal.h"
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
+
+using namespace dec;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;                    // tokens per compute step
 constexpr int kRowBytes = kHeadDim * 2;      // 256 bytes per token row
-constexpr int kH = kHeadsPerChunk;           // 4 query heads per wave
 static_assert(kChunkTokens % kStep == 0, "a schedule chunk is a whole number of steps");
 
 // LDS of one wave: one step's values (32 rows of 256 bytes), and the fp16
@@ -70,69 +69,11 @@ struct alignas(16) F16Weights {
     _Float16 lo[kH][kStep];
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float row_sum16(float v) {
-    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_f<0x141>(v);   // row_half_mirror
-    v += dpp_f<0x140>(v);   // row_mirror
-    return v;
-}
-
-// Row max as a signed-integer max of the order-preserving key
-// b ^ ((b >> 31) & 0x7fffffff) (all non-NaN floats, -inf included).
-__device__ __forceinline__ float row_max16(float v) {
-    const int b = __builtin_bit_cast(int, v);
-    int k = b ^ ((b >> 31) & 0x7fffffff);
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, true));
-    return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff));
-}
-
-// 2^x by the hardware exponential (about 1 ulp; arguments are <= 0, -inf
-// gives 0).
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ v4f mfma(v8h a, v8h b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ v8h as_v8h(uint4 u) { return __builtin_bit_cast(v8h, u); }
-
-// Partial softmax state of one work range as lane (g, j) holds it: head g,
-// dims 16 m + j of the unnormalised output, running max and sum (log2 units).
-struct PartialState {
-    float o[8];
-    float m, l;
-};
-
-__device__ __forceinline__ void write_partial(const DecodeArgs &a, const PartialState &st, const int lane,
-                                              const int nheads, const int64_t u0, const int64_t head_stride) {
-    const int g = lane >> 4;
-    const int j = lane & 15;
-    if (g < nheads) {
-        const int64_t unit = u0 + g * head_stride;
-        float *dst = a.ws_o + unit * kHeadDim + j;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) dst[16 * m] = st.o[m];
-        if (j == 0) {
-            a.ws_ml[unit * 2 + 0] = st.m;
-            a.ws_ml[unit * 2 + 1] = st.l;
-        }
-    }
-}
 
 // One work range: tokens [p0 P, min(p1 P, L)) of sequence b (p0 on a
 // schedule-chunk boundary) for head slot (KV head hk, query-head chunk
@@ -342,119 +283,40 @@ __device__ __forceinline__ PartialState f16_range(const DecodeArgs &a, F16Values
     return st;
 }
 
-// Split mode: block = (sequence, quad of head slots) x page range; one range
-// per wave (the INT4 split kernel's schedule).
+// Split mode: one page range of one sequence per wave (dec::split_item).
 template <int P>
 __global__ __launch_bounds__(kThreads) void decode_f16_mfma_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int head_slots = a.num_kv_heads * a.head_chunks;
-    const int quads = (head_slots + kWaves - 1) / kWaves;
-    const int b = blockIdx.x / quads;
-    const int slot = (blockIdx.x - b * quads) * kWaves + wave;
-    if (slot >= head_slots) return;
-    const int hk = slot / a.head_chunks;
-    const int chunk_id = slot - hk * a.head_chunks;
-    const int L = a.context_lens[b];
-    if (L <= 0) return;
-    const int npages = (L + P - 1) / P;
-    constexpr int kChunkPages = kChunkTokens / P;
-    const int nch_b = (npages + kChunkPages - 1) / kChunkPages;
-    const int nsplit_b = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    const int s = (int)blockIdx.y - (a.num_splits - nsplit_b);
-    if (s < 0) return;
-    const int p0 = (s * nch_b / nsplit_b) * kChunkPages;
-    const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
+    const SplitItem it = split_item<P>(a, wave);
+    if (!it.live) return;
     __shared__ F16Values values[kWaves];
     __shared__ F16Weights weights[kWaves];
-    const int qh0 = hk * a.group + chunk_id * kH;
-    const PartialState st = f16_range<P>(a, values[wave], weights[wave], lane, b, hk, chunk_id, L, p0, p1);
-    write_partial(a, st, lane, min(kH, a.group - chunk_id * kH),
-                  ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
+    const int qh0 = it.hk * a.group + it.chunk_id * kH;
+    const PartialState st = f16_range<P>(a, values[wave], weights[wave], lane, it.b, it.hk, it.chunk_id, it.L,
+                                         it.p0, it.p1);
+    write_partial(a, st, lane, min(kH, a.group - it.chunk_id * kH),
+                  ((int64_t)it.b * a.num_q_heads + qh0) * a.num_splits + it.s, a.num_splits);
 }
 
-// Balanced mode: the chunks (of kChunkTokens) of all sequences, in sequence
-// order, are cut into G equal ranges; block (range gi, head quad) processes
-// range gi for its 4 head slots, one partial state per (sequence it meets,
-// head) at position gi + b of that head's (sk_groups + batch) states (the
-// INT4 balanced kernel's schedule and layout).
+// Balanced mode (batch 16..4096): equal ranges of the batch's concatenated
+// chunks (dec::balanced_range); the block walks every sequence its range
+// meets and writes one partial state per (sequence, head).
 template <int P>
 __global__ __launch_bounds__(kThreads) void decode_f16_balanced_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int B = a.batch;
     union Shared {
-        struct {
-            int32_t prefix[kMaxScanBatch + 1];
-            int32_t part[kThreads];
-        } scan;
+        ScanSpace scan;
         F16Values waves[kWaves];
     };
     __shared__ Shared sm;
     __shared__ F16Weights weights[kWaves];
 
-    // Exclusive prefix sums of the per-sequence chunk counts.
-    if (B <= 64) {
-        if (wave == 0) {
-            const int L = lane < B ? a.context_lens[lane] : 0;
-            const int nch = L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
-            int inc = nch;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int v = __shfl_up(inc, off);
-                if (lane >= off) inc += v;
-            }
-            if (lane < B) sm.scan.prefix[lane] = inc - nch;
-            if (lane == B - 1) sm.scan.prefix[B] = inc;
-        }
-    } else {
-        const int per = (B + kThreads - 1) / kThreads;
-        const int i0 = threadIdx.x * per;
-        const int i1 = min(i0 + per, B);
-        int local = 0;
-        for (int i = i0; i < i1; ++i) {
-            const int L = a.context_lens[i];
-            local += L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
-        }
-        sm.scan.part[threadIdx.x] = local;
-        __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const int v = threadIdx.x >= off ? sm.scan.part[threadIdx.x - off] : 0;
-            __syncthreads();
-            sm.scan.part[threadIdx.x] += v;
-            __syncthreads();
-        }
-        int run = sm.scan.part[threadIdx.x] - local;
-        for (int i = i0; i < i1; ++i) {
-            sm.scan.prefix[i] = run;
-            const int L = a.context_lens[i];
-            run += L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
-        }
-        if (threadIdx.x == kThreads - 1) sm.scan.prefix[B] = sm.scan.part[kThreads - 1];
-    }
-    __syncthreads();
-    const int tot = __builtin_amdgcn_readfirstlane(sm.scan.prefix[B]);
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i <= B; i += kThreads) a.sk_prefix[i] = sm.scan.prefix[i];
-
-    const int G = balanced_groups(a.sk_min, a.sk_target, tot);
-    const int gi = blockIdx.x / a.quads;
-    const int qd = blockIdx.x - gi * a.quads;
-    const int start = (int)(((int64_t)gi * tot) / G);
-    const int end = (int)(((int64_t)(gi + 1) * tot) / G);
-    int b0 = 0;
-    if (tot > 0 && gi < G) {
-        int hi = B;
-        while (hi - b0 > 1) {
-            const int mid = (b0 + hi) >> 1;
-            if (sm.scan.prefix[mid] <= start) b0 = mid;
-            else hi = mid;
-        }
-    }
-    b0 = __builtin_amdgcn_readfirstlane(b0);
-    const int pb0 = __builtin_amdgcn_readfirstlane(sm.scan.prefix[b0]);
-    __syncthreads();   // the scan space becomes the waves' space
-    if (tot == 0 || gi >= G) return;
+    const BlockRange r = balanced_range(a, sm.scan, wave, lane);
+    if (r.tot == 0 || r.gi >= r.G) return;
+    const int qd = r.qd, gi = r.gi, start = r.start, end = r.end, b0 = r.b0, pb0 = r.pb0;
 
     const int head_slots = a.num_kv_heads * a.head_chunks;
     const int slot = qd * kWaves + wave;

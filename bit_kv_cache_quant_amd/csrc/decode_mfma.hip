@@ -75,90 +75,17 @@
 //   All cache bytes are read with non-temporal 16-byte loads.
 #include <type_traits>
 
-#include "kvq_internal.h"
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
 
+using namespace dec;
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = kChunkTokens;  // 64 tokens per chunk
-constexpr int kH = kHeadsPerChunk;    // 4 query heads
-
-__device__ __forceinline__ float half_to_float(uint32_t bits) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
-// All-reduce inside each row of 16 lanes; every lane of the row gets the result.
-__device__ __forceinline__ float row_max16(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
-    return v;
-}
-
-// Row max as an integer max (one DPP-fused instruction per step): float
-// order equals signed-integer order of the key b ^ ((b >> 31) & 0x7fffffff)
-// for all non-NaN floats, -inf included.
-__device__ __forceinline__ int row_max16_key(int k) {
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, true));
-    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, true));
-    return k;
-}
-__device__ __forceinline__ float row_max16_fast(float v) {
-    const int b = __builtin_bit_cast(int, v);
-    const int k = row_max16_key(b ^ ((b >> 31) & 0x7fffffff));
-    return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff));
-}
-// For v >= 0 (no -0, no NaN) the bits themselves order like the values.
-__device__ __forceinline__ float row_max16_nonneg(float v) {
-    return __builtin_bit_cast(float, row_max16_key(__builtin_bit_cast(int, v)));
-}
-
-__device__ __forceinline__ float row_sum16(float v) {
-    v += dpp_f<0xB1>(v);
-    v += dpp_f<0x4E>(v);
-    v += dpp_f<0x141>(v);
-    v += dpp_f<0x140>(v);
-    return v;
-}
-
-__device__ __forceinline__ int row_sum16_i(int v) {
-    v += dpp_i<0xB1>(v);
-    v += dpp_i<0x4E>(v);
-    v += dpp_i<0x141>(v);
-    v += dpp_i<0x140>(v);
-    return v;
-}
-
-// 2^x with the hardware exponential alone (v_exp_f32, about 1 ulp): the
-// softmax arguments are <= 0, and where the exact result would be an fp32
-// denormal (x < -126) this may give 0 instead, a weight below 2^-126 of the
-// largest one.  -inf gives 0.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Orders LDS traffic between the lanes of one wave (no cross-wave sharing).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Low / high nibbles of 8 two's-complement codes as offset-binary bytes
 // (c + 8 = c xor 8 on 4 bits).  Each is one 3-input bitwise op on gfx950
@@ -277,31 +204,6 @@ __device__ __forceinline__ void rows_broadcast(uint32_t x, uint32_t (&y)[4]) {
 // Address of tile (page phys) in a pool: base + phys * stride (wave-uniform).
 __device__ __forceinline__ const uint8_t *tile_addr(const uint8_t *base, uint32_t phys, uint32_t stride) {
     return base + (uint64_t)phys * stride;
-}
-
-// Partial softmax state of one work range, as lane (g, j) holds it: head g,
-// dims 16 m + j of the unnormalised output, running max and sum (log2 units).
-struct PartialState {
-    float o[8];
-    float m, l;
-};
-
-// Writes the state of query head qh0 + g to unit u0 + g * head_stride of the
-// workspace (o: kHeadDim floats, then (max, sum) in ws_ml).
-__device__ __forceinline__ void write_partial(const DecodeArgs &a, const PartialState &st, const int lane,
-                                              const int nheads, const int64_t u0, const int64_t head_stride) {
-    const int g = lane >> 4;
-    const int j = lane & 15;
-    if (g < nheads) {
-        const int64_t unit = u0 + g * head_stride;
-        float *dst = a.ws_o + unit * kHeadDim + j;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) dst[16 * m] = st.o[m];
-        if (j == 0) {
-            a.ws_ml[unit * 2 + 0] = st.m;
-            a.ws_ml[unit * 2 + 1] = st.l;
-        }
-    }
 }
 
 // One work range: tokens [p0 P, min(p1 P, L)) of sequence b (p0 on a chunk
@@ -645,65 +547,37 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
 }
 
 
+// Split mode: one page range of one sequence per wave (dec::split_item).
 template <int BH, int P>
 __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a) {
     // The wave index is uniform across the wave; saying so keeps everything
     // derived from it (head, tile addresses) in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    // blockIdx.x = (sequence, quad of head slots), blockIdx.y = page range;
-    // a head slot is (KV head, chunk of 4 of its query heads).
-    const int head_slots = a.num_kv_heads * a.head_chunks;
-    const int quads = (head_slots + kWaves - 1) / kWaves;
-    const int b = blockIdx.x / quads;
-    const int slot = (blockIdx.x - b * quads) * kWaves + wave;
-    if (slot >= head_slots) return;
-    const int hk = slot / a.head_chunks;
-    const int chunk_id = slot - hk * a.head_chunks;
-    const int L = a.context_lens[b];
-    if (L <= 0) return;
-    const int npages = (L + P - 1) / P;
-    // Page range s of this sequence: its chunks are shared out evenly over
-    // nsplit_b = ceil(npages / pages_per_split) ranges (no short remainder
-    // range), each a whole number of chunks and at most pages_per_split
-    // pages.  Ranges are dispatched with the sequence's last range at the
-    // highest blockIdx.y.
-    constexpr int kChunkPages = kChunk / P;
-    const int nch_b = (npages + kChunkPages - 1) / kChunkPages;
-    const int nsplit_b = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    const int s = (int)blockIdx.y - (a.num_splits - nsplit_b);
-    if (s < 0) return;
-    const int p0 = (s * nch_b / nsplit_b) * kChunkPages;
-    const int p1 = min(((s + 1) * nch_b / nsplit_b) * kChunkPages, npages);
+    const SplitItem it = split_item<P>(a, wave);
+    if (!it.live) return;
     __shared__ WaveValues values[kWaves];
     __shared__ WavePfix pfix[kWaves];
     __shared__ WaveQuery query[kWaves];
-    const int qh0 = hk * a.group + chunk_id * kH;
-    const PartialState st = decode_range<BH, P>(a, values[wave], pfix[wave], query[wave], lane, b, hk, chunk_id, L, p0, p1);
-    write_partial(a, st, lane, min(kH, a.group - chunk_id * kH),
-                  ((int64_t)b * a.num_q_heads + qh0) * a.num_splits + s, a.num_splits);
+    const int qh0 = it.hk * a.group + it.chunk_id * kH;
+    const PartialState st = decode_range<BH, P>(a, values[wave], pfix[wave], query[wave], lane, it.b, it.hk,
+                                                it.chunk_id, it.L, it.p0, it.p1);
+    write_partial(a, st, lane, min(kH, a.group - it.chunk_id * kH),
+                  ((int64_t)it.b * a.num_q_heads + qh0) * a.num_splits + it.s, a.num_splits);
 }
 
-// Balanced INT4 decode: the chunks of all sequences, in sequence order, form
-// one list of TOT chunks that is cut into G equal ranges; block (range gi,
-// head quad q) processes range gi for the 4 head slots of quad q, one
-// partial state per (sequence b it meets, head), stored at position gi + b
-// of that head's (sk_groups + batch) states (so a head's states for one
-// sequence are contiguous).  Every block gets the same
-// amount of cache to stream, whatever the mix of context lengths, so the
-// launch neither waits on a few long work items nor dispatches a second
-// round of them.  Each block first scans the context lengths (batch <=
-// kMaxScanBatch) to find its range.
+// Balanced mode (batch 16..4096): equal ranges of the batch's concatenated
+// chunks (dec::balanced_range); the block walks every sequence its range
+// meets, so every block streams the same amount of cache whatever the mix of
+// context lengths, and the launch neither waits on a few long work items nor
+// dispatches a second round of them.
 template <int BH, int P>
 __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int B = a.batch;
     union Shared {
-        struct {
-            int32_t prefix[kMaxScanBatch + 1];
-            int32_t part[kThreads];
-        } scan;
+        ScanSpace scan;
         WaveValues waves[kWaves];
     };
     __shared__ Shared sm;
@@ -711,70 +585,9 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
     __shared__ WaveQuery query[kWaves];
     __shared__ WaveHeld held[kWaves];
 
-    // Exclusive prefix sums of the per-sequence chunk counts.
-    if (B <= 64) {
-        // one wave: lane i holds sequence i; shuffle scan, no block barriers
-        if (wave == 0) {
-            const int L = lane < B ? a.context_lens[lane] : 0;
-            const int nch = L > 0 ? (L + kChunk - 1) / kChunk : 0;
-            int inc = nch;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int v = __shfl_up(inc, off);
-                if (lane >= off) inc += v;
-            }
-            if (lane < B) sm.scan.prefix[lane] = inc - nch;
-            if (lane == B - 1) sm.scan.prefix[B] = inc;
-        }
-    } else {
-        const int per = (B + kThreads - 1) / kThreads;
-        const int i0 = threadIdx.x * per;
-        const int i1 = min(i0 + per, B);
-        int local = 0;
-        for (int i = i0; i < i1; ++i) {
-            const int L = a.context_lens[i];
-            local += L > 0 ? (L + kChunk - 1) / kChunk : 0;
-        }
-        sm.scan.part[threadIdx.x] = local;
-        __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const int v = threadIdx.x >= off ? sm.scan.part[threadIdx.x - off] : 0;
-            __syncthreads();
-            sm.scan.part[threadIdx.x] += v;
-            __syncthreads();
-        }
-        int run = sm.scan.part[threadIdx.x] - local;
-        for (int i = i0; i < i1; ++i) {
-            sm.scan.prefix[i] = run;
-            const int L = a.context_lens[i];
-            run += L > 0 ? (L + kChunk - 1) / kChunk : 0;
-        }
-        if (threadIdx.x == kThreads - 1) sm.scan.prefix[B] = sm.scan.part[kThreads - 1];
-    }
-    __syncthreads();
-    const int tot = __builtin_amdgcn_readfirstlane(sm.scan.prefix[B]);
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i <= B; i += kThreads) a.sk_prefix[i] = sm.scan.prefix[i];
-
-    const int G = balanced_groups(a.sk_min, a.sk_target, tot);
-    const int gi = blockIdx.x / a.quads;
-    const int qd = blockIdx.x - gi * a.quads;
-    const int start = (int)(((int64_t)gi * tot) / G);
-    const int end = (int)(((int64_t)(gi + 1) * tot) / G);
-    // First sequence of the range: the last b with prefix[b] <= start.
-    int b0 = 0;
-    if (tot > 0 && gi < G) {
-        int hi = B;
-        while (hi - b0 > 1) {
-            const int mid = (b0 + hi) >> 1;
-            if (sm.scan.prefix[mid] <= start) b0 = mid;
-            else hi = mid;
-        }
-    }
-    b0 = __builtin_amdgcn_readfirstlane(b0);   // uniform: keep sequence state scalar
-    const int pb0 = __builtin_amdgcn_readfirstlane(sm.scan.prefix[b0]);
-    __syncthreads();   // the scan space becomes the waves' space
-    if (tot == 0 || gi >= G) return;
+    const BlockRange r = balanced_range(a, sm.scan, wave, lane);
+    if (r.tot == 0 || r.gi >= r.G) return;
+    const int qd = r.qd, gi = r.gi, start = r.start, end = r.end, b0 = r.b0, pb0 = r.pb0;
 
     const int head_slots = a.num_kv_heads * a.head_chunks;
     const int slot = qd * kWaves + wave;
