@@ -13,11 +13,13 @@
 // One wave merges one (sequence, query head): lane t owns dims 2t and 2t+1,
 // so the butterflies of the inverse FWHT are one in-register step (span 1)
 // and lane exchanges (spans 2..64); no LDS and no block barrier on that path.
-// With many splits per sequence (batch 1, long context) 4 or 16 waves share
-// one (sequence, head): each merges every 4th (16th) split, and their partial
-// states are merged once more through LDS.  The merge is latency-bound there
-// (few units), so more waves means fewer dependent load rounds per wave.
-#include "kvq_internal.h"
+// A wave takes its partial states 8 at a time, every load of a round issued
+// before any is used (the merge is latency-bound: few dependent rounds of
+// loads matter more than instruction counts).  With many splits per
+// sequence (batch 1, long context) 4 or 16 waves share one (sequence, head):
+// each merges every 4th (16th) split, and their states are merged once more
+// through LDS.
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
@@ -27,37 +29,54 @@ constexpr int kWaves = kThreads / 64;
 static_assert(kWaves == 4, "the balanced decode's partial layout assumes 4 waves per block");
 constexpr int kWideWaves = 16;     // waves per unit for very many splits
 
-__device__ __forceinline__ float wave_max(float v) {
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+// A unit's partial states are merged kRound at a time: lane k < kRound of a
+// round loads the (max, sum) pair of its state and every lane loads its two
+// output dims of all kRound states, all before any is used; maxima and sums
+// then come from lane reads.  Positions past the unit's states are read
+// clamped to limit - 1 (every position below limit is readable) and never
+// enter the result, so a round can be issued before nsplit is known.
+constexpr int kRound = 8;
+struct Round {
+    float2 mlt;           // (max, sum) of state base + t * step, t < kRound
+    float2 v[kRound];     // output dims 2t, 2t + 1 of states base + k * step
+};
+
+__device__ __forceinline__ Round load_round(const float *ml, const float *po, const int base, const int step,
+                                            const int limit, const int t) {
+    Round r;
+    const int sl = min(base + min(t, kRound - 1) * step, limit - 1);
+    r.mlt = *reinterpret_cast<const float2 *>(ml + 2 * (int64_t)sl);
+#pragma unroll
+    for (int k = 0; k < kRound; ++k)
+        r.v[k] = *reinterpret_cast<const float2 *>(po + (int64_t)min(base + k * step, limit - 1) * kHeadDim + 2 * t);
+    return r;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
-
-// Merge the partial states s0, s0 + step, ... < nsplit of one unit, state s
-// stored at position s * stride: returns (M, l) and o for dims 2t, 2t + 1
-// (relative to M).
-__device__ __forceinline__ void merge_splits(const float *ml, const float *po, int nsplit, int64_t stride, int s0,
-                                             int step, int t, float &M, float &lsum, float &o0, float &o1) {
-    float mloc = -INFINITY;
-    for (int s = s0 + t * step; s < nsplit; s += 64 * step) mloc = fmaxf(mloc, ml[2 * s * stride]);
-    M = wave_max(mloc);
-    float lloc = 0.0f;
-    for (int s = s0 + t * step; s < nsplit; s += 64 * step)
-        lloc = fmaf(ml[2 * s * stride + 1], exp2f(ml[2 * s * stride] - M), lloc);
-    lsum = wave_sum(lloc);
-    o0 = 0.0f;
-    o1 = 0.0f;
-#pragma unroll 8
-    for (int s = s0; s < nsplit; s += step) {
-        const float w = exp2f(ml[2 * s * stride] - M);
-        const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)s * stride * kHeadDim + 2 * t);
-        o0 = fmaf(v.x, w, o0);
-        o1 = fmaf(v.y, w, o1);
+// Folds the states base + k * step < nsplit of round r into (M, l, o0, o1)
+// (M = -inf and everything 0 while no state has been seen; branch-free).
+__device__ __forceinline__ void add_round(const Round &r, const int base, const int step, const int nsplit, float &M,
+                                          float &lsum, float &o0, float &o1) {
+    float mk[kRound], lk[kRound];
+    float Mr = M;
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+        mk[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.mlt.x), k));
+        lk[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.mlt.y), k));
+        if (base + k * step < nsplit) Mr = fmaxf(Mr, mk[k]);
     }
+    const float corr = Mr == -INFINITY ? 1.0f : dec::fast_exp2(M - Mr);
+    lsum *= corr;
+    o0 *= corr;
+    o1 *= corr;
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+        const bool live = base + k * step < nsplit;   // unwritten positions may hold anything
+        const float w = dec::fast_exp2(mk[k] - Mr);
+        lsum = live ? fmaf(lk[k], w, lsum) : lsum;
+        o0 = live ? fmaf(r.v[k].x, w, o0) : o0;
+        o1 = live ? fmaf(r.v[k].y, w, o1) : o1;
+    }
+    M = Mr;
 }
 
 // Inverse rotation of 128 values held as (2t, 2t+1) by lane t, then store.
@@ -81,39 +100,6 @@ __device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh
     *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(o0, o1);
 }
 
-// Merge of a unit with at most kFewSplits partial states (the common case
-// with many sequences): lane t loads the (M, l) pair of split t while every
-// lane loads its two dims of every split's o, all in one round of loads (an
-// index past the last split is clamped and its weight is zero); the maxima
-// and sums then come from lane reads, with no cross-lane reduction.
-constexpr int kFewSplits = 8;
-__device__ __forceinline__ void merge_few(const float *ml, const float *po, int nsplit, int t, float &lsum,
-                                          float &o0, float &o1) {
-    const int mine = min(t, nsplit - 1);
-    const float2 mlt = *reinterpret_cast<const float2 *>(ml + 2 * mine);
-    float2 v[kFewSplits];
-#pragma unroll
-    for (int k = 0; k < kFewSplits; ++k)
-        v[k] = *reinterpret_cast<const float2 *>(po + (int64_t)min(k, nsplit - 1) * kHeadDim + 2 * t);
-    float mk[kFewSplits];
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kFewSplits; ++k) {
-        mk[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlt.x), k));
-        if (k < nsplit) M = fmaxf(M, mk[k]);
-    }
-    lsum = 0.0f;
-    o0 = 0.0f;
-    o1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kFewSplits; ++k) {
-        const float w = k < nsplit ? exp2f(mk[k] - M) : 0.0f;
-        lsum = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlt.y), k)), w, lsum);
-        o0 = fmaf(v[k].x, w, o0);
-        o1 = fmaf(v[k].y, w, o1);
-    }
-}
-
 // NW = 1: 4 units per block, one wave each.  NW = 4 or 16: one unit per block,
 // NW waves each merging every NW-th split.
 template <int NW>
@@ -126,8 +112,10 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
     const int b = unit / a.num_q_heads;
     float *out = a.out + (int64_t)unit * kHeadDim;
     const int qh = unit - b * a.num_q_heads;
-    int nsplit;
-    int64_t first;
+    const int s0 = WIDE ? wave : 0, step = WIDE ? NW : 1;
+    int nsplit, limit;
+    Round r0;   // the first round of this wave's states
+    const float *ml, *po;
     if (a.sk_groups > 0) {
         // Balanced decode: the partial states of (b, qh) come from the ranges
         // g_first .. g_last that meet sequence b, at positions
@@ -147,27 +135,32 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         const int slot = hk * a.head_chunks + chunk_id;
         const int local = (slot % kWaves) * kHeadsPerChunk + (qh - hk * a.group) % kHeadsPerChunk;
         nsplit = g_last - g_first + 1;
-        first = ((int64_t)(slot / kWaves) * kWaves * kHeadsPerChunk + local) * (a.sk_groups + a.batch) + g_first + b;
+        limit = nsplit;
+        const int64_t first =
+            ((int64_t)(slot / kWaves) * kWaves * kHeadsPerChunk + local) * (a.sk_groups + a.batch) + g_first + b;
+        ml = a.ws_ml + first * 2;
+        po = a.ws_o + first * kHeadDim;
+        r0 = load_round(ml, po, s0, step, limit, t);
     } else {
+        // Split mode: the unit owns num_splits positions, the first nsplit of
+        // them written (none if the context is empty); the first round of
+        // loads is issued before the context length is known.
+        const int64_t first = (int64_t)unit * a.num_splits;
+        ml = a.ws_ml + first * 2;
+        po = a.ws_o + first * kHeadDim;
+        limit = a.num_splits;
+        r0 = load_round(ml, po, s0, step, limit, t);
         const int L = a.context_lens[b];
-        if (L <= 0) {
-            if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
-            return;
-        }
         const int npages = (L + a.page_size - 1) >> a.page_shift;
-        nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-        first = (int64_t)unit * a.num_splits;
+        nsplit = L > 0 ? (npages + a.pages_per_split - 1) / a.pages_per_split : 0;
     }
-    const float *ml = a.ws_ml + first * 2;
-    const float *po = a.ws_o + first * kHeadDim;
     const int bh = rotate_back ? a.had_block : 0;
 
-    float M, lsum, o0, o1;
-    if constexpr (!WIDE) {
-        if (nsplit <= kFewSplits) merge_few(ml, po, nsplit, t, lsum, o0, o1);
-        else merge_splits(ml, po, nsplit, 1, 0, 1, t, M, lsum, o0, o1);
-    } else {
-        merge_splits(ml, po, nsplit, 1, wave, NW, t, M, lsum, o0, o1);
+    float M = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    add_round(r0, s0, step, nsplit, M, lsum, o0, o1);
+    for (int base = s0 + kRound * step; base < nsplit; base += kRound * step)
+        add_round(load_round(ml, po, base, step, limit, t), base, step, nsplit, M, lsum, o0, o1);
+    if constexpr (WIDE) {
         __shared__ float sm[NW], sl[NW];
         __shared__ float so[NW][kHeadDim];
         if (t == 0) {
@@ -186,11 +179,15 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         o1 = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float f = (sm[w] == -INFINITY) ? 0.0f : exp2f(sm[w] - M);
+            const float f = (sm[w] == -INFINITY) ? 0.0f : dec::fast_exp2(sm[w] - M);
             lsum = fmaf(sl[w], f, lsum);
             o0 = fmaf(so[w][2 * t], f, o0);
             o1 = fmaf(so[w][2 * t + 1], f, o1);
         }
+    }
+    if (nsplit == 0) {   // empty context: a zero row
+        *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
+        return;
     }
     const float inv = 1.0f / lsum;
     rotate_back_and_store(o0 * inv, o1 * inv, bh, t, out);
@@ -202,11 +199,12 @@ hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t str
     const int units = a.batch * a.num_q_heads;
     const int rb = rotate_back ? 1 : 0;
     // Many splits per sequence (long context, small batch): spread each unit's
-    // splits over 4 or 16 waves; otherwise one wave per unit.
+    // splits over 4 or 16 waves, so that a wave merges about one round
+    // (kRound states); otherwise one wave per unit.
     const int per_unit = a.sk_groups > 0 ? a.sk_groups / a.batch + 2 : a.num_splits;
-    if (per_unit >= 128) {
+    if (per_unit > 4 * kRound) {
         hipLaunchKernelGGL(combine_kernel<kWideWaves>, dim3((unsigned)units), dim3(64 * kWideWaves), 0, stream, a, rb);
-    } else if (per_unit >= 32) {
+    } else if (per_unit > kRound) {
         hipLaunchKernelGGL(combine_kernel<kWaves>, dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
     } else {
         hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
