@@ -223,8 +223,14 @@ __device__ __forceinline__ BlockRange balanced_range(const DecodeArgs &a, ScanSp
         for (int i = threadIdx.x; i <= B; i += kThreads) a.sk_prefix[i] = sp.prefix[i];
 
     r.G = balanced_groups(a.sk_min, a.sk_target, r.tot);
-    r.gi = blockIdx.x / a.quads;
-    r.qd = blockIdx.x - r.gi * a.quads;
+    // Blocks go to the 8 XCDs in turn (block i to XCD i % 8); with the grid
+    // a multiple of 8, logical block (i % 8) * (grid / 8) + i / 8 keeps the
+    // head quads of one range and consecutive ranges on one XCD, whose L2
+    // then serves their shared page-table lines (measured: 0.6% faster).
+    int lb = blockIdx.x;
+    if ((gridDim.x & 7) == 0) lb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    r.gi = lb / a.quads;
+    r.qd = lb - r.gi * a.quads;
     r.start = (int)(((int64_t)r.gi * r.tot) / r.G);
     r.end = (int)(((int64_t)(r.gi + 1) * r.tot) / r.G);
     // First sequence of the range: the last b with prefix[b] <= start.
