@@ -174,7 +174,7 @@ def cpu_baseline(w, budget_s=12.0):
     import oracle
     import workloads as wl
 
-    def run(S):
+    def run(S, reps=1):
         sub_need = (w.context_lens[:S] + w.page_size - 1) // w.page_size
         npg = int(sub_need.sum())
         pt = np.full((S, int(sub_need.max())), -1, np.int32)
@@ -194,25 +194,29 @@ def cpu_baseline(w, budget_s=12.0):
         v_new = np.stack([w.rows(0, b, int(w.append_pos[b]), 1, "cpu")[1].numpy()[0] for b in range(S)])
         q = w.query(0, "cpu").numpy()[:S]
         t0 = time.perf_counter()
-        oracle.kv_quant_append(k_new, v_new, np.arange(S, dtype=np.int32), w.append_pos[:S].copy(), pt, kp, vp,
-                               w.had_block, w.page_size)
-        oracle.paged_decode_attn_int4(q, kp, vp, pt, w.context_lens[:S].copy(), w.num_kv_heads, w.page_size,
-                                      w.had_block, w.softmax_scale)
+        for _ in range(reps):   # (the append rewrites the same slots with the same bytes)
+            oracle.kv_quant_append(k_new, v_new, np.arange(S, dtype=np.int32), w.append_pos[:S].copy(), pt, kp,
+                                   vp, w.had_block, w.page_size)
+            oracle.paged_decode_attn_int4(q, kp, vp, pt, w.context_lens[:S].copy(), w.num_kv_heads, w.page_size,
+                                          w.had_block, w.softmax_scale)
         dt = time.perf_counter() - t0
         sub = wl.Workload(**{**w.__dict__, "batch": S, "context_lens": w.context_lens[:S],
                               "per_layer_page_tables": None})
-        nbytes = decode_bytes(sub) + append_bytes(S, w.num_kv_heads)
+        nbytes = reps * (decode_bytes(sub) + append_bytes(S, w.num_kv_heads))
         return dt, nbytes
 
-    S = 2
+    S, reps = 2, 1
     dt, nbytes = run(S)
     if dt < budget_s / 4:
         S = int(min(w.batch, max(S + 1, math.floor(S * budget_s / max(dt, 1e-3) * 0.8))))
         dt, nbytes = run(S)
+    if S == w.batch and dt < budget_s / 2:   # the whole batch is quick: repeat it
+        reps = max(2, int(budget_s * 0.8 / max(dt, 1e-3)))
+        dt, nbytes = run(S, reps)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"first {S} of {w.batch} sequences: append of their new tokens + fp64 decode "
-                      f"over their contexts (sum {int(w.context_lens[:S].sum())} tokens), "
+            "sample": f"first {S} of {w.batch} sequences, {reps} time(s): append of their new tokens + fp64 "
+                      f"decode over their contexts (sum {int(w.context_lens[:S].sum())} tokens), "
                       "same shapes, CPU-generated values"}
 
 
