@@ -205,6 +205,12 @@ def cpu_baseline(w, budget_s=12.0):
         nbytes = reps * (decode_bytes(sub) + append_bytes(S, w.num_kv_heads))
         return dt, nbytes
 
+    # one thread on a small sample first (the oracle's per-unit work is
+    # sequential either way), then every host thread
+    nthreads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    dt1, nbytes1 = run(4)
+    oracle.set_num_threads(nthreads)
     S, reps = 2, 1
     dt, nbytes = run(S)
     if dt < budget_s / 4:
@@ -213,8 +219,16 @@ def cpu_baseline(w, budget_s=12.0):
     if S == w.batch and dt < budget_s / 2:   # the whole batch is quick: repeat it
         reps = max(2, int(budget_s * 0.8 / max(dt, 1e-3)))
         dt, nbytes = run(S, reps)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": model, "host_cpus": os.cpu_count(),
+            "single_thread_value": round(nbytes1 / dt1 / 1e9, 4),
+            "single_thread_sample": "first 4 sequences, one thread",
             "sample": f"first {S} of {w.batch} sequences, {reps} time(s): append of their new tokens + fp64 "
                       f"decode over their contexts (sum {int(w.context_lens[:S].sum())} tokens), "
                       "same shapes, CPU-generated values"}
@@ -488,6 +502,36 @@ def extra_measurements(dev, args):
     ex["decode_b1_32k_36layers"] = {"ms_per_step": round(ms, 5), "us_per_layer": round(1000 * ms / w3.layers, 3),
                                     "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
                                     "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    # The same 36-layer step captured once in a HIP graph and replayed; every
+    # checked replay must give the eager step's output, with eager work and
+    # synchronisations in between.
+    torch.cuda.synchronize()
+    all_layers()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        all_layers()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        all_layers()
+    for _ in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager):
+            raise RuntimeError("graph replay of the batch-1 decode step differs from the eager step")
+        all_layers()
+        torch.cuda.synchronize()
+    ms_g, _ = time_calls(graph.replay, 10, 2)
+    ex["decode_b1_32k_36layers"].update({"graph_ms_per_step": round(ms_g, 5),
+                                         "graph_us_per_layer": round(1000 * ms_g / w3.layers, 3),
+                                         "graph_pct_of_hbm_peak":
+                                             round(100 * nb / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
+    del graph
     del caches
     torch.cuda.empty_cache()
 

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_oracle_dense_decode_f64.restype = ctypes.c_int
         L.kvq_oracle_num_threads.argtypes = []
         L.kvq_oracle_num_threads.restype = ctypes.c_int
+        L.kvq_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.kvq_oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -89,6 +91,12 @@ def _as(a, dtype) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().kvq_oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not
+    depend on it)."""
+    lib().kvq_oracle_set_num_threads(int(n))
 
 
 def f16_bits_to_f32(h: int) -> float:

@@ -508,3 +508,14 @@ int kvq_oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the next parallel regions (timing only: every unit is computed
+ * sequentially, so results do not depend on it). */
+void kvq_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
