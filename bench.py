@@ -237,7 +237,7 @@ def cpu_baseline(w, budget_s=12.0):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="main workload only (no extra measurements)")
     ap.add_argument("--append-only", action="store_true",
@@ -404,6 +404,7 @@ def main(argv=None):
             "traffic": traffic,
             "alg_bytes_per_launch": partial_alg,
             "avg_launch_ms": round(mean(t_partial), 5),
+            "launch_ms_p10_p50_p90": [round(float(np.percentile(t_partial, q)), 5) for q in (10, 50, 90)],
             "kernel_source_sha256_16": khash,
         },
     }
@@ -445,6 +446,24 @@ def append_measurements(dev, iters=20, warmup=3, with_decode_time=True):
         del kp, vp, k, v
         torch.cuda.empty_cache()
         return ex
+    # prompt append: 32,768 consecutive tokens of one sequence in one call
+    # (the prefill side of the same kernel), into a batch-1 32K-context cache
+    w3 = wl.c3(layers=1)
+    kp3 = torch.zeros((w3.num_pages, w3.num_kv_heads, kvq.page_tile_bytes(w3.head_dim, w3.page_size)),
+                      dtype=torch.uint8, device=dev)
+    vp3 = torch.zeros_like(kp3)
+    L3 = int(w3.prefill_lens[0])
+    k3, v3 = w3.rows(0, 0, 0, L3, dev)
+    s3 = torch.zeros(L3, dtype=torch.int32, device=dev)
+    p3 = torch.arange(L3, dtype=torch.int32, device=dev)
+    pt3 = torch.as_tensor(w3.table(0), device=dev)
+    ms, med = time_calls(lambda: kvq.kv_quant_append(k3, v3, s3, p3, pt3, kp3, vp3, w3.page_size, w3.had_block),
+                         iters, warmup)
+    nb3 = append_bytes(L3, w3.num_kv_heads)
+    ex["append_prompt_32768tok_bh128"] = {"ms": round(ms, 5), "tokens_per_s": round(L3 / (ms * 1e-3), 1),
+                                          "GBps": round(nb3 / (ms * 1e-3) / 1e9, 2),
+                                          "pct_of_hbm_peak": round(100 * nb3 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    del kp3, vp3, k3, v3
     # decode-time append (1 token per sequence)
     w2 = wl.c2()
     k2, v2 = w2.append_rows(0, dev)
