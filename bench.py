@@ -244,6 +244,8 @@ def main(argv=None):
                     help="only the append bandwidth measurement (65,536 tokens in one call), one JSON line")
     ap.add_argument("--fp16-only", action="store_true",
                     help="only the fp16 baseline decode on the main workload, one JSON line")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the causal prefill attention over a 32,768-token prompt, one JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB streaming kernel (counter calibration under rocprofv3 --pmc)")
@@ -268,6 +270,11 @@ def main(argv=None):
         return 0
     if args.fp16_only:
         print(json.dumps({"decode_fp16_c4": fp16_measurement(dev, iters=args.steps, warmup=args.warmup)}),
+              flush=True)
+        return 0
+
+    if args.prefill_only:
+        print(json.dumps({"prefill_b1_32k": prefill_measurement(dev, iters=args.steps, warmup=args.warmup)}),
               flush=True)
         return 0
 
@@ -555,7 +562,52 @@ def extra_measurements(dev, args):
     torch.cuda.empty_cache()
 
     ex["decode_fp16_c4"] = fp16_measurement(dev, iters=10, warmup=2)
+    ex["prefill_b1_32k"] = prefill_measurement(dev, iters=5, warmup=1)
     return ex
+
+
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 matrix rate, published
+PEAK_I8_TOPS = 5000.0         # MI355X dense int8 matrix rate, published
+
+
+def prefill_measurement(dev, iters, warmup):
+    """Causal prefill attention of a whole 32,768-token prompt (batch 1,
+    Hq 32, Hkv 8, D 128, Hadamard block 128, page size 16, shuffled pages)
+    over its INT4 cache.  Useful flops: 4 D Hq per (query, visible key) pair
+    (q.k and p.v, 2 each), L (L + 1) / 2 pairs.  The kernel issues more
+    matrix work than that: q.k as three int8 limb products per nibble half
+    (6 v_mfma_i32_16x16x64_i8 per 16 x 16 x 128 score tile) and p.v with the
+    weights split into fp16 hi + lo (2 fp16 products per useful one);
+    mfma_time_frac is the time those issued instructions take at the
+    published dense peaks over the measured time."""
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
+    w = wl.c3(layers=1)
+    kp, vp, pt = build_int4_cache(w, dev, layer=0)
+    L = int(w.context_lens[0])
+    g = torch.Generator(device=dev)
+    g.manual_seed(3030)
+    q = torch.randn((L, w.num_q_heads, w.head_dim), generator=g, device=dev).to(torch.float16)
+    qs = torch.tensor([0, L], dtype=torch.int32, device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    out = torch.empty((L, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    call = lambda: kvq.paged_prefill_attn_int4(q, qs, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.had_block,
+                                               w.softmax_scale, out=out)
+    ms, med = time_calls(call, iters, warmup)
+    pairs = L * (L + 1) // 2
+    useful = 4.0 * w.head_dim * w.num_q_heads * pairs
+    # issued work per 16 x 16 x 128 tile: q.k 6 int8 MFMAs of 16x16x64, p.v 8 fp16 MFMAs of 16x16x32
+    tiles = useful / (4.0 * 16 * 16 * 128)
+    t_issue = tiles * (6 * 2 * 16 * 16 * 64 / (PEAK_I8_TOPS * 1e12) + 8 * 2 * 16 * 16 * 32 / (PEAK_F16_TFLOPS * 1e12))
+    res = {"ms": round(ms, 4), "median_ms": round(med, 4), "prompt_tokens": L,
+           "useful_TFLOPs": round(useful / (ms * 1e-3) / 1e12, 1),
+           "useful_frac_of_f16_peak": round(useful / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+           "mfma_time_frac": round(t_issue / (ms * 1e-3), 4),
+           "prompt_tokens_per_s": round(L / (ms * 1e-3), 1)}
+    del kp, vp, q, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def fp16_measurement(dev, iters, warmup):

@@ -33,6 +33,8 @@ SIGNATURES = {
     "paged_decode_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attn_int4": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _F32, _P, _P, _SZ, _I32, _P]),
+    "paged_prefill_attn_int4": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
+                                               _I32, _I32, _F32, _P, _P]),
     "kv_append_fp16": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "paged_decode_attn_fp16": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _F32, _P, _P, _SZ, _I32, _P]),
@@ -195,6 +197,33 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
              int(pages_per_split), _stream(q)]
     fn = lib().paged_decode_attn_int4 if int4 else lib().paged_decode_attn_fp16
     _check(fn(*args), "paged_decode_attn_int4" if int4 else "paged_decode_attn_fp16")
+    return out
+
+
+def paged_prefill_attn_int4(q, q_start, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
+                            page_size: int, had_block: int, softmax_scale: float, out=None):
+    """Causal prefill attention over the INT4 cache: rows q_start[b] ..
+    q_start[b+1]-1 of q (fp16 [num_q][Hq][D]) are the last positions of
+    sequence b; returns fp32 [num_q][Hq][D]."""
+    import torch
+    nq, hq, d = q.shape
+    B = context_lens.numel()
+    want = (int(num_kv_heads), page_tile_bytes(d, int(page_size)))
+    if tuple(k_pool.shape[1:]) != want or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError(f"pools must both be [num_pages]{list(want)}")
+    if q_start.numel() != B + 1 or page_table.dim() != 2 or page_table.shape[0] < B:
+        raise ValueError("q_start must have batch + 1 entries and page_table one row per sequence")
+    if out is None:
+        out = torch.empty((nq, hq, d), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (nq, hq, d):
+        raise ValueError(f"out must be [{nq}][{hq}][{d}]")
+    _check(lib().paged_prefill_attn_int4(
+        _dev(q, torch.float16, "q", 3), _dev(q_start, torch.int32, "q_start", 1), nq,
+        _dev(k_pool, torch.uint8, "k_pool"), _dev(v_pool, torch.uint8, "v_pool"), k_pool.shape[0],
+        _dev(page_table, torch.int32, "page_table", 2), page_table.shape[1],
+        _dev(context_lens, torch.int32, "context_lens", 1), B, hq, int(num_kv_heads), d, int(page_size),
+        int(had_block), float(softmax_scale), _dev(out, torch.float32, "out", 3), _stream(q)),
+        "paged_prefill_attn_int4")
     return out
 
 

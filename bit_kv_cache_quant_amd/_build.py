@@ -23,6 +23,7 @@ SOURCES = {
     # MFMA results straight into VGPRs (no accumulator-register copies)
     "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "decode_f16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "combine.hip": [],
 }
 

@@ -374,6 +374,44 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int
     return need;
 }
 
+int paged_prefill_attn_int4(const uint16_t *q, const int32_t *q_start, int32_t num_q, const uint8_t *k_pool,
+                            const uint8_t *v_pool, int64_t num_pages, const int32_t *page_table,
+                            int32_t max_pages_per_seq, const int32_t *context_lens, int32_t batch,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t had_block, float softmax_scale, float *out, void *stream) {
+    if (num_q < 0 || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
+        num_pages <= 0 || num_q_heads % num_kv_heads)
+        return KVQ_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim || !valid_page_size(page_size) || !valid_had_block(had_block))
+        return KVQ_ERR_UNSUPPORTED;
+    if (num_q == 0 || batch == 0) return KVQ_OK;
+    if (!q || !q_start || !k_pool || !v_pool || !page_table || !context_lens || !out) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
+    if ((int64_t)num_q / 16 + batch > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+    const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
+    if ((int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
+    kvq::PrefillArgs a{};
+    a.q = q;
+    a.q_start = q_start;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.page_table = page_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.tile_bytes = (int64_t)kvq_page_tile_bytes(head_dim, page_size);
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.batch = batch;
+    a.num_q = num_q;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.head_chunks = chunks;
+    a.page_size = page_size;
+    a.had_block = had_block;
+    a.score_scale = softmax_scale * 1.4426950408889634f;
+    return kvq::launch_prefill_int4(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
 int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,
                            const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
                            int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,

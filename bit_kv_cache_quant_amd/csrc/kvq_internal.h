@@ -79,7 +79,32 @@ __host__ __device__ inline int32_t balanced_groups(int32_t gmin, int32_t gmax, i
     return g < 1 ? 1 : g;
 }
 
+// Causal prefill attention over the INT4 cache: query row i of sequence b
+// (rows q_start[b] .. q_start[b + 1] - 1, the last q_len_b positions of its
+// context) attends to the cached tokens 0 .. context_lens[b] - q_len_b + i.
+struct PrefillArgs {
+    const uint16_t *q;         // fp16 [num_q][num_q_heads][kHeadDim]
+    const int32_t *q_start;    // [batch + 1]
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    float *out;                // fp32 [num_q][num_q_heads][kHeadDim]
+    int64_t tile_bytes;
+    int32_t max_pages_per_seq;
+    int32_t batch;
+    int32_t num_q;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;
+    int32_t head_chunks;
+    int32_t page_size;
+    int32_t had_block;
+    float score_scale;         // softmax_scale * log2(e)
+};
+
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_prefill_int4(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_append_fp16(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fp16(const DecodeArgs &a, hipStream_t stream);

@@ -187,6 +187,34 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
                            int32_t pages_per_split, void *stream);
 
 /*
+ * paged_prefill_attn_int4 — causal attention of a prompt's queries over the
+ * INT4 paged cache, after the prompt's tokens have been appended
+ * (kv_quant_append); [EXPL] "KVキャッシュこそが..." (attention over the paged
+ * INT4 blocks, in the prefill and decode regimes) and "回転のトリック" (rotate
+ * the queries, rotate the outputs back).
+ *
+ * Query rows q_start[b] .. q_start[b + 1] - 1 belong to sequence b and are its
+ * last q_len_b = q_start[b + 1] - q_start[b] positions: row q_start[b] + i is
+ * position p = context_lens[b] - q_len_b + i and, for each query head, gets
+ *   softmax over k <= p of softmax_scale * (R q).(R k_k), then R (sum w_k R v_k)
+ * (the decode's computation at context length p + 1).
+ *
+ *   q            fp16 [num_q][num_q_heads][head_dim]
+ *   q_start      int32 [batch + 1], device: q_start[0] = 0, nondecreasing,
+ *                q_start[batch] = num_q, q_len_b <= context_lens[b]
+ *                (not checked on the device)
+ *   out          fp32 [num_q][num_q_heads][head_dim]
+ *   other arguments as for paged_decode_attn_int4.
+ * No workspace.  num_q == 0 or batch == 0 is a no-op returning KVQ_OK.
+ */
+int paged_prefill_attn_int4(const uint16_t *q, const int32_t *q_start, int32_t num_q,
+                            const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,
+                            const int32_t *page_table, int32_t max_pages_per_seq,
+                            const int32_t *context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t had_block, float softmax_scale, float *out, void *stream);
+
+/*
  * kv_append_fp16 — baseline append: copy each new token's fp16 K/V rows into
  * fp16 pools [num_pages][num_kv_heads][page_size][head_dim] through the page
  * table.  Same arguments and contract as kv_quant_append without had_block.

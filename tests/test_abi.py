@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
-    for must in ("kv_quant_append", "paged_decode_attn_int4", "kv_append_fp16",
+    for must in ("kv_quant_append", "paged_decode_attn_int4", "paged_prefill_attn_int4", "kv_append_fp16",
                  "paged_decode_attn_fp16", "paged_decode_attn_workspace_bytes",
                  "kvq_page_tile_bytes", "kvq_status_string"):
         assert must in names
@@ -170,3 +170,26 @@ def test_binding_rejects_mis_shaped_pools_before_launch():
     with pytest.raises(ValueError, match="pools must"):
         kvq.paged_decode_attn_int4(q, short_tile, short_tile, pt, torch.zeros(1, dtype=torch.int32), 8, 16, 64,
                                    0.088, 64)
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, qs=FAKE, nq=32, kp=FAKE, vp=FAKE, npages=8, pt=FAKE, maxp=4, cl=FAKE, B=1, hq=32, hkv=8,
+             d=128, P=16, bh=64, scale=0.088, out=FAKE, stream=None)
+    a.update(kw)
+    return kvq.lib().paged_prefill_attn_int4(a["q"], a["qs"], a["nq"], a["kp"], a["vp"], a["npages"], a["pt"],
+                                             a["maxp"], a["cl"], a["B"], a["hq"], a["hkv"], a["d"], a["P"],
+                                             a["bh"], a["scale"], a["out"], a["stream"])
+
+
+def test_prefill_host_validation():
+    """Rejected on the host before any launch (no pointer is dereferenced)."""
+    assert _prefill(d=64) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _prefill(P=8) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _prefill(bh=16) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _prefill(hq=30) == kvq.KVQ_ERR_INVALID_ARG
+    assert _prefill(nq=-1) == kvq.KVQ_ERR_INVALID_ARG
+    assert _prefill(q=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _prefill(qs=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _prefill(out=FAKE + 4) == kvq.KVQ_ERR_INVALID_ARG     # misaligned
+    assert _prefill(nq=0) == kvq.KVQ_OK                           # no-op
+    assert _prefill(B=0) == kvq.KVQ_OK
