@@ -1,6 +1,7 @@
 // C ABI of the INT4 KV-cache library: argument validation, split choice and
 // kernel launches.  The contract of every entry point is documented in
 // include/kvq.h.
+#include <cmath>
 #include <stdlib.h>
 #include <string.h>
 
@@ -380,7 +381,7 @@ int paged_prefill_attn_int4(const uint16_t *q, const int32_t *q_start, int32_t n
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                             int32_t had_block, float softmax_scale, float *out, void *stream) {
     if (num_q < 0 || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
-        num_pages <= 0 || num_q_heads % num_kv_heads)
+        num_pages <= 0 || num_q_heads % num_kv_heads || !(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
         return KVQ_ERR_INVALID_ARG;
     if (head_dim != kHeadDim || !valid_page_size(page_size) || !valid_had_block(had_block))
         return KVQ_ERR_UNSUPPORTED;

@@ -12,37 +12,45 @@
 // context) attends to the cached tokens 0 .. position(i): the same
 // computation as one decode step per query position, with the keys and
 // values reused across 16 query positions and the 4 query heads of a GQA
-// group, so the work is bound by the matrix cores rather than by HBM.
+// group, so the work is bound by the chip's arithmetic rather than by HBM.
 //
 // Block = 4 waves = the 4 query heads of one head slot (KV head, chunk of 4
 // of its query heads) x 16 consecutive query positions of one sequence; it
-// walks the keys in chunks of 64 staged once in LDS for the 4 waves.
-//   q.k  exact integer products on v_mfma_i32_16x16x64_i8, as in the
-//        decode: the rotated query of each row is a 21-bit fixed-point
-//        integer X = round(q' 2^(20-E)) (E the exponent of the row's max
-//        |q'|) split into limbs X = L0 2^14 + L1 2^7 + L2, one MFMA per limb
-//        and nibble half.  A (limb): row j = query position j; the lanes of
-//        k-group g hold dims 32g + 2e (even half) or 32g + 2e + 1 (odd half).
-//        B (keys): column j = key 16t + j, its 16 code bytes (dims 32g ..
-//        32g + 31) with the even dims' nibbles moved to the top of each byte
-//        and the odd dims' kept there: signed bytes 16 c, no offset term.
-//        The three limb results are exact in int32 and are recombined in
-//        fp32; the row's scale, 1/16 and the key's scale follow.  D: lane
-//        (g, j) holds rows 4g..4g+3 (query positions) for key j: scores,
-//        masked causally.  (fp16 products summed in fp32 were measurably less
+// walks the keys in chunks of 64, staged once in LDS for the 4 waves: key
+// codes pre-split into the two signed-byte operands below, values converted
+// once to fp16.  Everything is computed transposed (keys or dims as rows,
+// query positions as columns), so that the weights leave the score MFMA in
+// exactly the lanes and registers the p.v MFMA takes them from.
+//   q.k  S^T = K Q^T, exact integer products on v_mfma_i32_16x16x64_i8, as in
+//        the decode: the rotated query of each position is a 21-bit
+//        fixed-point integer X = round(q' 2^(20-E)) (E the exponent of its
+//        max |q'|) split into limbs X = L0 2^14 + L1 2^7 + L2, one MFMA per
+//        limb and nibble half.  A (keys): row j = key 16t + j, its 16 code
+//        bytes (dims 32g .. 32g + 31) with the even dims' nibbles moved to the
+//        top of each byte, or the odd dims' kept there: signed bytes 16 c.
+//        B (limb): column j = query position j, the dims 32g + 2e (even half)
+//        or 32g + 2e + 1 (odd half).  The limb results are exact in int32;
+//        L0 and L1 are combined in int32, the rest in fp32, then the key's
+//        scale.  D: lane (g, j) holds keys 16t + 4g + i (i = 0..3) of query
+//        position j.  (fp16 products summed in fp32 were measurably less
 //        accurate here: with the rotation every code is nonzero and the
 //        softmax of large scores amplifies their rounding.)
-//   softmax: online per query row; a row's 16 keys of a group are the 16
-//        lanes of one lane row (DPP reductions), its 4 rows per lane are
-//        rescaled lane-locally.
-//   p.v  A (weights): row j = query position j, k = keys 16g + 8h .. 16g + 8h +
-//        7 (MFMA half h), P = p * (value scale) split into fp16 hi + lo and
-//        passed through LDS.  B (values): the value codes of dim 16m + j of
-//        the same keys, read with the transposed 4-bit LDS read
-//        (ds_read_b64_tr_b4) from the decode's swizzled layout and converted
-//        to fp16.  D: lane (g, j) holds rows 4g..4g+3 of output dim 16m + j.
-//   Output: divided by the row sums, rotated back (spans below 16 between
-//   the lanes of a row, 16..64 between a lane's registers), stored in fp32.
+//   softmax: online per query position; a position's 64 scores of a chunk
+//        are 16 registers in each of the 4 lanes j, j + 16, j + 32, j + 48
+//        (two lane-swap steps reduce across them); the position's factor
+//        2^(E-20) / 16 times the softmax scale goes into the exponent's fma.
+//   p.v  O^T = V^T P^T.  B (weights): column j = query position j, k = 8g + e
+//        is key 32h + 4g + e (e < 4) or 32h + 16 + 4g + e - 4: exactly the
+//        scores lane (g, j) holds for key groups t = 2h and 2h + 1, so
+//        P = p * (value scale), split into fp16 hi + lo (two MFMAs, ~22
+//        bits), needs no data movement.  A (values): row j = dim 16m + j, the
+//        same 8 keys, read from the fp16 value rows with the transposed
+//        16-bit LDS read (ds_read_b64_tr_b16: in each group of 16 lanes,
+//        lane i's element e is element i & 3 of the word lane 4e + i/4
+//        points at).  D: lane (g, j) holds dims 16m + 4g + i of position j.
+//   Output: divided by the sums, rotated back (spans 1, 2 between a lane's
+//   registers i, 4, 8 between lane groups, 16..64 between registers m),
+//   stored as 16-byte rows of 4 dims.
 #include <type_traits>
 
 #include "decode_common.h"
@@ -55,22 +63,21 @@ using namespace dec;
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kQRows = 16;        // query positions per block
 constexpr int kKeys = kChunkTokens;   // keys per step
 constexpr int kKPitch = 80;       // LDS bytes per key row of codes (64 + 16: conflict-free 16-byte reads)
-constexpr int kVGroup = 1024;     // value codes of 16 keys, swizzled slots
-__host__ __device__ constexpr int vgroup(int t) { return t * kVGroup + 128 * ((t + 1) >> 1); }
-constexpr int kVBytes = vgroup(3) + kVGroup;
-constexpr int kPPitch = kKeys + 8;    // halves per weight row (16-byte aligned rows, spread banks)
+constexpr int kVRow = 2 * kHeadDim;   // bytes per fp16 value row
 
 struct alignas(16) PrefillShared {
-    uint8_t k[kKeys * kKPitch];            // key codes, row n at n * kKPitch
-    uint8_t v[kVBytes];                    // value codes, 4 swizzled groups
-    float ks[kKeys], vs[kKeys];            // scales
-    _Float16 p[kWaves][2][kQRows][kPPitch];   // per wave: weights hi / lo [query row][key]
+    uint8_t kev[kKeys * kKPitch];        // key codes, even dims' nibbles at the top of each byte
+    uint8_t kod[kKeys * kKPitch];        // key codes, odd dims' nibbles at the top (low nibble 0)
+    // values as fp16; row T's 16-byte piece p at piece slot p ^ 2 (T & 7), so
+    // that the 8 rows one half-wave reads transposed cover all 64 banks once
+    uint8_t v[kKeys * kVRow];
+    float ks[kKeys], vs[kKeys];          // scales
 };
 
 __device__ __forceinline__ v4f mfma(v8h a, v8h b, v4f c) {
@@ -96,6 +103,43 @@ __device__ __forceinline__ v8h nibbles_to_half(uint32_t w) {
     const v8h biased = __builtin_bit_cast(v8h, make_uint4(d[0], d[1], d[2], d[3]));
     const _Float16 off = static_cast<_Float16>(1032.0f);
     return biased - v8h{off, off, off, off, off, off, off, off};
+}
+
+// Lane-row exchanges over the 4 lanes j, j + 16, j + 32, j + 48 (the rows
+// of 16 lanes).  swap_rows<1> is v_permlane16_swap of x with itself: lo = the
+// value of the even row of the lane's row pair (0, 1) or (2, 3), hi = the odd
+// row's; swap_rows<2> is v_permlane32_swap: lo = the lower half's value
+// (rows 0, 1), hi = the upper half's.  (The results are copied to scalars
+// before the bit cast: a bit cast applied directly to an element of the
+// builtin's two-element vector read element 0 for both.)
+template <int SPAN>
+__device__ __forceinline__ void swap_rows(float x, float &lo, float &hi) {
+    const uint32_t a = __builtin_bit_cast(uint32_t, x);
+    const auto r = SPAN == 1 ? __builtin_amdgcn_permlane16_swap(a, a, false, false)
+                             : __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    lo = __builtin_bit_cast(float, r0);
+    hi = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float rows_max4(float x) {
+    float lo, hi;
+    swap_rows<1>(x, lo, hi);
+    swap_rows<2>(fmaxf(lo, hi), lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float rows_sum4(float x) {
+    float lo, hi;
+    swap_rows<1>(x, lo, hi);
+    swap_rows<2>(lo + hi, lo, hi);
+    return lo + hi;
+}
+// Butterfly between lane rows r and r ^ SPAN (SPAN 1 or 2): the lower row
+// gets a + b, the upper a - b (a the lower row's value).
+template <int SPAN>
+__device__ __forceinline__ float rows_butterfly(float x, const int g) {
+    float lo, hi;
+    swap_rows<SPAN>(x, lo, hi);
+    return (g & SPAN) ? lo - hi : lo + hi;
 }
 
 // Which sequence b and which of its 16-row query tiles global tile t is
@@ -156,10 +200,11 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const int pos0 = L - qlen + kQRows * tile;   // position of row 0
     const int last_pos = pos0 + rows - 1;
     const int nchunks = last_pos / kKeys + 1;
+    const int my_pos = pos0 + j;                 // this lane's query position
 
     __shared__ PrefillShared sh;
 
-    // ---- the rotated, scaled query of head qh: lane (row j, group g), dims 32g .. 32g + 31 ----
+    // ---- the rotated query of head qh: lane (g, j) holds position j, dims 32g .. 32g + 31 ----
     float x[32];
     {
         uint4 raw[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
@@ -200,24 +245,21 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
                     x[r] = upper ? (p - x[r]) : (x[r] + p);
                 }
             }
-        }
-        if constexpr (BH > 0) {
             const float c = rsqrtf(static_cast<float>(BH));
 #pragma unroll
             for (int r = 0; r < 32; ++r) x[r] *= c;
         }
     }
-    // 21-bit fixed point per (row, head): the row's 128 dims are in lanes
-    // j, j + 16, j + 32, j + 48
+    // 21-bit fixed point per (position, head): the position's 128 dims are in
+    // lanes j, j + 16, j + 32, j + 48
     float amax = 0.0f;
 #pragma unroll
     for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(x[r]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = rows_max4(amax);
     int qexp = 0;
     if (amax > 0.0f) (void)frexpf(amax, &qexp);     // amax < 2^qexp
     const float qmul = ldexpf(1.0f, 20 - qexp);
-    v4i qa[3][2];   // [limb][even / odd dims]: byte e of dword w = dim 32g + 2 (4w + e) + half
+    v4i qb[3][2];   // [limb][even / odd dims]: byte e of dword w = dim 32g + 2 (4w + e) + half
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         uint32_t wd[3][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -229,18 +271,13 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
             for (int l = 0; l < 3; ++l) wd[l][e >> 2] |= (static_cast<uint32_t>(limb[l]) & 0xFFu) << (8 * (e & 3));
         }
 #pragma unroll
-        for (int l = 0; l < 3; ++l) qa[l][h] = v4i{(int)wd[l][0], (int)wd[l][1], (int)wd[l][2], (int)wd[l][3]};
+        for (int l = 0; l < 3; ++l) qb[l][h] = v4i{(int)wd[l][0], (int)wd[l][1], (int)wd[l][2], (int)wd[l][3]};
     }
-    // the score factor of rows 4g + i (this lane's result rows): 2^(E-20) of
-    // that row, 1/16 for the nibble position, the softmax scale (log2 units)
-    float row_mul[4];
-    {
-        const float mine = ldexpf(a.score_scale * 0.0625f, qexp - 20);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) row_mul[i] = __shfl(mine, 4 * g + i);
-    }
+    // score factor of this position (log2 units): 2^(E-20), 1/16 for the
+    // nibble position, the softmax scale (positive)
+    const float rm = ldexpf(a.score_scale * 0.0625f, qexp - 20);
 
-    // ---- loads of one chunk: wave w takes key group w (16 keys) ----
+    // ---- loads of one chunk: wave w takes keys 16w .. 16w + 15 ----
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
     const int64_t page_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
@@ -251,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const int ln = lane >> 2, lp = lane & 3;   // key row, 16-byte piece of this lane's loads
     struct Raw { uint4 k, v; uint32_t s; };
     auto load = [&](int c, Raw &r) {
-        const int key0 = kKeys * c + 16 * wave;                      // first key of group `wave`
+        const int key0 = kKeys * c + 16 * wave;
         const int64_t page = pt[min(key0 / P, last_page)];
         const int slot0 = key0 % P;
         const uint8_t *kt = kpool + page * page_stride + code_off + (int64_t)(slot0 + ln) * kCodeBytesPerRow + 16 * lp;
@@ -262,96 +299,110 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
         r.s = lane < 32 ? *reinterpret_cast<const uint16_t *>(sp) : 0u;
     };
     auto stage = [&](const Raw &r) {
-        *reinterpret_cast<uint4 *>(&sh.k[(16 * wave + ln) * kKPitch + 16 * lp]) = r.k;
-        *reinterpret_cast<uint4 *>(&sh.v[vgroup(wave) + 16 * (4 * ln + (lp ^ ((ln >> 2) & 3)))]) = r.v;
+        const int T = 16 * wave + ln;
+        const uint32_t kw[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            ev[s] = (kw[s] << 4) & 0xF0F0F0F0u;
+            od[s] = kw[s] & 0xF0F0F0F0u;
+        }
+        *reinterpret_cast<uint4 *>(&sh.kev[T * kKPitch + 16 * lp]) = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+        *reinterpret_cast<uint4 *>(&sh.kod[T * kKPitch + 16 * lp]) = make_uint4(od[0], od[1], od[2], od[3]);
+        // value codes of dims 32 lp + 8 s .. + 7 -> fp16 piece 4 lp + s of row T
+        const uint32_t vw[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * lp + s) ^ (2 * (T & 7)))]) = nibbles_to_half(vw[s]);
         if (lane < 16) sh.ks[16 * wave + lane] = half_to_float(r.s);
         else if (lane < 32) sh.vs[16 * wave + lane - 16] = half_to_float(r.s);
     };
 
-    float m_run[4], l_lane[4];      // query rows 4g + i
-    v4f o[8];                       // output dims 16m + j, rows 4g + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m_run[i] = -INFINITY;
-        l_lane[i] = 0.0f;
-    }
+    float m_run = -INFINITY, l_lane = 0.0f;   // this lane's position
+    v4f o[8];                                   // dims 16m + 4g + i of position j
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // transposed-read address of dims 16m + 4 (j & 3) of key row 4g + j / 4
+    // (+ 32 h for half h, + 16 for its second read): piece 2m + (j & 3) / 2
+    const int tr_key = 4 * g + (j >> 2);
+    const uint32_t tr_base = tr_key * kVRow + 8 * (j & 1);
+    const int tr_piece = (j & 3) >> 1;
+    const int tr_x = 2 * (tr_key & 7);     // the row's piece swizzle (rows + 16, + 32 share it)
 
     auto compute = [&](int c, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
-        // q.k and the causal mask
-        float z[4][4];   // [key group t][row i]
+        // q.k: z[t][i] = score of key 16t + 4g + i before the position's factor
+        float z[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint4 kr = *reinterpret_cast<const uint4 *>(&sh.k[(16 * t + j) * kKPitch + 16 * g]);
-            // signed bytes 16 c: even dims (low nibbles) shifted up, odd dims in place
-            const v4i kev = {(int)((kr.x << 4) & 0xF0F0F0F0u), (int)((kr.y << 4) & 0xF0F0F0F0u),
-                             (int)((kr.z << 4) & 0xF0F0F0F0u), (int)((kr.w << 4) & 0xF0F0F0F0u)};
-            const v4i kod = {(int)(kr.x & 0xF0F0F0F0u), (int)(kr.y & 0xF0F0F0F0u), (int)(kr.z & 0xF0F0F0F0u),
-                             (int)(kr.w & 0xF0F0F0F0u)};
+            const v4i ke = *reinterpret_cast<const v4i *>(&sh.kev[(16 * t + j) * kKPitch + 16 * g]);
+            const v4i ko = *reinterpret_cast<const v4i *>(&sh.kod[(16 * t + j) * kKPitch + 16 * g]);
             const v4i zero = {0, 0, 0, 0};
             v4i dl[3];
 #pragma unroll
-            for (int l = 0; l < 3; ++l) dl[l] = mfma_i8(qa[l][1], kod, mfma_i8(qa[l][0], kev, zero));
-            const float sk = sh.ks[16 * t + j];
-            const int kp = kKeys * c + 16 * t + j;
+            for (int l = 0; l < 3; ++l) dl[l] = mfma_i8(ko, qb[l][1], mfma_i8(ke, qb[l][0], zero));
+            const float4 sk = *reinterpret_cast<const float4 *>(&sh.ks[16 * t + 4 * g]);
+            const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float dot = fmaf(static_cast<float>(dl[0][i]), 16384.0f,
-                                       fmaf(static_cast<float>(dl[1][i]), 128.0f, static_cast<float>(dl[2][i])));
-                const float sc = dot * row_mul[i] * sk;
-                z[t][i] = (!MASK || kp <= pos0 + 4 * g + i) ? sc : -INFINITY;
+                // |L0 . k| < 2^20, so L0 . k 2^7 + L1 . k is exact in int32
+                const float dot = fmaf(static_cast<float>((dl[0][i] << 7) + dl[1][i]), 128.0f,
+                                       static_cast<float>(dl[2][i]));
+                const float sc = dot * skv[i];
+                z[t][i] = (!MASK || kKeys * c + 16 * t + 4 * g + i <= my_pos) ? sc : -INFINITY;
             }
         }
-        // online softmax per row
+        // online softmax of this position (its 64 scores: 16 here, 48 in lanes j + 16 k)
+        float zm = z[0][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float zm = fmaxf(fmaxf(z[0][i], z[1][i]), fmaxf(z[2][i], z[3][i]));
-            zm = row_max16_fast(zm);
-            if (zm > m_run[i]) {
-                const float alpha = fast_exp2(m_run[i] - zm);
-                l_lane[i] *= alpha;
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int m = 0; m < 8; ++m) o[m][i] *= alpha;
-                m_run[i] = zm;
-            }
-        }
-        // weights times the value scale, hi / lo, into LDS [row][key]
-        _Float16(*pw)[kQRows][kPPitch] = sh.p[wave];
+            for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[t][i]);
+        zm = rows_max4(zm);
+        const float m_new = fmaxf(m_run, zm * rm);   // finite from the first chunk on (key 0 is visible)
+        const float alpha = fast_exp2(m_run - m_new);
+        l_lane *= alpha;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] *= alpha;
+        m_run = m_new;
+        // weights times the value scale, split hi / lo: the p.v B operands
+        v8h pb_hi[2], pb_lo[2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float sv = sh.vs[16 * t + j];
-            const int kp = kKeys * c + 16 * t + j;
+            const float4 sv = *reinterpret_cast<const float4 *>(&sh.vs[16 * t + 4 * g]);
+            const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(z[t][i] - m_run[i]);   // 0 for masked keys
-                l_lane[i] += p;
+                const float p = fast_exp2(fmaf(z[t][i], rm, -m_new));   // 0 for masked keys
+                l_lane += p;
                 // masked keys past the context may have any scale bytes (0 * NaN)
-                const float pv = (!MASK || kp <= pos0 + 4 * g + i) ? p * sv : 0.0f;
+                float pv = (!MASK || kKeys * c + 16 * t + 4 * g + i <= my_pos) ? p * svv[i] : 0.0f;
+                // hi and lo must both derive from this rounded product: left
+                // free, the compiler fuses the product into lo's conversion
+                // but not into hi's, and where the product lies within one
+                // fp32 rounding of an fp16 midpoint hi + lo then misses it by
+                // a whole fp16 ulp
+                asm("" : "+v"(pv));
                 const _Float16 h = static_cast<_Float16>(pv);
-                pw[0][4 * g + i][16 * t + j] = h;
-                pw[1][4 * g + i][16 * t + j] = static_cast<_Float16>(pv - static_cast<float>(h));
+                pb_hi[t >> 1][4 * (t & 1) + i] = h;
+                pb_lo[t >> 1][4 * (t & 1) + i] = static_cast<_Float16>(pv - static_cast<float>(h));
             }
         }
-        wave_lds_sync();
-        v8h pa_hi[2], pa_lo[2];
+        // p.v: dim tile m, key half h
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            pa_hi[h] = *reinterpret_cast<const v8h *>(&pw[0][j][16 * g + 8 * h]);
-            pa_lo[h] = *reinterpret_cast<const v8h *>(&pw[1][j][16 * g + 8 * h]);
-        }
-        wave_lds_sync();
-        // p.v: dim tile m, keys 16g + 8h + e of the lane group
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const v2i r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(
-                &sh.v[vgroup(g) + 16 * (4 * j + ((m >> 1) ^ ((j >> 2) & 3))) + 8 * (m & 1)]));
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const v8h vb = nibbles_to_half(static_cast<uint32_t>(h == 0 ? r.x : r.y));
-                o[m] = mfma(pa_hi[h], vb, o[m]);
-                o[m] = mfma(pa_lo[h], vb, o[m]);
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t addr = tr_base + 32 * h * kVRow + 16 * ((2 * m + tr_piece) ^ tr_x);
+                const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)&sh.v[addr]);
+                const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)&sh.v[addr + 16 * kVRow]);
+                const v8h va = __builtin_bit_cast(
+                    v8h, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
+                                    __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
+                o[m] = mfma(va, pb_hi[h], o[m]);
+                o[m] = mfma(va, pb_lo[h], o[m]);
             }
         }
     };
@@ -371,26 +422,31 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     if (!live) return;
 
     // ---- normalise, rotate back, store ----
+    const float inv = 1.0f / rows_sum4(l_lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float inv = 1.0f / row_sum16(l_lane[i]);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) o[m][i] *= inv;
-    }
+    for (int m = 0; m < 8; ++m) o[m] *= inv;
     if constexpr (BH > 0) {
 #pragma unroll
-        for (int span = 1; span < 16 && span < BH; span <<= 1) {   // partner lane j ^ span of the row
-            const bool upper = (j & span) != 0;
+        for (int s = 1; s < 4; s <<= 1) {                          // spans 1, 2: registers i ^ s
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = __shfl_xor(o[m][i], span, 16);
-                    o[m][i] = upper ? (p - o[m][i]) : (o[m][i] + p);
+                    if (i & s) continue;
+                    const float u = o[m][i], v = o[m][i + s];
+                    o[m][i] = u + v;
+                    o[m][i + s] = u - v;
                 }
         }
 #pragma unroll
-        for (int s = 1; s < 8 && 16 * s < BH; s <<= 1) {          // spans 16, 32, 64: registers m ^ s
+        for (int m = 0; m < 8; ++m)                                // spans 4, 8: lane rows g ^ 1, g ^ 2
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[m][i] = rows_butterfly<1>(o[m][i], g);
+                o[m][i] = rows_butterfly<2>(o[m][i], g);
+            }
+#pragma unroll
+        for (int s = 1; s < 8 && 16 * s < BH; s <<= 1) {           // spans 16, 32, 64: registers m ^ s
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 if (m & s) continue;
@@ -406,14 +462,10 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) o[m] *= cb;
     }
+    if (j < rows) {
+        float *dst = a.out + ((int64_t)(row0 + j) * a.num_q_heads + qh) * kHeadDim + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        if (r < rows) {
-            float *dst = a.out + ((int64_t)(row0 + r) * a.num_q_heads + qh) * kHeadDim + j;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) dst[16 * m] = o[m][i];
-        }
+        for (int m = 0; m < 8; ++m) *reinterpret_cast<float4 *>(dst + 16 * m) = make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
     }
 }
 

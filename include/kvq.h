@@ -204,6 +204,7 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
  *                q_start[batch] = num_q, q_len_b <= context_lens[b]
  *                (not checked on the device)
  *   out          fp32 [num_q][num_q_heads][head_dim]
+ *   softmax_scale  positive and finite (else KVQ_ERR_INVALID_ARG)
  *   other arguments as for paged_decode_attn_int4.
  * No workspace.  num_q == 0 or batch == 0 is a no-op returning KVQ_OK.
  */

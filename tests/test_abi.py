@@ -191,5 +191,8 @@ def test_prefill_host_validation():
     assert _prefill(q=None) == kvq.KVQ_ERR_INVALID_ARG
     assert _prefill(qs=None) == kvq.KVQ_ERR_INVALID_ARG
     assert _prefill(out=FAKE + 4) == kvq.KVQ_ERR_INVALID_ARG     # misaligned
+    assert _prefill(scale=0.0) == kvq.KVQ_ERR_INVALID_ARG        # the scale must be positive
+    assert _prefill(scale=-0.088) == kvq.KVQ_ERR_INVALID_ARG
+    assert _prefill(scale=float("nan")) == kvq.KVQ_ERR_INVALID_ARG
     assert _prefill(nq=0) == kvq.KVQ_OK                           # no-op
     assert _prefill(B=0) == kvq.KVQ_OK
