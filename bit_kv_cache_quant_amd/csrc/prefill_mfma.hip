@@ -61,6 +61,8 @@ namespace {
 using namespace dec;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -360,33 +362,53 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
             for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[t][i]);
         zm = rows_max4(zm);
         const float m_new = fmaxf(m_run, zm * rm);   // finite from the first chunk on (key 0 is visible)
-        const float alpha = fast_exp2(m_run - m_new);
-        l_lane *= alpha;
+        // rescale only when some position of the wave has a new maximum (a
+        // wave-uniform branch; alpha is exactly 1 for the others)
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+            const float alpha = fast_exp2(m_run - m_new);
+            l_lane *= alpha;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o[m] *= alpha;
-        m_run = m_new;
-        // weights times the value scale, split hi / lo: the p.v B operands
-        v8h pb_hi[2], pb_lo[2];
+            for (int m = 0; m < 8; ++m) o[m] *= alpha;
+            m_run = m_new;
+        }
+        // weights times the value scale, split hi / lo: the p.v B operands,
+        // built a pair of keys at a time (v_cvt_pk_f16_f32)
+        v2h ph[4][2], pl[4][2];   // [t][i / 2]
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float4 sv = *reinterpret_cast<const float4 *>(&sh.vs[16 * t + 4 * g]);
             const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
+            float pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(fmaf(z[t][i], rm, -m_new));   // 0 for masked keys
+                const float p = fast_exp2(fmaf(z[t][i], rm, -m_run));   // 0 for masked keys
                 l_lane += p;
                 // masked keys past the context may have any scale bytes (0 * NaN)
-                float pv = (!MASK || kKeys * c + 16 * t + 4 * g + i <= my_pos) ? p * svv[i] : 0.0f;
+                pv[i] = (!MASK || kKeys * c + 16 * t + 4 * g + i <= my_pos) ? p * svv[i] : 0.0f;
                 // hi and lo must both derive from this rounded product: left
                 // free, the compiler fuses the product into lo's conversion
                 // but not into hi's, and where the product lies within one
                 // fp32 rounding of an fp16 midpoint hi + lo then misses it by
                 // a whole fp16 ulp
-                asm("" : "+v"(pv));
-                const _Float16 h = static_cast<_Float16>(pv);
-                pb_hi[t >> 1][4 * (t & 1) + i] = h;
-                pb_lo[t >> 1][4 * (t & 1) + i] = static_cast<_Float16>(pv - static_cast<float>(h));
+                asm("" : "+v"(pv[i]));
             }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const v2h hi = __builtin_convertvector((v2f){pv[2 * u], pv[2 * u + 1]}, v2h);
+                const v2f back = __builtin_convertvector(hi, v2f);
+                ph[t][u] = hi;
+                pl[t][u] = __builtin_convertvector((v2f){pv[2 * u] - back[0], pv[2 * u + 1] - back[1]}, v2h);
+            }
+        }
+        v8h pb_hi[2], pb_lo[2];   // element 4 (t & 1) + i of half t / 2
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            pb_hi[h] = __builtin_shufflevector(__builtin_shufflevector(ph[2 * h][0], ph[2 * h][1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(ph[2 * h + 1][0], ph[2 * h + 1][1], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+            pb_lo[h] = __builtin_shufflevector(__builtin_shufflevector(pl[2 * h][0], pl[2 * h][1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(pl[2 * h + 1][0], pl[2 * h + 1][1], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
         }
         // p.v: dim tile m, key half h
 #pragma unroll
@@ -407,18 +429,24 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
         }
     };
 
+    // chunks below n_full hold only keys every position of the tile sees
+    // (64 c + 63 <= pos0); the rest need the causal mask.  Two loops, one
+    // per variant, keep the accumulators in place (one loop choosing per
+    // chunk made the compiler copy them around).
+    const int n_full = min((pos0 + 1) / kKeys, nchunks);
     Raw raw;
     load(0, raw);
-    for (int c = 0; c < nchunks; ++c) {
-        __syncthreads();          // every wave is done with the previous chunk's LDS
-        stage(raw);
-        __syncthreads();
-        if (c + 1 < nchunks) load(c + 1, raw);
-        if (live) {
-            if (kKeys * c + kKeys - 1 > pos0) compute(c, std::true_type{});
-            else compute(c, std::false_type{});
+    auto run = [&](int c0, int c1, auto masked) {
+        for (int c = c0; c < c1; ++c) {
+            __syncthreads();          // every wave is done with the previous chunk's LDS
+            stage(raw);
+            __syncthreads();
+            if (c + 1 < nchunks) load(c + 1, raw);
+            if (live) compute(c, masked);
         }
-    }
+    };
+    run(0, n_full, std::false_type{});
+    run(n_full, nchunks, std::true_type{});
     if (!live) return;
 
     // ---- normalise, rotate back, store ----
