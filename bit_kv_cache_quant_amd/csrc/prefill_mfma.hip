@@ -76,11 +76,16 @@ constexpr int kVRow = 2 * kHeadDim;   // bytes per fp16 value row
 struct alignas(16) PrefillShared {
     uint8_t kev[kKeys * kKPitch];        // key codes, even dims' nibbles at the top of each byte
     uint8_t kod[kKeys * kKPitch];        // key codes, odd dims' nibbles at the top (low nibble 0)
-    // values as fp16; row T's 16-byte piece p at piece slot p ^ 2 (T & 7), so
-    // that the 8 rows one half-wave reads transposed cover all 64 banks once
+    // values as fp16; row T's 16-byte piece p at piece slot p ^ vswz(T)
     uint8_t v[kKeys * kVRow];
     float ks[kKeys], vs[kKeys];          // scales
 };
+
+// Piece swizzle of value row T: bits 1-3 (2 (T & 7)) give the 8 rows a
+// half-wave reads transposed 8 different 32-byte piece pairs (all 64 banks
+// once); bit 0 ((T >> 1) & 1) with bit 1 gives the 4 rows of one staging
+// write pass 4 different piece positions mod 4 (16 lanes, 16 bank groups).
+__host__ __device__ constexpr int vswz(int T) { return (2 * (T & 7)) | ((T >> 1) & 1); }
 
 __device__ __forceinline__ v4f mfma(v8h a, v8h b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -313,9 +318,10 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
         *reinterpret_cast<uint4 *>(&sh.kod[T * kKPitch + 16 * lp]) = make_uint4(od[0], od[1], od[2], od[3]);
         // value codes of dims 32 lp + 8 s .. + 7 -> fp16 piece 4 lp + s of row T
         const uint32_t vw[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+        const int vx = vswz(T);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * lp + s) ^ (2 * (T & 7)))]) = nibbles_to_half(vw[s]);
+            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * lp + s) ^ vx)]) = nibbles_to_half(vw[s]);
         if (lane < 16) sh.ks[16 * wave + lane] = half_to_float(r.s);
         else if (lane < 32) sh.vs[16 * wave + lane - 16] = half_to_float(r.s);
     };
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const int tr_key = 4 * g + (j >> 2);
     const uint32_t tr_base = tr_key * kVRow + 8 * (j & 1);
     const int tr_piece = (j & 3) >> 1;
-    const int tr_x = 2 * (tr_key & 7);     // the row's piece swizzle (rows + 16, + 32 share it)
+    const int tr_x = vswz(tr_key);          // the row's piece swizzle (rows + 16, + 32 share it)
 
     auto compute = [&](int c, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
