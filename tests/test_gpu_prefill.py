@@ -64,14 +64,52 @@ def test_prefill_whole_prompt(dev, bh, P):
     _check(w, dev, [200])
 
 
-def test_prefill_ragged_batch_tails_and_empty(dev):
+@pytest.mark.parametrize("bh,P", [(64, 16), (0, 32)])
+def test_prefill_ragged_batch_tails_and_empty(dev, bh, P):
     """Several sequences, query counts that are not multiples of the 16-row
     tile, a sequence with no queries and an empty one; queries are each
     sequence's last positions (chunked prefill)."""
     lens = [130, 17, 64, 0, 5, 300]
     qlens = [130, 5, 33, 0, 5, 1]
-    w = wl.small(len(lens), lens, 64, 16, cfg_id=250)
+    w = wl.small(len(lens), lens, bh, P, cfg_id=250 + P)
     _check(w, dev, qlens)
+
+
+def test_prefill_graph_replay(dev):
+    """The prefill call enqueues one kernel and allocates nothing, so it can
+    be captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, gives the eager result bit for bit."""
+    w = wl.small(2, [200, 77], 64, 16, cfg_id=280)
+    kp, vp = int4_pools(w, dev)
+    prefill(w, 0, dev, kp, vp, w.had_block)
+    qlens = [200, 20]
+    qs = torch.as_tensor(np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32), device=dev)
+    q = _queries(int(sum(qlens)), w.num_q_heads, 1000 + w.cfg_id, dev)
+    pt = torch.as_tensor(w.table(0), device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    out = torch.empty((int(sum(qlens)), w.num_q_heads, D), dtype=torch.float32, device=dev)
+    call = lambda: kvq.paged_prefill_attn_int4(q, qs, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.had_block,
+                                               w.softmax_scale, out=out)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        call()
+        torch.cuda.synchronize()
+    say("prefill graph: 3 replays equal to the eager call")
 
 
 @pytest.mark.parametrize("group", [1, 2, 8])
