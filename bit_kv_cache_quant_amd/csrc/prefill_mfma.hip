@@ -209,6 +209,17 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const int nchunks = last_pos / kKeys + 1;
     const int my_pos = pos0 + j;                 // this lane's query position
 
+    // Out of contract (more queries than cached tokens, which includes an
+    // empty context): the rows get zeros and no page is read.
+    if (qlen > L) {
+        if (live && j < rows) {
+            float *dst = a.out + ((int64_t)(row0 + j) * a.num_q_heads + qh) * kHeadDim + 4 * g;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) *reinterpret_cast<float4 *>(dst + 16 * m) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        return;
+    }
+
     __shared__ PrefillShared sh;
 
     // ---- the rotated query of head qh: lane (g, j) holds position j, dims 32g .. 32g + 31 ----

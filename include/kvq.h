@@ -201,8 +201,9 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
  *
  *   q            fp16 [num_q][num_q_heads][head_dim]
  *   q_start      int32 [batch + 1], device: q_start[0] = 0, nondecreasing,
- *                q_start[batch] = num_q, q_len_b <= context_lens[b]
- *                (not checked on the device)
+ *                q_start[batch] = num_q, q_len_b <= context_lens[b]; a
+ *                sequence with q_len_b > context_lens[b] gets zero rows
+ *                and none of its pages is read
  *   out          fp32 [num_q][num_q_heads][head_dim]
  *   softmax_scale  positive and finite (else KVQ_ERR_INVALID_ARG)
  *   other arguments as for paged_decode_attn_int4.

@@ -75,6 +75,29 @@ def test_prefill_ragged_batch_tails_and_empty(dev, bh, P):
     _check(w, dev, qlens)
 
 
+def test_prefill_more_queries_than_context_gives_zero_rows(dev):
+    """Out of contract, handled on the device: a sequence claiming more query
+    positions than cached tokens gets zero rows (none of its pages is read);
+    the other sequences are unaffected."""
+    w = wl.small(2, [40, 5], 64, 16, cfg_id=290)
+    kp, vp = int4_pools(w, dev)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    prefill(w, 0, dev, kp, vp, w.had_block, host_pools=(hk, hv))
+    qlens = [3, 8]
+    qs = torch.as_tensor(np.array([0, 3, 11], np.int32), device=dev)
+    q = _queries(11, w.num_q_heads, 1000 + w.cfg_id, dev)
+    out = kvq.paged_prefill_attn_int4(q, qs, kp, vp, torch.as_tensor(w.table(0), device=dev),
+                                      torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, w.page_size,
+                                      w.had_block, w.softmax_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[3:] == 0.0)
+    want = oracle.paged_decode_attn_int4(q.cpu().numpy()[:3], hk, hv, np.repeat(w.table(0)[:1], 3, axis=0),
+                                         np.array([38, 39, 40], np.int32), w.num_kv_heads, w.page_size,
+                                         w.had_block, w.softmax_scale)
+    assert float(np.max(np.abs(got[:3] - want))) <= ATOL
+
+
 def test_prefill_graph_replay(dev):
     """The prefill call enqueues one kernel and allocates nothing, so it can
     be captured in a HIP graph: every replay, with eager work and
