@@ -15,12 +15,12 @@
 // token-head).  Both products are exact integer contractions once the fp32
 // operand is written in fixed point, so they map onto int8 MFMA:
 //
-//   q.k : the rotated, pre-scaled query of head hq is written as a 21-bit
-//         fixed-point integer X = round(q' 2^(20-E)), E the exponent of
-//         max|q'| of that head, split into limbs X = L0 2^14 + L1 2^7 + L2
-//         (L0 signed, L1, L2 in [0,127]).  One MFMA row per (head, limb):
-//         4 heads x 3 limbs use 12 of the 16 rows (the 4th limb row of each
-//         head is zero).  Keys enter as offset-binary nibbles u = c + 8 in
+//   q.k : the rotated, pre-scaled query of head hq is written as a 28-bit
+//         fixed-point integer X = round(q' 2^(27-E)), E the exponent of
+//         max|q'| of that head, split into limbs
+//         X = L0 2^21 + L1 2^14 + L2 2^7 + L3 (L0 signed, L1..L3 in
+//         [0,127]).  One MFMA row per (head, limb): 4 heads x 4 limbs fill
+//         the 16 rows.  Keys enter as offset-binary nibbles u = c + 8 in
 //         [0, 15]; the accumulator starts at -8 sum_d L (per row), so the
 //         integer result is exactly sum_d L_d c_d.
 //   p.v : the unnormalised weight times the value scale, P = p s_V, is
@@ -30,10 +30,13 @@
 //         also enter as offset-binary nibbles u = c + 8; the MFMA gives
 //         sum_t F_t u_t exactly, and 8 sum_t F_t (one number per head and
 //         chunk) is subtracted in fp32.
-// Limbs are recombined with integer shifts (exact, below 2^31) and one
-// conversion.  The approximations are the 2^-21 relative roundings of q' and
-// P, and fp32 rounding of the accumulation and of the offset subtraction
-// (relative error ~1e-6), far inside the 2e-3 tolerance.
+// Limbs are recombined with integer shifts (exact, below 2^31) and fp32
+// conversions.  The approximations are the 2^-28 relative rounding of q' and
+// the 2^-21 one of P (each relative to the largest element of its vector),
+// and fp32 rounding of the accumulation and of the offset subtraction.  (With
+// a 21-bit query the query's rounding dominated the error: scores are sums of
+// 128 products with keys up to 7 scale units, and a sharp softmax turns their
+// absolute error into a relative weight error.)
 //
 // Work decomposition: one wave owns one work item (sequence, KV head, 4 of
 // its query heads, a page range of at most 2048 tokens) and walks it in
@@ -113,16 +116,20 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// D0 2^14 + D1 2^7 + D2 of one (head, limbs 0..2) row group, exact in 32
-// bits (|D0| <= 2^16 for q.k; 0 <= D0 < 64*127*15 for p.v), then one rounding.
-// (Two shift-and-add instructions; the empty asm keeps the compiler from
-// re-associating them into three.)
-__device__ __forceinline__ float limbs_to_float(v4i d) {
-    int s = (d[0] << 7) + d[1];
-    asm("" : "+v"(s));
-    s = (s << 7) + d[2];
-    return static_cast<float>(s);
+// D0 2^21 + D1 2^14 + D2 2^7 + D3 of one (head, limbs 0..3) row group of
+// q.k: |D0| <= 2^16 and |D1..D3| < 2^17, so the halves D0 2^7 + D1 (below
+// 2^24: exact in fp32) and D2 2^7 + D3 (below 2^25) are exact in int32, and
+// the sum takes one fma (one rounding, plus at most one in the low half's
+// conversion, both relative 2^-24 to the largest term).
+__device__ __forceinline__ float limbs4_to_float(v4i d) {
+    const int hi = (d[0] << 7) + d[1];
+    const int lo = (d[2] << 7) + d[3];
+    return fmaf(static_cast<float>(hi), 16384.0f, static_cast<float>(lo));
 }
+// D0 2^14 + D1 2^7 + D2 of one (head, limbs 0..2) row group of p.v, exact in
+// 32 bits (0 <= D0 < 64*127*15), then one rounding.  (Two shift-and-add
+// instructions; the empty asm keeps the compiler from re-associating them
+// into three.)
 __device__ __forceinline__ float ulimbs_to_float(v4i d) {
     uint32_t s = (static_cast<uint32_t>(d[0]) << 7) + static_cast<uint32_t>(d[1]);
     asm("" : "+v"(s));
@@ -366,17 +373,18 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     amax = row_max16(amax);
     int qexp = 0;
     if (amax > 0.0f) (void)frexpf(amax, &qexp);      // amax < 2^qexp
-    const float qmul = ldexpf(1.0f, 20 - qexp);
+    const float qmul = ldexpf(1.0f, 27 - qexp);
     int lsum[4] = {0, 0, 0, 0};
     QLimbs &qlimb = sq.qlimb;
     {
-        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]; limb 3 stays 0
+        uint32_t w[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // [limb][parity]
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
+            // |X| <= 2^27 (exact in fp32 before the conversion)
             const int X = static_cast<int>(rintf(qv[k] * qmul));
-            const int limb[3] = {X >> 14, (X >> 7) & 127, X & 127};
+            const int limb[4] = {X >> 21, (X >> 14) & 127, (X >> 7) & 127, X & 127};
 #pragma unroll
-            for (int r = 0; r < 3; ++r) {
+            for (int r = 0; r < 4; ++r) {
                 lsum[r] += limb[r];
                 w[r][k & 1] |= (static_cast<uint32_t>(limb[r]) & 0xFFu) << (8 * (k >> 1));
             }
@@ -388,11 +396,10 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             qlimb[g][r][1][j >> 2][j & 3] = w[r][1];
         }
     }
-    v4i qk_init;    // rows (head g, limbs 0..2, zero row): -8 sum_d L, offset-binary keys
+    v4i qk_init;    // rows (head g, limbs 0..3): -8 sum_d L, offset-binary keys
 #pragma unroll
-    for (int r = 0; r < 3; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
-    qk_init[3] = 0;
-    const float score_mul = ldexpf(a.score_scale, qexp - 20);   // head g
+    for (int r = 0; r < 4; ++r) qk_init[r] = -8 * row_sum16_i(lsum[r]);
+    const float score_mul = ldexpf(a.score_scale, qexp - 27);   // head g
     wave_lds_sync();
     v4i qa0, qa1;   // A operands: row (head j/4, limb j%4), k-slots of group g
     {
@@ -455,7 +462,7 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             split_offset(cd.k[t].w, lo[3], hi[3]);
             v4i d = mfma(qa0, v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]}, qk_init);
             d = mfma(qa1, v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}, d);
-            const float sc = limbs_to_float(d) * score_mul * half_to_float(ks[t]);
+            const float sc = limbs4_to_float(d) * score_mul * half_to_float(ks[t]);
             z[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? sc : -INFINITY;
             zmax = fmaxf(zmax, z[t]);
         }
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void decode_int4_balanced_kernel(DecodeAr
     WaveHeld &hw = held[wave];
     int pb = pb0;
     for (int b = b0; b < B && pb < end; ++b) {
-        const int L = a.context_lens[b];
+        const int L = decode_len(a, b);
         const int nch = L > 0 ? (L + kChunk - 1) / kChunk : 0;
         const int pb1 = pb + nch;
         const int c0 = max(start, pb) - pb;

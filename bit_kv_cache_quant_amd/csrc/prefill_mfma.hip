@@ -22,19 +22,22 @@
 // query positions as columns), so that the weights leave the score MFMA in
 // exactly the lanes and registers the p.v MFMA takes them from.
 //   q.k  S^T = K Q^T, exact integer products on v_mfma_i32_16x16x64_i8, as in
-//        the decode: the rotated query of each position is a 21-bit
-//        fixed-point integer X = round(q' 2^(20-E)) (E the exponent of its
-//        max |q'|) split into limbs X = L0 2^14 + L1 2^7 + L2, one MFMA per
-//        limb and nibble half.  A (keys): row j = key 16t + j, its 16 code
+//        the decode: the rotated query of each position is a 24-bit
+//        fixed-point integer X = round(q' 2^(23-E)) (E chosen with max |q'| <
+//        2^E (1 - 2^-7)) written in balanced signed 8-bit digits
+//        X = D0 2^16 + D1 2^8 + D2, each in [-128, 127], one MFMA per digit
+//        and nibble half.  A (keys): row j = key 16t + j, its 16 code
 //        bytes (dims 32g .. 32g + 31) with the even dims' nibbles moved to the
 //        top of each byte, or the odd dims' kept there: signed bytes 16 c.
-//        B (limb): column j = query position j, the dims 32g + 2e (even half)
-//        or 32g + 2e + 1 (odd half).  The limb results are exact in int32;
-//        L0 and L1 are combined in int32, the rest in fp32, then the key's
-//        scale.  D: lane (g, j) holds keys 16t + 4g + i (i = 0..3) of query
-//        position j.  (fp16 products summed in fp32 were measurably less
-//        accurate here: with the rotation every code is nonzero and the
-//        softmax of large scores amplifies their rounding.)
+//        B (digit): column j = query position j, the dims 32g + 2e (even half)
+//        or 32g + 2e + 1 (odd half).  The digit results are exact in int32
+//        (below 2^21 in magnitude); D0 and D1 are combined in int32, the
+//        rest in fp32, then the key's scale.  D: lane (g, j) holds keys
+//        16t + 4g + i (i = 0..3) of query position j.  (fp16 products summed
+//        in fp32 were measurably less accurate here: with the rotation every
+//        code is nonzero and the softmax of large scores amplifies their
+//        rounding.  So was a 21-bit query: its rounding, relative 2^-21 to
+//        the largest element, dominated the error at sharp softmax scales.)
 //   softmax: online per query position; a position's 64 scores of a chunk
 //        are 16 registers in each of the 4 lanes j, j + 16, j + 32, j + 48
 //        (two lane-swap steps reduce across them); the position's factor
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
 
     const int q0 = a.q_start[b];
     const int qlen = a.q_start[b + 1] - q0;
-    const int L = a.context_lens[b];
+    const int L = prefill_len(a, b);
     const int rows = min(kQRows, qlen - kQRows * tile);
     const int row0 = q0 + kQRows * tile;
     const int pos0 = L - qlen + kQRows * tile;   // position of row 0
@@ -268,32 +271,40 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
             for (int r = 0; r < 32; ++r) x[r] *= c;
         }
     }
-    // 21-bit fixed point per (position, head): the position's 128 dims are in
+    // 24-bit fixed point per (position, head): the position's 128 dims are in
     // lanes j, j + 16, j + 32, j + 48
     float amax = 0.0f;
 #pragma unroll
     for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(x[r]));
     amax = rows_max4(amax);
     int qexp = 0;
-    if (amax > 0.0f) (void)frexpf(amax, &qexp);     // amax < 2^qexp
-    const float qmul = ldexpf(1.0f, 20 - qexp);
-    v4i qb[3][2];   // [limb][even / odd dims]: byte e of dword w = dim 32g + 2 (4w + e) + half
+    // amax (1 + 2^-7) < 2^qexp, so |X| <= 2^23 / (1 + 2^-7) < 127 (2^16 +
+    // 2^8 + 1): the top digit stays in [-128, 127]
+    if (amax > 0.0f) (void)frexpf(amax * 1.0078125f, &qexp);
+    const float qmul = ldexpf(1.0f, 23 - qexp);
+    v4i qb[3][2];   // [digit][even / odd dims]: byte e of dword w = dim 32g + 2 (4w + e) + half
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         uint32_t wd[3][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int X = static_cast<int>(rintf(x[2 * e + h] * qmul));
-            const int limb[3] = {X >> 14, (X >> 7) & 127, X & 127};
+            // balanced digits: D2 = X mod 256 in [-128, 127], then the same on
+            // (X - D2) / 256; the bytes of X - D2 2^0 - D1 2^8 are D0's
+            const int d2 = static_cast<int>(static_cast<int8_t>(X & 0xFF));
+            const int x1 = (X - d2) >> 8;
+            const int d1 = static_cast<int>(static_cast<int8_t>(x1 & 0xFF));
+            const int d0 = (x1 - d1) >> 8;
+            const int dig[3] = {d0, d1, d2};
 #pragma unroll
-            for (int l = 0; l < 3; ++l) wd[l][e >> 2] |= (static_cast<uint32_t>(limb[l]) & 0xFFu) << (8 * (e & 3));
+            for (int l = 0; l < 3; ++l) wd[l][e >> 2] |= (static_cast<uint32_t>(dig[l]) & 0xFFu) << (8 * (e & 3));
         }
 #pragma unroll
         for (int l = 0; l < 3; ++l) qb[l][h] = v4i{(int)wd[l][0], (int)wd[l][1], (int)wd[l][2], (int)wd[l][3]};
     }
-    // score factor of this position (log2 units): 2^(E-20), 1/16 for the
+    // score factor of this position (log2 units): 2^(E-23), 1/16 for the
     // nibble position, the softmax scale (positive)
-    const float rm = ldexpf(a.score_scale * 0.0625f, qexp - 20);
+    const float rm = ldexpf(a.score_scale * 0.0625f, qexp - 23);
 
     // ---- loads of one chunk: wave w takes keys 16w .. 16w + 15 ----
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
@@ -364,8 +375,9 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
             const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // |L0 . k| < 2^20, so L0 . k 2^7 + L1 . k is exact in int32
-                const float dot = fmaf(static_cast<float>((dl[0][i] << 7) + dl[1][i]), 128.0f,
+                // |D . k| <= 128 * 128 * 128 = 2^21 for each digit, so
+                // D0 . k 2^8 + D1 . k is exact in int32
+                const float dot = fmaf(static_cast<float>((dl[0][i] << 8) + dl[1][i]), 256.0f,
                                        static_cast<float>(dl[2][i]));
                 const float sc = dot * skv[i];
                 z[t][i] = (!MASK || kKeys * c + 16 * t + 4 * g + i <= my_pos) ? sc : -INFINITY;
