@@ -305,12 +305,12 @@ def main(argv=None):
     mid.record()
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step(ev=None, mid_ev=None):
         kvq.kv_quant_append(k_new, v_new, seq, pos, pt, kp, vp, w.page_size, w.had_block)
         if ev is not None:
             ev[0].record()
         kvq.paged_decode_attn_int4(q, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.had_block, w.softmax_scale,
-                                   maxctx, out=out, workspace=ws)
+                                   maxctx, out=out, workspace=ws, phase_event=mid_ev)
 
     for _ in range(args.warmup):
         step()
@@ -323,9 +323,8 @@ def main(argv=None):
     def make_events(n):
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n)) for _ in range(args.steps)]
         for e in evs:
-            e[-1].record()                # instantiate; the library re-records the decode-phase one
+            e[-1].record()                # instantiate; the decode call re-records it between its kernels
         return evs
-    kvq.set_decode_phase_event(None)
     bracket = make_events(2)              # (before the partial kernel, after it)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -335,12 +334,10 @@ def main(argv=None):
     t_start.record()
     for i in range(args.steps):
         e1, em = bracket[i]
-        kvq.set_decode_phase_event(em)
-        step(ev=(e1,))
+        step(ev=(e1,), mid_ev=em)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    kvq.set_decode_phase_event(None)
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
     t_partial = [e1.elapsed_time(em) for e1, em in bracket]
@@ -350,12 +347,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     for i in range(args.steps):
         e0, e1, e2, em = phase[i]
-        kvq.set_decode_phase_event(em)
         e0.record()
-        step(ev=(e1,))
+        step(ev=(e1,), mid_ev=em)
         e2.record()
     torch.cuda.synchronize()
-    kvq.set_decode_phase_event(None)
     t_append = [p[0].elapsed_time(p[1]) for p in phase]
     t_combine = [p[3].elapsed_time(p[2]) for p in phase]
     mean = lambda xs: sum(xs) / len(xs)
@@ -384,7 +379,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "int4 cache x fp16 scales; int8 MFMA fixed-point q.k and p.v, fp32 softmax",
         "data": "synthetic",
         "config": {
             "workload": "decode step with append: batch 256, ctx U[1024,8192] (seeded), 8 KV heads x 128, "
@@ -624,8 +619,8 @@ def fp16_measurement(dev, iters, warmup):
     maxctx = int(w.context_lens.max())
     out = torch.empty((w.batch, 32, 128), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.workspace_bytes(w.batch, 32, 8, maxctx, 16), dtype=torch.uint8, device=dev)
-    call = lambda: kvq.paged_decode_attn_fp16(q, kp, vp, pt, cl, 8, 16, w.softmax_scale, maxctx,
-                                              out=out, workspace=ws)
+    call = lambda ev=None: kvq.paged_decode_attn_fp16(q, kp, vp, pt, cl, 8, 16, w.softmax_scale, maxctx,
+                                                      out=out, workspace=ws, phase_event=ev)
     ms, med = time_calls(call, iters, warmup)
     # partial kernel alone: an event before the call and the library's event after the kernel
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
@@ -633,11 +628,9 @@ def fp16_measurement(dev, iters, warmup):
         em.record()
     torch.cuda.synchronize()
     for e0, em in evs:
-        kvq.set_decode_phase_event(em)
         e0.record()
-        call()
+        call(em)
     torch.cuda.synchronize()
-    kvq.set_decode_phase_event(None)
     part = sum(e0.elapsed_time(em) for e0, em in evs) / iters
     nb = decode_bytes(w, int4=False)
     res = {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),

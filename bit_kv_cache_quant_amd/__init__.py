@@ -32,13 +32,12 @@ SIGNATURES = {
     "kv_quant_append": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _I32, _P]),
     "paged_decode_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attn_int4": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
-                                              _I32, _I32, _F32, _P, _P, _SZ, _I32, _P]),
+                                              _I32, _I32, _F32, _P, _P, _SZ, _I32, _P, _P]),
     "paged_prefill_attn_int4": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                _I32, _I32, _F32, _P, _P]),
     "kv_append_fp16": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "paged_decode_attn_fp16": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
-                                              _I32, _F32, _P, _P, _SZ, _I32, _P]),
-    "kvq_set_decode_phase_event": (ctypes.c_int, [_P]),
+                                              _I32, _F32, _P, _P, _SZ, _I32, _P, _P]),
 }
 
 _lib = None
@@ -78,14 +77,6 @@ def workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_context
                     page_size: int, pages_per_split: int = 0, head_dim: int = HEAD_DIM) -> int:
     return int(lib().paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                                        max_context_len, page_size, pages_per_split))
-
-
-def set_decode_phase_event(event) -> None:
-    """Timing hook: record ``event`` (a torch.cuda.Event that has been recorded
-    once, or None) between the split-K partial kernel and the combine kernel
-    of every later decode call."""
-    handle = None if event is None else event.cuda_event
-    _check(lib().kvq_set_decode_phase_event(handle), "kvq_set_decode_phase_event")
 
 
 # --------------------------------------------------------------------------
@@ -163,9 +154,15 @@ def kv_append_fp16(k_new, v_new, token_seq, token_pos, page_table, k_pool, v_poo
     _check(rc, "kv_append_fp16")
 
 
+def _event_handle(event):
+    """hipEvent_t of a torch.cuda.Event (which must have been recorded once, so
+    that it exists), or None."""
+    return None if event is None else event.cuda_event
+
+
 def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
             page_size: int, had_block: int, softmax_scale: float, max_context_len: int,
-            out=None, workspace=None, pages_per_split: int = 0):
+            out=None, workspace=None, pages_per_split: int = 0, phase_event=None):
     import torch
     B, hq, d = q.shape
     if int4:
@@ -184,7 +181,10 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
     need = workspace_bytes(B, hq, num_kv_heads, max_context_len, page_size, pages_per_split, d) if B else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_ptr = _dev(workspace, torch.uint8, "workspace")
+    if workspace.device != q.device:
+        raise ValueError(f"workspace must be on {q.device}, got {workspace.device}")
+    ws_bytes = workspace.numel()
     pool_dtype = torch.uint8 if int4 else torch.float16
     args = [_dev(q, torch.float16, "q", 3), _dev(k_pool, pool_dtype, "k_pool"),
             _dev(v_pool, pool_dtype, "v_pool"), k_pool.shape[0],
@@ -193,8 +193,8 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
             int(num_kv_heads), d, int(page_size)]
     if int4:
         args.append(int(had_block))
-    args += [float(softmax_scale), _dev(out, torch.float32, "out", 3), workspace.data_ptr(), ws_bytes,
-             int(pages_per_split), _stream(q)]
+    args += [float(softmax_scale), _dev(out, torch.float32, "out", 3), ws_ptr, ws_bytes,
+             int(pages_per_split), _event_handle(phase_event), _stream(q)]
     fn = lib().paged_decode_attn_int4 if int4 else lib().paged_decode_attn_fp16
     _check(fn(*args), "paged_decode_attn_int4" if int4 else "paged_decode_attn_fp16")
     return out
@@ -229,15 +229,18 @@ def paged_prefill_attn_int4(q, q_start, k_pool, v_pool, page_table, context_lens
 
 def paged_decode_attn_int4(q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
                            page_size: int, had_block: int, softmax_scale: float,
-                           max_context_len: int, out=None, workspace=None, pages_per_split: int = 0):
-    """One decode step over the INT4 cache; returns fp32 [B][Hq][D]."""
+                           max_context_len: int, out=None, workspace=None, pages_per_split: int = 0,
+                           phase_event=None):
+    """One decode step over the INT4 cache; returns fp32 [B][Hq][D].
+    ``phase_event`` (a torch.cuda.Event recorded once before, or None) is
+    recorded between the split-K partial kernel and the merge."""
     return _decode(True, q, k_pool, v_pool, page_table, context_lens, num_kv_heads, page_size,
-                   had_block, softmax_scale, max_context_len, out, workspace, pages_per_split)
+                   had_block, softmax_scale, max_context_len, out, workspace, pages_per_split, phase_event)
 
 
 def paged_decode_attn_fp16(q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
                            page_size: int, softmax_scale: float, max_context_len: int,
-                           out=None, workspace=None, pages_per_split: int = 0):
+                           out=None, workspace=None, pages_per_split: int = 0, phase_event=None):
     """Baseline decode over fp16 pools; returns fp32 [B][Hq][D]."""
     return _decode(False, q, k_pool, v_pool, page_table, context_lens, num_kv_heads, page_size,
-                   0, softmax_scale, max_context_len, out, workspace, pages_per_split)
+                   0, softmax_scale, max_context_len, out, workspace, pages_per_split, phase_event)

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         po = a.ws_o + first * kHeadDim;
         limit = a.num_splits;
         r0 = load_round(ml, po, s0, step, limit, t);
-        const int L = a.context_lens[b];
+        const int L = decode_len(a, b);
         const int npages = (L + a.page_size - 1) >> a.page_shift;
         nsplit = L > 0 ? (npages + a.pages_per_split - 1) / a.pages_per_split : 0;
     }

@@ -136,7 +136,7 @@ __device__ __forceinline__ SplitItem split_item(const DecodeArgs &a, const int w
     if (slot >= head_slots) return it;
     it.hk = slot / a.head_chunks;
     it.chunk_id = slot - it.hk * a.head_chunks;
-    it.L = a.context_lens[it.b];
+    it.L = decode_len(a, it.b);
     if (it.L <= 0) return it;
     const int npages = (it.L + P - 1) / P;
     constexpr int kChunkPages = kChunkTokens / P;
@@ -180,7 +180,7 @@ __device__ __forceinline__ BlockRange balanced_range(const DecodeArgs &a, ScanSp
     if (B <= 64) {
         // one wave: lane i holds sequence i; shuffle scan, no block barriers
         if (wave == 0) {
-            const int L = lane < B ? a.context_lens[lane] : 0;
+            const int L = lane < B ? decode_len(a, lane) : 0;
             const int nch = L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
             int inc = nch;
 #pragma unroll
@@ -197,7 +197,7 @@ __device__ __forceinline__ BlockRange balanced_range(const DecodeArgs &a, ScanSp
         const int i1 = min(i0 + per, B);
         int local = 0;
         for (int i = i0; i < i1; ++i) {
-            const int L = a.context_lens[i];
+            const int L = decode_len(a, i);
             local += L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
         }
         sp.part[threadIdx.x] = local;
@@ -211,7 +211,7 @@ __device__ __forceinline__ BlockRange balanced_range(const DecodeArgs &a, ScanSp
         int run = sp.part[threadIdx.x] - local;
         for (int i = i0; i < i1; ++i) {
             sp.prefix[i] = run;
-            const int L = a.context_lens[i];
+            const int L = decode_len(a, i);
             run += L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
         }
         if (threadIdx.x == kThreads - 1) sp.prefix[B] = sp.part[kThreads - 1];

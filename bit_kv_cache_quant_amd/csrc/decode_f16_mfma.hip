@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void decode_f16_balanced_kernel(DecodeArg
     const int64_t unit_base = ((int64_t)(qd * kWaves + wave) * kH) * per_head + gi;
     int pb = pb0;
     for (int b = b0; b < B && pb < end; ++b) {
-        const int L = a.context_lens[b];
+        const int L = decode_len(a, b);
         const int nch = L > 0 ? (L + kChunkTokens - 1) / kChunkTokens : 0;
         const int pb1 = pb + nch;
         const int c0 = max(start, pb) - pb;

@@ -111,9 +111,6 @@ size_t balanced_workspace_bytes(const BalancedPlan &pl, int32_t batch) {
     return floats * sizeof(float) + (((size_t)batch + 1) * sizeof(int32_t) + 15) / 16 * 16;
 }
 
-// Timing hook (see kvq_set_decode_phase_event in include/kvq.h).
-void *g_phase_event = nullptr;
-
 // Optional debug mode (environment variable KVQ_CHECK=1): copy the page table
 // and lengths to the host (this synchronises the stream) and range-check them.
 bool debug_checks_enabled() {
@@ -130,6 +127,7 @@ int check_append_indices(const int32_t *token_seq, const int32_t *token_pos, int
                          int32_t page_size, hipStream_t stream) {
     int32_t *seq = (int32_t *)malloc(sizeof(int32_t) * num_tokens);
     int32_t *pos = (int32_t *)malloc(sizeof(int32_t) * num_tokens);
+    int32_t *pt = nullptr;
     int rc = KVQ_OK;
     if (!seq || !pos) { free(seq); free(pos); return KVQ_ERR_INVALID_ARG; }
     if (hipMemcpyAsync(seq, token_seq, sizeof(int32_t) * num_tokens, hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -137,15 +135,27 @@ int check_append_indices(const int32_t *token_seq, const int32_t *token_pos, int
         hipStreamSynchronize(stream) != hipSuccess) {
         rc = KVQ_ERR_HIP;
     }
+    // the page-table rows the call addresses (0 .. largest sequence), in one copy on the stream
+    int32_t rows = 0;
     for (int32_t t = 0; rc == KVQ_OK && t < num_tokens; ++t) {
-        if (seq[t] < 0 || pos[t] < 0 || pos[t] / page_size >= max_pages_per_seq) { rc = KVQ_ERR_INVALID_ARG; break; }
-        int32_t page = -1;
-        const int32_t *src = page_table + (int64_t)seq[t] * max_pages_per_seq + pos[t] / page_size;
-        if (hipMemcpy(&page, src, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) { rc = KVQ_ERR_HIP; break; }
+        if (seq[t] < 0 || pos[t] < 0 || pos[t] / page_size >= max_pages_per_seq) rc = KVQ_ERR_INVALID_ARG;
+        else if (seq[t] + 1 > rows) rows = seq[t] + 1;
+    }
+    if (rc == KVQ_OK) {
+        const size_t n = (size_t)rows * max_pages_per_seq;
+        pt = (int32_t *)malloc(sizeof(int32_t) * n);
+        if (!pt) rc = KVQ_ERR_INVALID_ARG;
+        else if (hipMemcpyAsync(pt, page_table, sizeof(int32_t) * n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+                 hipStreamSynchronize(stream) != hipSuccess)
+            rc = KVQ_ERR_HIP;
+    }
+    for (int32_t t = 0; rc == KVQ_OK && t < num_tokens; ++t) {
+        const int32_t page = pt[(size_t)seq[t] * max_pages_per_seq + pos[t] / page_size];
         if (page < 0 || page >= num_pages) rc = KVQ_ERR_INVALID_ARG;
     }
     free(seq);
     free(pos);
+    free(pt);
     return rc;
 }
 
@@ -211,7 +221,8 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
                   const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
                   int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale, float *out,
-                  void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *stream) {
+                  void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *phase_event,
+                  void *stream) {
     int rc = validate_decode(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                              max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, out);
     if (rc != KVQ_OK) return rc;
@@ -252,6 +263,7 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     }
     a.tile_bytes = int4 ? (int64_t)kvq_page_tile_bytes(head_dim, page_size) : (int64_t)page_size * head_dim * 2;
     a.max_pages_per_seq = max_pages_per_seq;
+    a.max_context_len = max_context_len;
     a.batch = batch;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
@@ -265,7 +277,7 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.score_scale = softmax_scale * 1.4426950408889634f;
     hipError_t e = int4 ? kvq::launch_decode_int4_mfma(a, st) : kvq::launch_decode_fp16(a, st);
     if (e != hipSuccess) return KVQ_ERR_HIP;
-    if (g_phase_event && hipEventRecord(static_cast<hipEvent_t>(g_phase_event), st) != hipSuccess)
+    if (phase_event && hipEventRecord(static_cast<hipEvent_t>(phase_event), st) != hipSuccess)
         return KVQ_ERR_HIP;
     e = kvq::launch_combine(a, int4 && had_block > 0, st);
     return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
@@ -389,6 +401,7 @@ int paged_prefill_attn_int4(const uint16_t *q, const int32_t *q_start, int32_t n
     if (!q || !q_start || !k_pool || !v_pool || !page_table || !context_lens || !out) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
     if ((int64_t)num_q / 16 + batch > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)max_pages_per_seq * page_size > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
     const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
     if ((int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
     kvq::PrefillArgs a{};
@@ -418,25 +431,21 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
                            int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale,
                            float *out, void *workspace, size_t workspace_bytes, int32_t pages_per_split,
-                           void *stream) {
+                           void *phase_event, void *stream) {
     return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                          max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
-                         softmax_scale, out, workspace, workspace_bytes, pages_per_split, stream);
+                         softmax_scale, out, workspace, workspace_bytes, pages_per_split, phase_event, stream);
 }
 
 int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, int64_t num_pages,
                            const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
                            int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t page_size, float softmax_scale, float *out,
-                           void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *stream) {
+                           void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                           void *phase_event, void *stream) {
     return decode_common(false, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                          max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, 0, softmax_scale, out,
-                         workspace, workspace_bytes, pages_per_split, stream);
-}
-
-int kvq_set_decode_phase_event(void *event) {
-    g_phase_event = event;
-    return KVQ_OK;
+                         workspace, workspace_bytes, pages_per_split, phase_event, stream);
 }
 
 }  // extern "C"

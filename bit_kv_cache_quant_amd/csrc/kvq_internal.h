@@ -43,6 +43,7 @@ struct DecodeArgs {
     float *ws_ml;              // [batch][num_q_heads][num_splits][2]  (max in log2 units, sum)
     int64_t tile_bytes;
     int32_t max_pages_per_seq;
+    int32_t max_context_len;   // every context length read is clamped to this
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -102,6 +103,17 @@ struct PrefillArgs {
     int32_t had_block;
     float score_scale;         // softmax_scale * log2(e)
 };
+
+// Context length of sequence b as the kernels use it: context_lens[b]
+// clamped to the largest length the caller sized the page table and the
+// workspace for, so a length past that contract can give a wrong row but
+// never an access outside the buffers.
+__device__ __forceinline__ int32_t decode_len(const DecodeArgs &a, int b) {
+    return min(a.context_lens[b], a.max_context_len);
+}
+__device__ __forceinline__ int32_t prefill_len(const PrefillArgs &a, int b) {
+    return min(a.context_lens[b], a.max_pages_per_seq * a.page_size);
+}
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_prefill_int4(const PrefillArgs &a, hipStream_t stream);

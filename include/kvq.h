@@ -32,8 +32,7 @@
  * Conventions for every entry point
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
  *     The caller allocates and frees every buffer; the library allocates
- *     nothing and keeps no state between calls apart from the optional
- *     timing hook kvq_set_decode_phase_event.  All entry points are
+ *     nothing and keeps no state between calls.  All entry points are
  *     re-entrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it and return; they never synchronize.
@@ -175,6 +174,12 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   pages_per_split  0 = library's choice, else about this many pages per
  *                  range (whole 64-token chunks; per-sequence ranges are
  *                  capped at 2048 tokens, batch-wide ranges at 64 chunks)
+ *   phase_event    NULL, or a hipEvent_t (as void*) that this call records on
+ *                  `stream` after the split-K partial kernel and before the
+ *                  merge kernel, so that a caller can time the two kernels
+ *                  apart with events recorded before and after the call
+ * A context length above max_context_len is read as max_context_len (the
+ * row is then wrong, but no buffer is accessed out of bounds).
  * batch == 0 is a no-op returning KVQ_OK.
  */
 int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
@@ -184,7 +189,7 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                            int32_t had_block, float softmax_scale, float *out,
                            void *workspace, size_t workspace_bytes,
-                           int32_t pages_per_split, void *stream);
+                           int32_t pages_per_split, void *phase_event, void *stream);
 
 /*
  * paged_prefill_attn_int4 — causal attention of a prompt's queries over the
@@ -239,18 +244,8 @@ int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint
                            int32_t batch, int32_t max_context_len, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                            float softmax_scale, float *out, void *workspace,
-                           size_t workspace_bytes, int32_t pages_per_split, void *stream);
-
-/*
- * kvq_set_decode_phase_event — timing hook for benchmarks and profilers.
- * When `event` (a hipEvent_t passed as void*) is non-NULL, every later call of
- * a decode entry point records it on its stream right after the split-K
- * partial kernel and before the combine kernel, so that the caller can time
- * the two kernels separately with events recorded before and after the call.
- * NULL switches the hook off.  This is the library's only process-wide
- * setting; set it while no decode call is in flight.  Returns KVQ_OK.
- */
-int kvq_set_decode_phase_event(void *event);
+                           size_t workspace_bytes, int32_t pages_per_split,
+                           void *phase_event, void *stream);
 
 #ifdef __cplusplus
 }

@@ -124,12 +124,12 @@ def test_append_host_validation_rejects_before_launch():
 
 def _decode(**kw):
     a = dict(q=FAKE, kp=FAKE, vp=FAKE, npages=8, pt=FAKE, maxp=4, cl=FAKE, B=2, maxctx=64, hq=32, hkv=8,
-             d=128, P=16, bh=64, scale=0.088, out=FAKE, ws=FAKE, wsb=1 << 20, pps=0, stream=None)
+             d=128, P=16, bh=64, scale=0.088, out=FAKE, ws=FAKE, wsb=1 << 20, pps=0, ev=None, stream=None)
     a.update(kw)
     return kvq.lib().paged_decode_attn_int4(a["q"], a["kp"], a["vp"], a["npages"], a["pt"], a["maxp"],
                                             a["cl"], a["B"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["P"],
                                             a["bh"], a["scale"], a["out"], a["ws"], a["wsb"], a["pps"],
-                                            a["stream"])
+                                            a["ev"], a["stream"])
 
 
 def test_decode_host_validation_rejects_before_launch():
@@ -170,6 +170,20 @@ def test_binding_rejects_mis_shaped_pools_before_launch():
     with pytest.raises(ValueError, match="pools must"):
         kvq.paged_decode_attn_int4(q, short_tile, short_tile, pt, torch.zeros(1, dtype=torch.int32), 8, 16, 64,
                                    0.088, 64)
+
+
+def test_binding_rejects_a_host_workspace_before_launch():
+    """The workspace is checked like every other tensor: a CPU tensor (or a
+    non-contiguous view) never reaches the kernels as a device pointer."""
+    import torch
+    pool = torch.zeros((4, 8, 1056), dtype=torch.uint8)
+    q = torch.zeros((1, 32, 128), dtype=torch.float16)
+    pt = torch.zeros((1, 4), dtype=torch.int32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    # the workspace is checked before the other tensors are marshalled
+    with pytest.raises(ValueError, match="workspace must be a GPU tensor"):
+        kvq.paged_decode_attn_int4(q, pool, pool, pt, torch.zeros(1, dtype=torch.int32), 8, 16, 64, 0.088, 64,
+                                   workspace=ws)
 
 
 def _prefill(**kw):

@@ -178,3 +178,48 @@ def test_decode_rotation_off_matches_naive_oracle(dev):
     w = wl.small(len(lens), lens, 0, 32, cfg_id=97)
     got, want, _ = _int4_case(w, dev, had_block=0)
     _assert_close(got, want)
+
+
+@pytest.mark.parametrize("had_block", [0, 128])
+@pytest.mark.parametrize("pages_per_split", [0, 2])
+def test_decode_ranges_cross_sequences_page32(dev, had_block, pages_per_split):
+    """The batch-wide ranges with 32-token pages: a 64-token chunk is two
+    pages, so a range boundary falls on every other page; ragged lengths
+    (empty, one token, half pages, whole chunks) over 21 sequences."""
+    r = np.random.default_rng(77)
+    lens = [int(x) for x in r.integers(0, 400, size=21)]
+    lens[2] = 0
+    lens[7] = 1
+    lens[9] = 32
+    lens[10] = 64
+    lens[11] = 33
+    w = wl.small(len(lens), lens, had_block, 32, cfg_id=160 + had_block + pages_per_split)
+    got, want, _ = _int4_case(w, dev, pages_per_split=pages_per_split)
+    _assert_close(got, want)
+    assert np.all(got[2] == 0)
+
+
+@pytest.mark.parametrize("lens", [[100, 300, 50], [int(x) for x in np.random.default_rng(5).integers(0, 300, 20)]])
+def test_decode_context_len_above_max_is_clamped(dev, lens):
+    """A context length above max_context_len (outside the contract) is read
+    as max_context_len: the row is that of the shorter context, and nothing
+    outside the buffers is touched.  Here every buffer is sized for the real
+    lengths, so the call stays in bounds either way; the rows must equal the
+    oracle's at the clamped lengths (split schedule for 3 sequences, the
+    batch-wide one for 20)."""
+    lens = list(lens)
+    lens[1] = 300
+    w = wl.small(len(lens), lens, 64, 16, cfg_id=170 + len(lens))
+    kp, vp = int4_pools(w, dev)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    prefill(w, 0, dev, kp, vp, w.had_block, host_pools=(hk, hv))
+    q = w.query(0, dev)
+    maxctx = 200
+    out = kvq.paged_decode_attn_int4(q, kp, vp, torch.as_tensor(w.table(0), device=dev),
+                                     torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, w.page_size,
+                                     w.had_block, w.softmax_scale, maxctx)
+    torch.cuda.synchronize()
+    clamped = np.minimum(w.context_lens, maxctx).astype(np.int32)
+    want = oracle.paged_decode_attn_int4(q.cpu().numpy(), hk, hv, w.table(0), clamped, w.num_kv_heads,
+                                         w.page_size, w.had_block, w.softmax_scale)
+    _assert_close(out.cpu().numpy(), want)
