@@ -21,6 +21,8 @@ KVQ_ERR_INVALID_ARG = -1
 KVQ_ERR_UNSUPPORTED = -2
 KVQ_ERR_WORKSPACE = -3
 KVQ_ERR_HIP = -4
+KVQ_ERR_TOO_LARGE = -5
+SCRATCH_BYTES = 32 << 20     # KVQ_SCRATCH_BYTES: the allocation-free decode's static scratch
 
 HEAD_DIM = 128
 
@@ -36,6 +38,8 @@ SIGNATURES = {
     "paged_prefill_attn_int4": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                _I32, _I32, _F32, _P, _P]),
     "kv_append_fp16": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "paged_decode_attn_int4_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
+                                                      _I32, _I32, _I32, _F32, _P, _I32, _P, _P]),
     "paged_decode_attn_fp16": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _F32, _P, _P, _SZ, _I32, _P, _P]),
 }
@@ -244,3 +248,29 @@ def paged_decode_attn_fp16(q, k_pool, v_pool, page_table, context_lens, num_kv_h
     """Baseline decode over fp16 pools; returns fp32 [B][Hq][D]."""
     return _decode(False, q, k_pool, v_pool, page_table, context_lens, num_kv_heads, page_size,
                    0, softmax_scale, max_context_len, out, workspace, pages_per_split, phase_event)
+
+
+def paged_decode_attn_int4_noalloc(q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
+                                   page_size: int, had_block: int, softmax_scale: float,
+                                   max_context_len: int, out, pages_per_split: int = 0, phase_event=None):
+    """paged_decode_attn_int4 without a workspace: the library's static
+    per-GPU scratch holds the partial states, and nothing is allocated (the
+    caller passes ``out``, fp32 [B][Hq][D]).  Calls that overlap on one GPU
+    race on that scratch."""
+    import torch
+    B, hq, d = q.shape
+    want = (int(num_kv_heads), page_tile_bytes(d, int(page_size)))
+    if tuple(k_pool.shape[1:]) != want or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError(f"pools must both be [num_pages]{list(want)}, got {tuple(k_pool.shape)} "
+                         f"and {tuple(v_pool.shape)}")
+    if context_lens.numel() != B or page_table.dim() != 2 or page_table.shape[0] < B:
+        raise ValueError("context_lens must have one entry per sequence and page_table one row each")
+    if out is None or tuple(out.shape) != (B, hq, d):
+        raise ValueError(f"out must be given, [{B}][{hq}][{d}]")
+    _check(lib().paged_decode_attn_int4_noalloc(
+        _dev(q, torch.float16, "q", 3), _dev(k_pool, torch.uint8, "k_pool"), _dev(v_pool, torch.uint8, "v_pool"),
+        k_pool.shape[0], _dev(page_table, torch.int32, "page_table", 2), page_table.shape[1],
+        _dev(context_lens, torch.int32, "context_lens", 1), B, int(max_context_len), hq, int(num_kv_heads), d,
+        int(page_size), int(had_block), float(softmax_scale), _dev(out, torch.float32, "out", 3),
+        int(pages_per_split), _event_handle(phase_event), _stream(q)), "paged_decode_attn_int4_noalloc")
+    return out

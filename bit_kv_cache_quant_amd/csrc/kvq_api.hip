@@ -2,15 +2,38 @@
 // kernel launches.  The contract of every entry point is documented in
 // include/kvq.h.
 #include <cmath>
+#include <mutex>
 #include <stdlib.h>
 #include <string.h>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 
+// Static split-K scratch of paged_decode_attn_int4_noalloc (one copy per
+// GPU, held until the process ends).  Host code never uses this name as an
+// address: kernels get the device address from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[KVQ_SCRATCH_BYTES];
+
 namespace {
 
 using kvq::kHeadDim;
+
+// Device address of the current GPU's scratch, looked up once per GPU (with
+// that GPU current) and kept; nullptr if the runtime lookup fails.
+constexpr int kMaxDevices = 64;
+void *scratch_of_current_device() {
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
 
 bool valid_page_size(int32_t p) { return p == 16 || p == 32; }
 bool valid_had_block(int32_t bh) { return bh == 0 || bh == 32 || bh == 64 || bh == 128; }
@@ -222,7 +245,7 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
                   int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale, float *out,
                   void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *phase_event,
-                  void *stream) {
+                  void *stream, bool use_scratch = false) {
     int rc = validate_decode(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                              max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, out);
     if (rc != KVQ_OK) return rc;
@@ -236,6 +259,14 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     BalancedPlan bp;
     const bool balanced = balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &bp);
     const size_t need = balanced ? balanced_workspace_bytes(bp, batch) : workspace_bytes_for(batch, num_q_heads, nsplit);
+    if (use_scratch) {
+        // the static scratch stands in for the workspace; sizes are checked
+        // before anything touches the device
+        if (need > KVQ_SCRATCH_BYTES) return KVQ_ERR_TOO_LARGE;
+        workspace = scratch_of_current_device();
+        if (!workspace) return KVQ_ERR_HIP;
+        workspace_bytes = KVQ_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (debug_checks_enabled()) {
@@ -294,6 +325,7 @@ const char *kvq_status_string(int status) {
         case KVQ_ERR_UNSUPPORTED: return "unsupported head_dim, page_size, had_block or size";
         case KVQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case KVQ_ERR_HIP: return "HIP runtime error";
+        case KVQ_ERR_TOO_LARGE: return "request needs more than the library's static scratch";
         default: return "unknown status";
     }
 }
@@ -435,6 +467,16 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
     return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                          max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
                          softmax_scale, out, workspace, workspace_bytes, pages_per_split, phase_event, stream);
+}
+
+int paged_decode_attn_int4_noalloc(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,
+                                   const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                                   int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale,
+                                   float *out, int32_t pages_per_split, void *phase_event, void *stream) {
+    return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
+                         max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
+                         softmax_scale, out, nullptr, 0, pages_per_split, phase_event, stream, true);
 }
 
 int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool, int64_t num_pages,

@@ -86,7 +86,8 @@ enum {
     KVQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad combination */
     KVQ_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / had_block outside the supported set */
     KVQ_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
-    KVQ_ERR_HIP = -4            /* the HIP runtime reported an error */
+    KVQ_ERR_HIP = -4,           /* the HIP runtime reported an error */
+    KVQ_ERR_TOO_LARGE = -5      /* the call needs more than the static scratch holds */
 };
 
 /* Static, human-readable text for a status code (host function). */
@@ -238,6 +239,35 @@ int kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
  * no rotation.  Same arguments, split and workspace as paged_decode_attn_int4
  * without had_block.
  */
+/*
+ * paged_decode_attn_int4_noalloc — paged_decode_attn_int4 for callers that
+ * cannot allocate device memory (code under HIP-graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ * result, with the split-K partial states in a static device buffer of
+ * KVQ_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends, instead of a caller's workspace.
+ *   - Allocates nothing: no hipMalloc, no hipFree, no allocating library call.
+ *   - A call whose partial states need more than KVQ_SCRATCH_BYTES (what
+ *     paged_decode_attn_workspace_bytes reports for the schedule the call
+ *     takes) returns KVQ_ERR_TOO_LARGE before anything is launched.
+ *   - The buffer of a GPU is found on the first call made with that GPU
+ *     current (a runtime lookup, no allocation); `stream` must belong to the
+ *     current GPU.
+ *   - Every call on one GPU uses the same buffer, which keeps the last call's
+ *     contents (nothing in it needs to start at zero): calls on one stream
+ *     are ordered, but calls that overlap on one GPU (different streams, or
+ *     other threads) race and give wrong results.
+ * Other arguments, contract and errors as paged_decode_attn_int4.
+ */
+#define KVQ_SCRATCH_BYTES ((size_t)32 << 20)
+int paged_decode_attn_int4_noalloc(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                                   int64_t num_pages, const int32_t *page_table,
+                                   int32_t max_pages_per_seq, const int32_t *context_lens,
+                                   int32_t batch, int32_t max_context_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                   int32_t had_block, float softmax_scale, float *out,
+                                   int32_t pages_per_split, void *phase_event, void *stream);
+
 int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                            int64_t num_pages, const int32_t *page_table,
                            int32_t max_pages_per_seq, const int32_t *context_lens,

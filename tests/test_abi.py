@@ -210,3 +210,22 @@ def test_prefill_host_validation():
     assert _prefill(scale=float("nan")) == kvq.KVQ_ERR_INVALID_ARG
     assert _prefill(nq=0) == kvq.KVQ_OK                           # no-op
     assert _prefill(B=0) == kvq.KVQ_OK
+
+
+def test_noalloc_decode_rejects_requests_beyond_the_scratch_on_the_host():
+    """The allocation-free decode refuses, before touching the device, a call
+    whose partial states need more than its static scratch (here batch 4096 x
+    8192 context: 260 MiB against 32 MiB); a call that fits is checked the
+    same way as the workspace entry point."""
+    lib = kvq.lib()
+    need = kvq.workspace_bytes(4096, 32, 8, 8192, 16)
+    assert need > kvq.SCRATCH_BYTES
+    rc = lib.paged_decode_attn_int4_noalloc(FAKE, FAKE, FAKE, 1 << 20, FAKE, 512, FAKE, 4096, 8192, 32, 8, 128,
+                                            16, 64, 0.088, FAKE, 0, None, None)
+    assert rc == kvq.KVQ_ERR_TOO_LARGE
+    assert "scratch" in kvq.status_string(kvq.KVQ_ERR_TOO_LARGE)
+    # argument errors come first, as in the workspace entry point
+    assert lib.paged_decode_attn_int4_noalloc(FAKE, FAKE, FAKE, 8, FAKE, 4, FAKE, 2, 64, 32, 8, 256, 16, 64, 0.088,
+                                              FAKE, 0, None, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.paged_decode_attn_int4_noalloc(None, FAKE, FAKE, 8, FAKE, 4, FAKE, 0, 64, 32, 8, 128, 16, 64, 0.088,
+                                              None, 0, None, None) == kvq.KVQ_OK
