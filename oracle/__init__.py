@@ -67,6 +67,18 @@ def lib() -> ctypes.CDLL:
         L.kvq_oracle_paged_decode_attn_fp16.restype = ctypes.c_int
         L.kvq_oracle_dense_decode_f64.argtypes = [P, P, P, i32, i32, i32, i32, f64, P]
         L.kvq_oracle_dense_decode_f64.restype = ctypes.c_int
+        L.kvq_oracle_tile_bytes_cfg.argtypes = [ctypes.c_int, ctypes.c_int, P]
+        L.kvq_oracle_tile_bytes_cfg.restype = i64
+        L.kvq_oracle_quantize_vector_cfg.argtypes = [P, ctypes.c_int, P, P, P]
+        L.kvq_oracle_quantize_vector_cfg.restype = ctypes.c_int
+        L.kvq_oracle_reconstruct_cfg.argtypes = [P, ctypes.c_int, P, P]
+        L.kvq_oracle_reconstruct_cfg.restype = ctypes.c_int
+        L.kvq_oracle_kv_quant_append_cfg.argtypes = [P, P, P, P, i32, P, i32, P, P, i64, i32, i32, i32, P]
+        L.kvq_oracle_kv_quant_append_cfg.restype = ctypes.c_int
+        L.kvq_oracle_paged_decode_attn_cfg.argtypes = [P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, P, f32, P]
+        L.kvq_oracle_paged_decode_attn_cfg.restype = ctypes.c_int
+        L.kvq_oracle_e2m1_value.argtypes = [ctypes.c_int]
+        L.kvq_oracle_e2m1_value.restype = f32
         L.kvq_oracle_num_threads.argtypes = []
         L.kvq_oracle_num_threads.restype = ctypes.c_int
         L.kvq_oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -244,4 +256,91 @@ def dequantize_pool(pool: np.ndarray, page_table, context_len: int, seq: int, he
         sb = pg[s0:s0 + 2]
         s = float(np.frombuffer(bytes(sb), dtype="<f2")[0])
         out[j] = codes * s
+    return out
+
+
+# --------------------------------------------------------------------------
+# Quantizer variants (per-group scales, scale search, randomized Hadamard,
+# MXFP4).  A configuration is (format, had_block, scale_group, scale_search,
+# sign_mask): format 0 = INT4 codes with fp16 scales, 1 = MXFP4 (E2M1 codes,
+# E8M0 scales, groups of 32); sign_mask is a 128-bit integer (bit i: channel
+# i negated before the rotation).
+FMT_INT4 = 0
+FMT_MXFP4 = 1
+
+
+class QCfg(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("had_block", ctypes.c_int32), ("scale_group", ctypes.c_int32),
+                ("scale_search", ctypes.c_int32), ("sign_mask", ctypes.c_uint32 * 4)]
+
+
+def qcfg(fmt: int = FMT_INT4, had_block: int = 0, scale_group: int = 128, scale_search: int = 0,
+         sign_mask: int = 0) -> QCfg:
+    c = QCfg()
+    c.format, c.had_block, c.scale_group, c.scale_search = int(fmt), int(had_block), int(scale_group), \
+        int(scale_search)
+    for w in range(4):
+        c.sign_mask[w] = (int(sign_mask) >> (32 * w)) & 0xFFFFFFFF
+    return c
+
+
+def scale_bytes_per_vector(cfg: QCfg, head_dim: int = 128) -> int:
+    return (head_dim // cfg.scale_group) * (1 if cfg.format == FMT_MXFP4 else 2)
+
+
+def tile_bytes_cfg(head_dim: int, page_size: int, cfg: QCfg) -> int:
+    n = int(lib().kvq_oracle_tile_bytes_cfg(head_dim, page_size, ctypes.byref(cfg)))
+    if n < 0:
+        raise RuntimeError("oracle tile_bytes_cfg rejected its arguments")
+    return n
+
+
+def quantize_vector_cfg(x_f16, cfg: QCfg):
+    """One vector of fp16 values -> (packed uint8 codes [D/2], scale bytes)."""
+    x = _as(x_f16, np.float16).view(np.uint16)
+    d = x.size
+    codes = np.zeros(d // 2, np.uint8)
+    scales = np.zeros(scale_bytes_per_vector(cfg, d), np.uint8)
+    _check(lib().kvq_oracle_quantize_vector_cfg(_ptr(x), d, ctypes.byref(cfg), _ptr(codes), _ptr(scales)),
+           "quantize_vector_cfg")
+    return codes, scales
+
+
+def reconstruct_cfg(x_f16, cfg: QCfg) -> np.ndarray:
+    """Quantize one fp16 vector and bring it back to the original basis (fp64)."""
+    x = _as(x_f16, np.float16).view(np.uint16)
+    out = np.zeros(x.size, np.float64)
+    _check(lib().kvq_oracle_reconstruct_cfg(_ptr(x), x.size, ctypes.byref(cfg), _ptr(out)), "reconstruct_cfg")
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return float(lib().kvq_oracle_e2m1_value(int(code)))
+
+
+def kv_quant_append_cfg(k_new, v_new, token_seq, token_pos, page_table, k_pool, v_pool, cfg: QCfg,
+                        page_size: int) -> None:
+    k = _as(k_new, np.float16).view(np.uint16)
+    v = _as(v_new, np.float16).view(np.uint16)
+    T, hkv, d = k.shape
+    ts, tp = _as(token_seq, np.int32), _as(token_pos, np.int32)
+    pt = _as(page_table, np.int32)
+    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+    _check(lib().kvq_oracle_kv_quant_append_cfg(_ptr(k), _ptr(v), _ptr(ts), _ptr(tp), T, _ptr(pt), pt.shape[1],
+                                                _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], hkv, d,
+                                                int(page_size), ctypes.byref(cfg)),
+           "kv_quant_append_cfg")
+
+
+def paged_decode_attn_cfg(q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int, page_size: int,
+                          cfg: QCfg, softmax_scale: float) -> np.ndarray:
+    qq = _as(q, np.float16).view(np.uint16)
+    B, hq, d = qq.shape
+    pt, cl = _as(page_table, np.int32), _as(context_lens, np.int32)
+    out = np.zeros((B, hq, d), np.float32)
+    _check(lib().kvq_oracle_paged_decode_attn_cfg(_ptr(qq), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                                  _ptr(pt), pt.shape[1], _ptr(cl), B, hq, int(num_kv_heads), d,
+                                                  int(page_size), ctypes.byref(cfg), float(softmax_scale),
+                                                  _ptr(out)),
+           "paged_decode_attn_cfg")
     return out

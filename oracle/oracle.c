@@ -25,6 +25,10 @@
  *   [SUMM]  "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World
  *           LLM Serving" (gist.science AI-generated summary), sections on the
  *           problem, the solution and the results.
+ *   [BDFP4] "BitDecoding-FP4:FP4 KVキャッシュのネイティブ復号" (sns.style),
+ *           opening summary and section 深掘り分析: the quantizer variants at
+ *           the end of this file (scales per group chosen by search, 4-bit
+ *           microscaling formats).
  * Where the pages leave a step open, the reading taken is stated at the step.
  * Every such reading is one the HIP path must reproduce exactly.
  */
@@ -496,6 +500,358 @@ int kvq_oracle_dense_decode_f64(const double *q, const double *k, const double *
         dense_ctx c = { k, v, num_kv_heads, qh / group, head_dim };
         attend_one(q + (int64_t)qh * head_dim, L, head_dim, softmax_scale, fetch_dense, &c,
                    out + (int64_t)qh * head_dim);
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantizer variants on the same paged cache and the same attention.       */
+/*                                                                           */
+/* Sources: "BitDecoding-FP4:FP4 KVキャッシュのネイティブ復号", section      */
+/* 深掘り分析 (Outlier-Aware Key Quantization: with one scale per token, a   */
+/* single outlier widens the range of the whole token; smoothing and a      */
+/* Hadamard rotation spread outliers, and a scale search picks a suitable    */
+/* scale per group) and its opening summary (4-bit microscaling KV formats,  */
+/* NVFP4 and MXFP4); "KVキャッシュを4ビットへ — SAW-INT4...", section         */
+/* 回転のトリック (block-diagonal Hadamard, in the QuaRot / SpinQuant line of */
+/* rotations, whose randomized form multiplies by a random +-1 diagonal      */
+/* first).                                                                   */
+/*                                                                           */
+/* Readings (the pages fix no arithmetic for these):                        */
+/*  - scale groups: contiguous groups of scale_group channels of the         */
+/*    (rotated) head vector, one scale each; scale_group = had_block gives   */
+/*    one scale per Hadamard block; 128 is the method's token-wise scale;    */
+/*  - scale search (INT4): candidate scales s_k = fp16(fp32(m a_k) / 7)      */
+/*    for the clipping ratios a_k = (16 - k) / 16, k = 0..7, m the group's  */
+/*    absmax; each candidate's codes are those of the plain quantizer with  */
+/*    s_k, its error is the sum over the group of D_i^2, where D_i is the    */
+/*    residual y_i - s_k c_i (exact in fp32 for these ratios) in units of   */
+/*    2^(E-12), E the exponent with m < 2^E, rounded to an integer (ties to  */
+/*    even): an exact integer, so the choice does not depend on the order of */
+/*    the sum; the smallest error wins, ties to the larger ratio;            */
+/*  - randomized Hadamard: x -> R (S x) with S = diag(+-1) given as a        */
+/*    128-bit mask (bit i set: channel i negated); keys and values are       */
+/*    written with R S, the query is rotated with R S as well, and the       */
+/*    output is brought back with S R (the inverse of R S);                  */
+/*  - MXFP4: groups of 32, OCP microscaling layout: E2M1 elements            */
+/*    {0, 0.5, 1, 1.5, 2, 3, 4, 6} with a sign bit, and one E8M0 shared      */
+/*    scale 2^X per group with X = floor(log2 m) - 2 (m = the group's        */
+/*    absmax; 2 is the exponent of E2M1's largest normal value); an element */
+/*    becomes the E2M1 value nearest y / 2^X (ties to the code whose         */
+/*    mantissa bit is 0; beyond 6 it saturates to 6); the sign bit is the    */
+/*    sign bit of y; a group of zeros gets X = -127 (byte 0) and zero codes. */
+/* Scales of a page follow its code rows: for (KV head h, slot, group g) at  */
+/* Hkv * P * D/2 + ((h * P + slot) * (D / G) + g) * scale_bytes, with       */
+/* scale_bytes 2 (fp16) for INT4 and 1 (E8M0) for MXFP4.                     */
+/* ------------------------------------------------------------------------ */
+
+#define ORACLE_FMT_INT4 0
+#define ORACLE_FMT_MXFP4 1
+
+typedef struct {
+    int32_t format;
+    int32_t had_block;
+    int32_t scale_group;
+    int32_t scale_search;
+    uint32_t sign_mask[4];
+} kvq_oracle_qcfg;
+
+static int cfg_ok(const kvq_oracle_qcfg *c, int d)
+{
+    if (!c || d <= 0 || d > ORACLE_MAX_D || (d & 1) || d > 128) return 0;
+    int bh = c->had_block;
+    if (bh < 0 || (bh > 0 && (bh > d || (bh & (bh - 1)) || d % bh))) return 0;
+    int g = c->scale_group;
+    if (g <= 0 || d % g) return 0;
+    if (c->format == ORACLE_FMT_INT4) return c->scale_search == 0 || c->scale_search == 1;
+    if (c->format == ORACLE_FMT_MXFP4) return g == 32 && c->scale_search == 0;
+    return 0;
+}
+
+static int scale_bytes_of(const kvq_oracle_qcfg *c) { return c->format == ORACLE_FMT_MXFP4 ? 1 : 2; }
+
+static int sign_of(const kvq_oracle_qcfg *c, int i) { return (c->sign_mask[i >> 5] >> (i & 31)) & 1u; }
+
+int64_t kvq_oracle_tile_bytes_cfg(int d, int p, const kvq_oracle_qcfg *c)
+{
+    if (!cfg_ok(c, d) || p <= 0) return -1;
+    return (int64_t)p * (d / 2) + (int64_t)p * (d / c->scale_group) * scale_bytes_of(c);
+}
+
+/* y = R (S x) in fp32: widen, negate the masked channels (exact), then the
+ * block FWHT and the 1/sqrt(Bh) factor exactly as the plain quantizer does. */
+static void rotate_fwd_cfg_f32(const uint16_t *x, int d, const kvq_oracle_qcfg *c, float *y)
+{
+    for (int i = 0; i < d; i++) {
+        y[i] = kvq_oracle_f16_to_f32(x[i]);
+        if (sign_of(c, i)) y[i] = -y[i];
+    }
+    if (c->had_block > 1) {
+        kvq_oracle_fwht_f32(y, d, c->had_block);
+        float cb = kvq_oracle_hadamard_scale(c->had_block);
+        for (int i = 0; i < d; i++) y[i] = y[i] * cb;
+    }
+}
+
+/* INT4 codes of one group for a given fp16 scale (as the plain quantizer). */
+static void int4_codes(const float *y, int n, float s, int *codes)
+{
+    for (int i = 0; i < n; i++) {
+        int code = 0;
+        if (s != 0.0f) {
+            code = (int)rintf(y[i] / s);
+            if (code < -8) code = -8;
+            if (code > 7) code = 7;
+        }
+        codes[i] = code;
+    }
+}
+
+/* One INT4 group: codes and the fp16 scale bits. */
+static void int4_group(const float *y, int n, int search, int *codes, uint16_t *s16_out)
+{
+    float m = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float a = fabsf(y[i]);
+        if (a > m) m = a;
+    }
+    if (!search) {
+        uint16_t s16 = kvq_oracle_f32_to_f16(m / 7.0f);
+        int4_codes(y, n, kvq_oracle_f16_to_f32(s16), codes);
+        *s16_out = s16;
+        return;
+    }
+    int E = 0;
+    if (m > 0.0f) (void)frexpf(m, &E);           /* m = f 2^E, f in [0.5, 1): m < 2^E */
+    int64_t best_err = -1;
+    int cand[ORACLE_MAX_D];
+    for (int k = 0; k < 8; k++) {
+        float a = (float)(16 - k) / 16.0f;
+        uint16_t s16 = kvq_oracle_f32_to_f16((m * a) / 7.0f);
+        float s = kvq_oracle_f16_to_f32(s16);
+        int4_codes(y, n, s, cand);
+        int64_t err = 0;
+        for (int i = 0; i < n; i++) {
+            float r = y[i] - s * (float)cand[i];
+            double D = rint(ldexp((double)r, 12 - E));
+            err += (int64_t)D * (int64_t)D;
+        }
+        if (best_err < 0 || err < best_err) {
+            best_err = err;
+            *s16_out = s16;
+            for (int i = 0; i < n; i++) codes[i] = cand[i];
+        }
+    }
+}
+
+/* E2M1 magnitudes by code 0..7, and the nearest code to a >= 0 (ties to the
+ * even code, whose mantissa bit is 0; saturates at 6). */
+static const float e2m1_grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static int e2m1_nearest(float a)
+{
+    int best = 0;
+    float bd = fabsf(a - e2m1_grid[0]);
+    for (int k = 1; k < 8; k++) {
+        float dk = fabsf(a - e2m1_grid[k]);
+        if (dk < bd || (dk == bd && (k & 1) == 0)) { best = k; bd = dk; }
+    }
+    return best;
+}
+
+float kvq_oracle_e2m1_value(int code)
+{
+    float v = e2m1_grid[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+/* One MXFP4 group: 4-bit codes (sign in bit 3) and the E8M0 byte. */
+static void mxfp4_group(const float *y, int n, int *codes, uint8_t *e8m0_out)
+{
+    float m = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float a = fabsf(y[i]);
+        if (a > m) m = a;
+    }
+    if (m == 0.0f) {
+        for (int i = 0; i < n; i++) codes[i] = signbit(y[i]) ? 8 : 0;
+        *e8m0_out = 0;
+        return;
+    }
+    int E = 0;
+    (void)frexpf(m, &E);          /* floor(log2 m) = E - 1 */
+    int X = E - 1 - 2;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    for (int i = 0; i < n; i++) {
+        float v = ldexpf(y[i], -X);
+        codes[i] = (signbit(y[i]) ? 8 : 0) | e2m1_nearest(fabsf(v));
+    }
+    *e8m0_out = (uint8_t)(X + 127);
+}
+
+/* One (token, KV head, K-or-V) vector under a variant: D/2 packed code bytes
+ * and D / scale_group scales (fp16 little-endian or E8M0 bytes). */
+int kvq_oracle_quantize_vector_cfg(const uint16_t *x, int d, const kvq_oracle_qcfg *c,
+                                   uint8_t *codes_out, uint8_t *scales_out)
+{
+    if (!cfg_ok(c, d)) return ORACLE_BAD;
+    float y[ORACLE_MAX_D];
+    int codes[ORACLE_MAX_D];
+    rotate_fwd_cfg_f32(x, d, c, y);
+    int G = c->scale_group;
+    for (int g = 0; g < d / G; g++) {
+        if (c->format == ORACLE_FMT_INT4) {
+            uint16_t s16 = 0;
+            int4_group(y + g * G, G, c->scale_search, codes + g * G, &s16);
+            scales_out[2 * g] = (uint8_t)(s16 & 0xFF);
+            scales_out[2 * g + 1] = (uint8_t)(s16 >> 8);
+        } else {
+            mxfp4_group(y + g * G, G, codes + g * G, scales_out + g);
+        }
+    }
+    for (int j = 0; j < d / 2; j++)
+        codes_out[j] = (uint8_t)((codes[2 * j] & 0xF) | ((codes[2 * j + 1] & 0xF) << 4));
+    return ORACLE_OK;
+}
+
+/* Element i of a stored vector (still in the rotated basis). */
+static double dequant_cfg(const uint8_t *codes, const uint8_t *scales, int d, const kvq_oracle_qcfg *c, int i)
+{
+    uint8_t byte = codes[i / 2];
+    int nib = (i & 1) ? (byte >> 4) : (byte & 0xF);
+    int g = i / c->scale_group;
+    if (c->format == ORACLE_FMT_INT4) {
+        int code = (nib & 8) ? nib - 16 : nib;
+        uint16_t s16 = (uint16_t)(scales[2 * g] | (scales[2 * g + 1] << 8));
+        return (double)code * (double)kvq_oracle_f16_to_f32(s16);
+    }
+    (void)d;
+    return (double)kvq_oracle_e2m1_value(nib) * ldexp(1.0, (int)scales[g] - 127);
+}
+
+/* Reconstruction of x in the original basis (S R applied to the dequantized
+ * vector, fp64): for accuracy reports. */
+int kvq_oracle_reconstruct_cfg(const uint16_t *x, int d, const kvq_oracle_qcfg *c, double *out)
+{
+    uint8_t codes[ORACLE_MAX_D / 2], scales[ORACLE_MAX_D * 2];
+    if (kvq_oracle_quantize_vector_cfg(x, d, c, codes, scales) != ORACLE_OK) return ORACLE_BAD;
+    for (int i = 0; i < d; i++) out[i] = dequant_cfg(codes, scales, d, c, i);
+    kvq_oracle_rotate_f64(out, d, c->had_block);
+    for (int i = 0; i < d; i++)
+        if (sign_of(c, i)) out[i] = -out[i];
+    return ORACLE_OK;
+}
+
+static int64_t scale_offset_cfg(int hkv, int d, int p, int h, int slot, const kvq_oracle_qcfg *c)
+{
+    int ng = d / c->scale_group;
+    return (int64_t)hkv * p * (d / 2) + ((int64_t)h * p + slot) * ng * scale_bytes_of(c);
+}
+
+int kvq_oracle_kv_quant_append_cfg(const uint16_t *k_new, const uint16_t *v_new,
+                                   const int32_t *token_seq, const int32_t *token_pos,
+                                   int32_t num_tokens, const int32_t *page_table,
+                                   int32_t max_pages_per_seq, uint8_t *k_pool,
+                                   uint8_t *v_pool, int64_t num_pages,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t page_size, const kvq_oracle_qcfg *c)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || page_size <= 0 || !cfg_ok(c, head_dim)) return ORACLE_BAD;
+    int64_t tb = kvq_oracle_tile_bytes_cfg(head_dim, page_size, c);
+    int sbytes = scale_bytes_of(c) * (head_dim / c->scale_group);
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int32_t t = 0; t < num_tokens; t++) {
+        int slot = 0;
+        int64_t page = locate(page_table, max_pages_per_seq, num_pages,
+                              token_seq[t], token_pos[t], page_size, &slot);
+        if (page < 0) { bad = 1; continue; }
+        for (int h = 0; h < num_kv_heads; h++) {
+            for (int which = 0; which < 2; which++) {
+                const uint16_t *src = (which == 0 ? k_new : v_new) +
+                                      ((int64_t)t * num_kv_heads + h) * head_dim;
+                uint8_t *pg = (which == 0 ? k_pool : v_pool) + page * num_kv_heads * tb;
+                uint8_t sc[ORACLE_MAX_D * 2];
+                if (kvq_oracle_quantize_vector_cfg(src, head_dim, c,
+                                                   pg + code_offset(head_dim, page_size, h, slot),
+                                                   sc) != ORACLE_OK) {
+                    bad = 1;
+                    continue;
+                }
+                memcpy(pg + scale_offset_cfg(num_kv_heads, head_dim, page_size, h, slot, c), sc,
+                       (size_t)sbytes);
+            }
+        }
+    }
+    return bad ? ORACLE_BAD : ORACLE_OK;
+}
+
+typedef struct {
+    const uint8_t *k_pool, *v_pool;
+    const int32_t *page_table;
+    int max_pages;
+    int64_t num_pages;
+    int seq, kvh, hkv, d, p;
+    const kvq_oracle_qcfg *c;
+} paged_cfg_ctx;
+
+static void fetch_paged_cfg(const void *vctx, int j, int which, double *out)
+{
+    const paged_cfg_ctx *x = (const paged_cfg_ctx *)vctx;
+    int slot = 0;
+    int64_t page = locate(x->page_table, x->max_pages, x->num_pages, x->seq, j, x->p, &slot);
+    const uint8_t *pool = which == 0 ? x->k_pool : x->v_pool;
+    const uint8_t *pg = pool + page * x->hkv * kvq_oracle_tile_bytes_cfg(x->d, x->p, x->c);
+    const uint8_t *codes = pg + code_offset(x->d, x->p, x->kvh, slot);
+    const uint8_t *scales = pg + scale_offset_cfg(x->hkv, x->d, x->p, x->kvh, slot, x->c);
+    for (int i = 0; i < x->d; i++) out[i] = dequant_cfg(codes, scales, x->d, x->c, i);
+}
+
+/* Decode attention over a variant's cache, fp64: q' = R (S q); softmax over
+ * the dequantized (rotated) keys; o = S R (sum w v').  L <= 0: zero row. */
+int kvq_oracle_paged_decode_attn_cfg(const uint16_t *q, const uint8_t *k_pool,
+                                     const uint8_t *v_pool, int64_t num_pages,
+                                     const int32_t *page_table, int32_t max_pages_per_seq,
+                                     const int32_t *context_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size,
+                                     const kvq_oracle_qcfg *c, float softmax_scale, float *out)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || page_size <= 0 ||
+        num_q_heads % num_kv_heads || !cfg_ok(c, head_dim))
+        return ORACLE_BAD;
+    for (int b = 0; b < batch; b++) {
+        int L = context_lens[b];
+        if (L > (int64_t)max_pages_per_seq * page_size) return ORACLE_BAD;
+        for (int lp = 0; lp < (L + page_size - 1) / page_size; lp++) {
+            int32_t pg = page_table[(int64_t)b * max_pages_per_seq + lp];
+            if (pg < 0 || pg >= num_pages) return ORACLE_BAD;
+        }
+    }
+    int group = num_q_heads / num_kv_heads;
+    int64_t units = (int64_t)batch * num_q_heads;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t u = 0; u < units; u++) {
+        int b = (int)(u / num_q_heads), qh = (int)(u % num_q_heads);
+        double qrot[ORACLE_MAX_D], o[ORACLE_MAX_D];
+        const uint16_t *qrow = q + ((int64_t)b * num_q_heads + qh) * head_dim;
+        for (int i = 0; i < head_dim; i++) {
+            qrot[i] = (double)kvq_oracle_f16_to_f32(qrow[i]);
+            if (sign_of(c, i)) qrot[i] = -qrot[i];
+        }
+        kvq_oracle_rotate_f64(qrot, head_dim, c->had_block);
+        paged_cfg_ctx x = { k_pool, v_pool, page_table, max_pages_per_seq, num_pages, b, qh / group,
+                            num_kv_heads, head_dim, page_size, c };
+        int L = context_lens[b];
+        attend_one(qrot, L, head_dim, (double)softmax_scale, fetch_paged_cfg, &x, o);
+        if (L > 0) {
+            kvq_oracle_rotate_f64(o, head_dim, c->had_block);
+            for (int i = 0; i < head_dim; i++)
+                if (sign_of(c, i)) o[i] = -o[i];
+        }
+        float *orow = out + ((int64_t)b * num_q_heads + qh) * head_dim;
+        for (int i = 0; i < head_dim; i++) orow[i] = (float)o[i];
     }
     return ORACLE_OK;
 }
