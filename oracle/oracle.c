@@ -538,8 +538,10 @@ int kvq_oracle_dense_decode_f64(const double *q, const double *k, const double *
 /*    scale 2^X per group with X = floor(log2 m) - 2 (m = the group's        */
 /*    absmax; 2 is the exponent of E2M1's largest normal value); an element */
 /*    becomes the E2M1 value nearest y / 2^X (ties to the code whose         */
-/*    mantissa bit is 0; beyond 6 it saturates to 6); the sign bit is the    */
-/*    sign bit of y; a group of zeros gets X = -127 (byte 0) and zero codes. */
+/*    mantissa bit is 0; beyond 6 it saturates to 6); the sign bit is set   */
+/*    iff y < 0, so a zero (of either sign) is stored as +0 and the stored   */
+/*    byte does not depend on how a zero was reached; a group of zeros gets  */
+/*    X = -127 (byte 0) and zero codes.                                      */
 /* Scales of a page follow its code rows: for (KV head h, slot, group g) at  */
 /* Hkv * P * D/2 + ((h * P + slot) * (D / G) + g) * scale_bytes, with       */
 /* scale_bytes 2 (fp16) for INT4 and 1 (E8M0) for MXFP4.                     */
@@ -674,7 +676,7 @@ static void mxfp4_group(const float *y, int n, int *codes, uint8_t *e8m0_out)
         if (a > m) m = a;
     }
     if (m == 0.0f) {
-        for (int i = 0; i < n; i++) codes[i] = signbit(y[i]) ? 8 : 0;
+        for (int i = 0; i < n; i++) codes[i] = 0;
         *e8m0_out = 0;
         return;
     }
@@ -685,7 +687,7 @@ static void mxfp4_group(const float *y, int n, int *codes, uint8_t *e8m0_out)
     if (X > 127) X = 127;
     for (int i = 0; i < n; i++) {
         float v = ldexpf(y[i], -X);
-        codes[i] = (signbit(y[i]) ? 8 : 0) | e2m1_nearest(fabsf(v));
+        codes[i] = (y[i] < 0.0f ? 8 : 0) | e2m1_nearest(fabsf(v));
     }
     *e8m0_out = (uint8_t)(X + 127);
 }
