@@ -26,8 +26,31 @@ SCRATCH_BYTES = 32 << 20     # KVQ_SCRATCH_BYTES: the allocation-free decode's s
 
 HEAD_DIM = 128
 
+FORMAT_INT4 = 0
+FORMAT_MXFP4 = 1
+
+
+class QuantConfig(ctypes.Structure):
+    """kvq_quant_config: quantizer variant (format, had_block, scale_group,
+    scale_search, sign_mask as four 32-bit words; see include/kvq.h)."""
+    _fields_ = [("format", ctypes.c_int32), ("had_block", ctypes.c_int32), ("scale_group", ctypes.c_int32),
+                ("scale_search", ctypes.c_int32), ("sign_mask", ctypes.c_uint32 * 4)]
+
+
+def quant_config(format: int = FORMAT_INT4, had_block: int = 0, scale_group: int = 128, scale_search: int = 0,
+                 sign_mask: int = 0) -> QuantConfig:
+    """A configuration; sign_mask is a 128-bit integer (bit i negates channel i)."""
+    c = QuantConfig()
+    c.format, c.had_block, c.scale_group, c.scale_search = int(format), int(had_block), int(scale_group), \
+        int(scale_search)
+    for w in range(4):
+        c.sign_mask[w] = (int(sign_mask) >> (32 * w)) & 0xFFFFFFFF
+    return c
+
+
 # Every symbol include/kvq.h declares, with its ctypes signature.
 _P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_CFG = ctypes.POINTER(QuantConfig)
 SIGNATURES = {
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_page_tile_bytes": (_SZ, [_I32, _I32]),
@@ -37,6 +60,9 @@ SIGNATURES = {
                                               _I32, _I32, _F32, _P, _P, _SZ, _I32, _P, _P]),
     "paged_prefill_attn_int4": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                _I32, _I32, _F32, _P, _P]),
+    "kvq_page_tile_bytes_cfg": (_SZ, [_I32, _I32, _CFG]),
+    "kv_quant_append_cfg": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _CFG,
+                                           _P]),
     "kv_append_fp16": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "paged_decode_attn_int4_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                       _I32, _I32, _I32, _F32, _P, _I32, _P, _P]),
@@ -134,6 +160,36 @@ def kv_quant_append(k_new, v_new, token_seq, token_pos, page_table, k_pool, v_po
         _dev(k_pool, torch.uint8, "k_pool"), _dev(v_pool, torch.uint8, "v_pool"), k_pool.shape[0],
         hkv, d, int(page_size), int(had_block), _stream(k_new))
     _check(rc, "kv_quant_append")
+
+
+def page_tile_bytes_cfg(head_dim: int, page_size: int, cfg: QuantConfig) -> int:
+    return int(lib().kvq_page_tile_bytes_cfg(head_dim, page_size, ctypes.byref(cfg)))
+
+
+def kv_quant_append_cfg(k_new, v_new, token_seq, token_pos, page_table, k_pool, v_pool,
+                        page_size: int, cfg: QuantConfig) -> None:
+    """kv_quant_append under a quantizer configuration; pools uint8
+    [num_pages][Hkv][page_tile_bytes_cfg(...)]."""
+    import torch
+    T, hkv, d = k_new.shape
+    if tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError("k_new and v_new shapes differ")
+    tile = page_tile_bytes_cfg(d, int(page_size), cfg)
+    if tile == 0:
+        raise KVQError(KVQ_ERR_UNSUPPORTED, "kv_quant_append_cfg")
+    if (k_pool.dim() != 3 or tuple(v_pool.shape) != tuple(k_pool.shape)
+            or tuple(k_pool.shape[1:]) != (hkv, tile)):
+        raise ValueError(f"pools must both be [num_pages][{hkv}][{tile}], got {tuple(k_pool.shape)} "
+                         f"and {tuple(v_pool.shape)}")
+    if token_seq.numel() != T or token_pos.numel() != T:
+        raise ValueError("token_seq/token_pos must have one entry per token")
+    rc = lib().kv_quant_append_cfg(
+        _dev(k_new, torch.float16, "k_new", 3), _dev(v_new, torch.float16, "v_new", 3),
+        _dev(token_seq, torch.int32, "token_seq"), _dev(token_pos, torch.int32, "token_pos"), T,
+        _dev(page_table, torch.int32, "page_table", 2), page_table.shape[1],
+        _dev(k_pool, torch.uint8, "k_pool"), _dev(v_pool, torch.uint8, "v_pool"), k_pool.shape[0],
+        hkv, d, int(page_size), ctypes.byref(cfg), _stream(k_new))
+    _check(rc, "kv_quant_append_cfg")
 
 
 def kv_append_fp16(k_new, v_new, token_seq, token_pos, page_table, k_pool, v_pool,

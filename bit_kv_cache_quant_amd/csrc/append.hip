@@ -186,9 +186,21 @@ __device__ __forceinline__ float rotate_chunks(const uint4 (&raw)[4], float (&y)
     return c1 * c2;
 }
 
+// Randomized Hadamard: the entries of chunk c (8 fp16 values, one 16-byte
+// load) whose bits are set in byte c of the 128-bit sign mask are negated
+// before the rotation, by flipping their fp16 sign bits (exact).
+__device__ __forceinline__ uint4 sign_flip_words(uint4 w, const uint32_t (&mask)[4], int chunk) {
+    const uint32_t b = (mask[chunk >> 2] >> (8 * (chunk & 3))) & 0xFFu;
+    w.x ^= ((b & 1u) << 15) | ((b & 2u) << 30);
+    w.y ^= ((b & 4u) << 13) | ((b & 8u) << 28);
+    w.z ^= ((b & 16u) << 11) | ((b & 32u) << 26);
+    w.w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
+    return w;
+}
+
 // A block covers 64 consecutive tokens of one (KV head, K or V): quad g takes
 // token base + g, so consecutive quads write consecutive slots of a page.
-template <int BH>
+template <int BH, bool SIGNS>
 __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs a) {
     const int q = threadIdx.x & 3;
     const int32_t t = (int32_t)blockIdx.x * kTokensPerBlock + (int32_t)(threadIdx.x >> 2);
@@ -207,6 +219,10 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
     uint4 raw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) raw[i] = src[4 * i];
+    if constexpr (SIGNS) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = sign_flip_words(raw[i], a.sign_mask, 4 * i + q);
+    }
 
     float y[32];
     // 1/sqrt(Bh) is a power of two for Bh = 64: then y * c is exact, and
@@ -337,6 +353,235 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Quantizer variants: one scale per group of G channels (INT4, optionally
+// chosen by a search over clipping ratios) or MXFP4 (E2M1 codes, one E8M0
+// scale per 32 channels).  Source: "BitDecoding-FP4:FP4 KVキャッシュのネイティブ
+// 復号", section 深掘り分析 (a scale chosen per group by scale search, after a
+// Hadamard rotation) and its opening summary (4-bit microscaling formats).
+// The arithmetic is bit-exact with the definition in include/kvq.h
+// (kv_quant_append_cfg).  The mapping is the token-wise kernel's: a quad of
+// lanes per vector, lane q holding chunks 4 i + q in y[8 i .. 8 i + 7], so
+// group g of G channels is registers y[R g .. R g + R - 1] (R = G / 4) of
+// every lane of the quad.
+// ---------------------------------------------------------------------------
+
+// m / 7 as the IEEE quotient (Markstein, see the file header).
+__device__ __forceinline__ float div7(float m) {
+    const float r7 = __builtin_bit_cast(float, 0x3E124925u);
+    const float m0 = m * r7;
+    float s32 = __builtin_fmaf(__builtin_fmaf(-m0, 7.0f, m), r7, m0);
+    asm("" : "+v"(s32));   // keeps the fp16 conversion from folding into the fma
+    return s32;
+}
+
+// Correctly rounded 1 / s for a positive finite fp16 value s (see the header).
+__device__ __forceinline__ float rcp_fp16(float s) {
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    return __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+
+// IEEE y / s for an fp16 divisor s given rcp = 1 / s (see the header; both
+// may carry the lane's sign, the quotient is odd in the divisor).
+__device__ __forceinline__ float div_fp16(float y, float s, float rcp) {
+    const float q0 = y * rcp;
+    const float e = __builtin_fmaf(-q0, s, y);
+    return __builtin_fmaf(e, rcp, q0);
+}
+
+__device__ __forceinline__ float quad_max_nonneg(float v) {
+    int k = __builtin_bit_cast(int, v);
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
+    k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, k);
+}
+
+__device__ __forceinline__ uint32_t quad_sum_u32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+    return v;
+}
+
+// Exponent E with m < 2^E for a normal positive fp32 m (frexp's exponent).
+__device__ __forceinline__ int frexp_exp(float m) {
+    return (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFFu) - 126;
+}
+
+// Error of INT4 candidate scale s (fp16 value; this lane's R registers):
+// sum of D^2, D = round-half-even((y - s c) 2^(12 - E)) with the candidate's
+// codes c; |D| <= 2^12, so the quad's sum over up to 128 channels fits in 32
+// bits.  y carries the lane's sign, which D^2 does not see.
+template <int R>
+__device__ __forceinline__ uint32_t int4_candidate_err(const float *y, float s, float sign, float scl) {
+    uint32_t err = 0;
+    if (s > 0.0f) {
+        const float sd = s * sign, rcp = rcp_fp16(s) * sign;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float c = __builtin_rintf(__builtin_amdgcn_fmed3f(div_fp16(y[r], sd, rcp), -8.0f, 7.0f));
+            const float res = __builtin_fmaf(-sd, c, y[r]);   // s c is exact: one rounding, as y - s c
+            const int D = (int)__builtin_rintf(res * scl);
+            const uint32_t a = (uint32_t)(D < 0 ? -D : D);
+            err += __umul24(a, a);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int D = (int)__builtin_rintf(y[r] * scl);
+            const uint32_t a = (uint32_t)(D < 0 ? -D : D);
+            err += __umul24(a, a);
+        }
+    }
+    return err;
+}
+
+template <int FMT, int G, bool SEARCH>
+__global__ __launch_bounds__(kBlockThreads) void quant_append_grouped_kernel(AppendArgs a) {
+    constexpr int NG = kHeadDim / G;       // scale groups per vector
+    constexpr int R = G / 4;               // registers of one group in each lane of the quad
+    constexpr int SB = FMT == KVQ_FMT_MXFP4 ? 1 : 2;   // bytes per scale
+    const int q = threadIdx.x & 3;
+    const int32_t t = (int32_t)blockIdx.x * kTokensPerBlock + (int32_t)(threadIdx.x >> 2);
+    if (t >= a.num_tokens) return;  // the whole quad leaves together
+    const int32_t h = (int32_t)blockIdx.y;
+    const bool is_v = blockIdx.z != 0;
+
+    const int32_t seq = a.token_seq[t];
+    const int32_t pos = a.token_pos[t];
+    const int32_t page = a.page_table[(int64_t)seq * a.max_pages_per_seq + (pos >> a.page_shift)];
+    const int32_t slot = pos & (a.page_size - 1);
+
+    const uint4 *src = reinterpret_cast<const uint4 *>((is_v ? a.v_new : a.k_new) +
+                                                       ((int64_t)t * a.num_kv_heads + h) * kHeadDim) + q;
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = sign_flip_words(src[4 * i], a.sign_mask, 4 * i + q);
+
+    // y = R (S x), times the lane's sign (see rotate_chunks)
+    float y[32];
+    float sign = 1.0f;
+    auto scale_entries = [&](float c) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) y[r] = y[r] * c;
+    };
+    switch (a.had_block) {
+        case 32: sign = rotate_chunks<32>(raw, y, q); scale_entries(inv_sqrt_block<32>()); break;
+        case 64: sign = rotate_chunks<64>(raw, y, q); scale_entries(inv_sqrt_block<64>()); break;
+        case 128: sign = rotate_chunks<128>(raw, y, q); scale_entries(inv_sqrt_block<128>()); break;
+        default:
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[8 * i + 2 * e] = half_bits_to_float(w4[e]);
+                    y[8 * i + 2 * e + 1] = half_bits_to_float(w4[e] >> 16);
+                }
+            }
+            break;
+    }
+
+    uint32_t nib[32];          // stored nibble of each entry
+    uint32_t sbits[NG];        // stored scale of each group (fp16 bits or E8M0 byte), same in the quad
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        float *yg = &y[R * gi];
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) m = fmaxf(m, fabsf(yg[r]));
+        m = quad_max_nonneg(m);
+        if constexpr (FMT == KVQ_FMT_INT4) {
+            _Float16 s16 = static_cast<_Float16>(div7(m));
+            if constexpr (SEARCH) {
+                // candidates fp16(fp32(m a_k) / 7), a_k = (16 - k) / 16: the
+                // smallest integer error wins, ties to the smaller k
+                const float scl = ldexpf(1.0f, 12 - (m > 0.0f ? frexp_exp(m) : 0));
+                uint32_t best = 0xFFFFFFFFu;
+#pragma unroll 1
+                for (int k = 0; k < 8; ++k) {
+                    const _Float16 c16 = static_cast<_Float16>(div7(m * (static_cast<float>(16 - k) * 0.0625f)));
+                    const uint32_t err = quad_sum_u32(int4_candidate_err<R>(yg, static_cast<float>(c16), sign, scl));
+                    if (err < best) {
+                        best = err;
+                        s16 = c16;
+                    }
+                }
+            }
+            const float s = static_cast<float>(s16);
+            sbits[gi] = __builtin_bit_cast(uint16_t, s16);
+            if (s > 0.0f) {
+                const float sd = s * sign, rcp = rcp_fp16(s) * sign;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float qt = __builtin_amdgcn_fmed3f(div_fp16(yg[r], sd, rcp), -8.0f, 7.0f);
+                    // round half to even, low nibble = code + 8; xor 8: two's complement
+                    nib[R * gi + r] = (__builtin_bit_cast(uint32_t, qt + 12582920.0f) & 0xFu) ^ 8u;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) nib[R * gi + r] = 0u;
+            }
+        } else {
+            // MXFP4: X = floor(log2 m) - 2, element = nearest E2M1 value to
+            // y / 2^X (ties to the even code, saturating at 6), sign bit set
+            // iff the value is negative
+            if (m > 0.0f) {
+                int X = frexp_exp(m) - 3;
+                X = X < -127 ? -127 : (X > 127 ? 127 : X);
+                sbits[gi] = (uint32_t)(X + 127);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float v = ldexpf(yg[r], -X);
+                    const float av = fabsf(v);
+                    const uint32_t mag = (uint32_t)(av > 0.25f) + (uint32_t)(av >= 0.75f) + (uint32_t)(av > 1.25f) +
+                                         (uint32_t)(av >= 1.75f) + (uint32_t)(av > 2.5f) + (uint32_t)(av >= 3.5f) +
+                                         (uint32_t)(av > 5.0f);
+                    const bool neg = (v != 0.0f) && ((v < 0.0f) != (sign < 0.0f));
+                    nib[R * gi + r] = mag | (neg ? 8u : 0u);
+                }
+            } else {
+                sbits[gi] = 0u;
+#pragma unroll
+                for (int r = 0; r < R; ++r) nib[R * gi + r] = 0u;
+            }
+        }
+    }
+
+    uint8_t *pool = static_cast<uint8_t *>(is_v ? a.v_pool : a.k_pool);
+    uint8_t *page_base = pool + (int64_t)page * a.num_kv_heads * a.tile_bytes;
+    uint8_t *code_row = page_base + ((int64_t)h * a.page_size + slot) * kCodeBytesPerRow;
+    uint8_t *scale_at = page_base + (int64_t)a.num_kv_heads * a.page_size * kCodeBytesPerRow +
+                        ((int64_t)h * a.page_size + slot) * (NG * SB);
+    __shared__ __attribute__((aligned(16))) uint32_t words[kTokensPerBlock][kCodeBytesPerRow / 4];
+    uint32_t *my_words = words[threadIdx.x >> 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w |= nib[8 * i + k] << (4 * k);
+        my_words[4 * i + q] = w;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint4 w4 = *reinterpret_cast<const uint4 *>(&my_words[4 * q]);
+    __builtin_nontemporal_store(v4u{w4.x, w4.y, w4.z, w4.w}, reinterpret_cast<v4u *>(code_row + 16 * q));
+    if (q == 0) {
+        if constexpr (NG * SB == 8) {
+            const uint2 v2 = make_uint2(sbits[0] | (sbits[1] << 16), sbits[2] | (sbits[3] << 16));
+            *reinterpret_cast<uint2 *>(scale_at) = v2;
+        } else if constexpr (NG * SB == 4) {
+            const uint32_t v1 = SB == 2 ? (sbits[0] | (sbits[NG - 1] << 16))
+                                        : (sbits[0] | (sbits[NG > 1 ? 1 : 0] << 8) | (sbits[NG > 2 ? 2 : 0] << 16) |
+                                           (sbits[NG > 3 ? 3 : 0] << 24));
+            __builtin_nontemporal_store(v1, reinterpret_cast<uint32_t *>(scale_at));
+        } else {
+            static_assert(NG * SB == 2, "scale bytes per vector");
+            __builtin_nontemporal_store(static_cast<uint16_t>(sbits[0]), reinterpret_cast<uint16_t *>(scale_at));
+        }
+    }
+}
+
 // fp16 baseline: copy one 256-byte row per 16 lanes.
 __global__ __launch_bounds__(kBlockThreads) void append_fp16_kernel(AppendArgs a) {
     const int lane = threadIdx.x & (kLanesPerVec - 1);
@@ -366,13 +611,38 @@ dim3 grid_for(const AppendArgs &a) {
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock), (unsigned)a.num_kv_heads, 2);
+    const bool signs = (a.sign_mask[0] | a.sign_mask[1] | a.sign_mask[2] | a.sign_mask[3]) != 0;
+    if (a.format != KVQ_FMT_INT4 || a.scale_group != kHeadDim || a.scale_search) {
+        // per-group scales, scale search, MXFP4
+#define KVQ_GROUPED(FMT, G, S) hipLaunchKernelGGL((quant_append_grouped_kernel<FMT, G, S>), grid, dim3(kBlockThreads), 0, stream, a)
+        if (a.format == KVQ_FMT_MXFP4) {
+            if (a.scale_group != 32 || a.scale_search) return hipErrorInvalidValue;
+            KVQ_GROUPED(KVQ_FMT_MXFP4, 32, false);
+        } else if (a.scale_group == 32) {
+            if (a.scale_search) KVQ_GROUPED(KVQ_FMT_INT4, 32, true); else KVQ_GROUPED(KVQ_FMT_INT4, 32, false);
+        } else if (a.scale_group == 64) {
+            if (a.scale_search) KVQ_GROUPED(KVQ_FMT_INT4, 64, true); else KVQ_GROUPED(KVQ_FMT_INT4, 64, false);
+        } else if (a.scale_group == 128) {
+            KVQ_GROUPED(KVQ_FMT_INT4, 128, true);
+        } else {
+            return hipErrorInvalidValue;
+        }
+#undef KVQ_GROUPED
+        return hipGetLastError();
+    }
+#define KVQ_TOKEN(BHV) \
+    do { \
+        if (signs) hipLaunchKernelGGL((quant_append_kernel<BHV, true>), grid, dim3(kBlockThreads), 0, stream, a); \
+        else hipLaunchKernelGGL((quant_append_kernel<BHV, false>), grid, dim3(kBlockThreads), 0, stream, a); \
+    } while (0)
     switch (a.had_block) {
-        case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kBlockThreads), 0, stream, a); break;
-        case 32: hipLaunchKernelGGL(quant_append_kernel<32>, grid, dim3(kBlockThreads), 0, stream, a); break;
-        case 64: hipLaunchKernelGGL(quant_append_kernel<64>, grid, dim3(kBlockThreads), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL(quant_append_kernel<128>, grid, dim3(kBlockThreads), 0, stream, a); break;
+        case 0: KVQ_TOKEN(0); break;
+        case 32: KVQ_TOKEN(32); break;
+        case 64: KVQ_TOKEN(64); break;
+        case 128: KVQ_TOKEN(128); break;
         default: return hipErrorInvalidValue;
     }
+#undef KVQ_TOKEN
     return hipGetLastError();
 }
 

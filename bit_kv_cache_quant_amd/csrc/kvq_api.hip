@@ -35,10 +35,25 @@ void *scratch_of_current_device() {
     return ptrs[dev];
 }
 
+static_assert(kvq::KVQ_FMT_INT4 == KVQ_FORMAT_INT4 && kvq::KVQ_FMT_MXFP4 == KVQ_FORMAT_MXFP4, "format codes");
+
 bool valid_page_size(int32_t p) { return p == 16 || p == 32; }
 bool valid_had_block(int32_t bh) { return bh == 0 || bh == 32 || bh == 64 || bh == 128; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int log2i(int32_t v) { int s = 0; while ((1 << s) < v) ++s; return s; }
+
+bool valid_cfg(const kvq_quant_config *c) {
+    if (!c || !valid_had_block(c->had_block)) return false;
+    if (c->format == KVQ_FORMAT_INT4)
+        return (c->scale_group == 32 || c->scale_group == 64 || c->scale_group == 128) &&
+               (c->scale_search == 0 || c->scale_search == 1);
+    if (c->format == KVQ_FORMAT_MXFP4) return c->scale_group == 32 && c->scale_search == 0;
+    return false;
+}
+
+size_t scale_bytes_cfg(const kvq_quant_config *c) {
+    return (size_t)(kHeadDim / c->scale_group) * (c->format == KVQ_FORMAT_MXFP4 ? 1 : 2);
+}
 
 // Split-K choice shared by the workspace query and the decode calls.  One
 // split is one wave's work item.  Aim for about 2048 of them (two per SIMD)
@@ -366,6 +381,52 @@ int kv_quant_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t 
     a.page_size = page_size;
     a.page_shift = log2i(page_size);
     a.had_block = had_block;
+    a.format = KVQ_FORMAT_INT4;
+    a.scale_group = kHeadDim;
+    return kvq::launch_quant_append(a, st) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_page_tile_bytes_cfg(int32_t head_dim, int32_t page_size, const kvq_quant_config *cfg) {
+    if (head_dim != kHeadDim || !valid_page_size(page_size) || !valid_cfg(cfg)) return 0;
+    return (size_t)page_size * (head_dim / 2) + (size_t)page_size * scale_bytes_cfg(cfg);
+}
+
+int kv_quant_append_cfg(const uint16_t *k_new, const uint16_t *v_new, const int32_t *token_seq,
+                        const int32_t *token_pos, int32_t num_tokens, const int32_t *page_table,
+                        int32_t max_pages_per_seq, uint8_t *k_pool, uint8_t *v_pool, int64_t num_pages,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, const kvq_quant_config *cfg,
+                        void *stream) {
+    int rc = validate_append(k_new, v_new, token_seq, token_pos, num_tokens, page_table, max_pages_per_seq,
+                             k_pool, v_pool, num_pages, num_kv_heads, head_dim, page_size);
+    if (rc != KVQ_OK) return rc;
+    if (!cfg) return KVQ_ERR_INVALID_ARG;
+    if (!valid_cfg(cfg)) return KVQ_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return KVQ_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_checks_enabled()) {
+        rc = check_append_indices(token_seq, token_pos, num_tokens, page_table, max_pages_per_seq, num_pages,
+                                  page_size, st);
+        if (rc != KVQ_OK) return rc;
+    }
+    kvq::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.token_seq = token_seq;
+    a.token_pos = token_pos;
+    a.page_table = page_table;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.tile_bytes = (int64_t)kvq_page_tile_bytes_cfg(head_dim, page_size, cfg);
+    a.num_tokens = num_tokens;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.num_kv_heads = num_kv_heads;
+    a.page_size = page_size;
+    a.page_shift = log2i(page_size);
+    a.had_block = cfg->had_block;
+    a.format = cfg->format;
+    a.scale_group = cfg->scale_group;
+    a.scale_search = cfg->scale_search;
+    for (int i = 0; i < 4; ++i) a.sign_mask[i] = cfg->sign_mask[i];
     return kvq::launch_quant_append(a, st) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -14,6 +14,8 @@ constexpr int kChunkTokens = 64;       // decode processes tokens in chunks of 6
 constexpr int kMaxSplitTokens = 2048;  // longest page range one decode wave takes (split mode)
 constexpr int kMaxScanBatch = 4096;    // balanced decode: largest batch one block scans
 constexpr int kMaxRangeChunks = 64;    // balanced decode: longest work range, in chunks
+constexpr int KVQ_FMT_INT4 = 0;        // quantizer formats (KVQ_FORMAT_* in include/kvq.h)
+constexpr int KVQ_FMT_MXFP4 = 1;
 
 struct AppendArgs {
     const uint16_t *k_new;
@@ -30,6 +32,13 @@ struct AppendArgs {
     int32_t page_size;
     int32_t page_shift;        // log2(page_size)
     int32_t had_block;
+    // Quantizer variant (kv_quant_append_cfg): KVQ_FORMAT_*, channels per
+    // scale, scale search, and the sign mask applied before the rotation
+    // (bit i: channel i negated).  The plain method is INT4, 128, 0, no signs.
+    int32_t format;
+    int32_t scale_group;
+    int32_t scale_search;
+    uint32_t sign_mask[4];
 };
 
 struct DecodeArgs {

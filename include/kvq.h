@@ -277,6 +277,74 @@ int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint
                            size_t workspace_bytes, int32_t pages_per_split,
                            void *phase_event, void *stream);
 
+/*
+ * Quantizer variants ("BitDecoding-FP4:FP4 KVキャッシュのネイティブ復号", section
+ * 深掘り分析: with one scale per token a single outlier widens the range of
+ * the whole token, so smoothing and a Hadamard rotation spread outliers and
+ * a scale search picks a scale per group; opening summary: 4-bit
+ * microscaling KV formats, NVFP4 / MXFP4; "KVキャッシュを4ビットへ", section
+ * 回転のトリック: block-diagonal Hadamard in the QuaRot / SpinQuant line of
+ * rotations, whose randomized form multiplies by a random +-1 diagonal).
+ *
+ * A configuration (a HOST pointer, read during the call):
+ *   format        KVQ_FORMAT_INT4: INT4 codes, fp16 scales;
+ *                 KVQ_FORMAT_MXFP4: E2M1 codes, one E8M0 scale per 32 channels
+ *   had_block     0, 32, 64, 128, as for kv_quant_append
+ *   scale_group   channels per scale: INT4 128 (one per token and head: the
+ *                 method itself), 64 or 32 (one per Hadamard block when equal
+ *                 to had_block); MXFP4 32
+ *   scale_search  INT4: 0 = absmax / 7; 1 = search over clipping ratios;
+ *                 MXFP4: 0
+ *   sign_mask     randomized Hadamard: bit i (word i / 32, bit i % 32) set
+ *                 negates channel i before the rotation; all zero = plain
+ * Computation, for each vector x (fp16 [128]) and each group of scale_group
+ * channels of y = R (S x) (S the sign mask, R the block rotation as in
+ * kv_quant_append, fp32 in the same order):
+ *   INT4, no search: s = fp16(m / 7) with m the group's absmax, codes as in
+ *     kv_quant_append;
+ *   INT4, search: among s_k = fp16(fp32(m (16 - k) / 16) / 7), k = 0..7,
+ *     the one whose codes give the smallest sum over the group of D^2,
+ *     D = round-half-even((y - s_k c) 2^(12 - E)) with m < 2^E (an exact
+ *     integer), ties to the smaller k;
+ *   MXFP4: scale 2^X with X = floor(log2 m) - 2 (byte X + 127; 0 for an
+ *     all-zero group), each element the E2M1 value {0, .5, 1, 1.5, 2, 3, 4,
+ *     6} nearest y / 2^X (ties to the code with a zero mantissa bit,
+ *     saturating at 6), sign bit set iff y < 0.
+ * Layout: a page holds the code rows of every KV head (page_size x 64 bytes
+ * each, as for INT4), then the scales: (128 / scale_group) per (head, slot),
+ * (head, slot, group) at num_kv_heads * page_size * 64 +
+ * ((head * page_size + slot) * (128 / scale_group) + group) * scale_bytes,
+ * scale_bytes 2 (fp16, little-endian) or 1 (E8M0).
+ */
+enum { KVQ_FORMAT_INT4 = 0, KVQ_FORMAT_MXFP4 = 1 };
+
+typedef struct kvq_quant_config {
+    int32_t format;
+    int32_t had_block;
+    int32_t scale_group;
+    int32_t scale_search;
+    uint32_t sign_mask[4];
+} kvq_quant_config;
+
+/* Bytes of one (page, KV head) share of a pool under `cfg`:
+ * page_size * 64 + page_size * (128 / scale_group) * scale_bytes; 0 for
+ * unsupported arguments. */
+size_t kvq_page_tile_bytes_cfg(int32_t head_dim, int32_t page_size, const kvq_quant_config *cfg);
+
+/*
+ * kv_quant_append_cfg — kv_quant_append under a quantizer configuration:
+ * the same arguments with `cfg` (host pointer) in place of had_block; pools
+ * uint8 [num_pages][num_kv_heads][kvq_page_tile_bytes_cfg(...)].  The stored
+ * bytes are bit-exact with the definition above.  cfg = {INT4, Bh, 128, 0,
+ * 0} is exactly kv_quant_append.
+ */
+int kv_quant_append_cfg(const uint16_t *k_new, const uint16_t *v_new,
+                        const int32_t *token_seq, const int32_t *token_pos, int32_t num_tokens,
+                        const int32_t *page_table, int32_t max_pages_per_seq,
+                        uint8_t *k_pool, uint8_t *v_pool, int64_t num_pages,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                        const kvq_quant_config *cfg, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

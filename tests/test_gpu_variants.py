@@ -1,0 +1,109 @@
+"""GPU parity of the quantizer variants (kv_quant_append_cfg,
+paged_decode_attn_cfg) with the oracle: per-group INT4 scales (with and
+without scale search), the randomized Hadamard sign mask, and MXFP4.  Pools
+are canary-filled and compared whole, byte for byte; attention within 2e-3
+of the fp64 oracle on the same cache."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_quant_amd as kvq
+import oracle
+import workloads as wl
+from gpu_util import ATOL, canary, say
+
+pytestmark = pytest.mark.gpu
+D = wl.HEAD_DIM
+MASK = 0x9E3779B97F4A7C15F39CC0605CEDC834   # a fixed 128-bit sign mask
+
+# (format, had_block, scale_group, scale_search, sign_mask)
+APPEND_CFGS = [
+    (0, 32, 32, 0, 0), (0, 64, 64, 0, 0), (0, 128, 32, 0, 0), (0, 0, 32, 0, 0), (0, 0, 64, 0, MASK),
+    (0, 32, 32, 1, 0), (0, 64, 64, 1, MASK), (0, 128, 128, 1, 0), (0, 0, 32, 1, 0),
+    (0, 32, 128, 0, MASK), (0, 64, 128, 0, MASK), (0, 128, 128, 0, MASK), (0, 0, 128, 0, MASK),
+    (1, 0, 32, 0, 0), (1, 32, 32, 0, 0), (1, 64, 32, 0, MASK), (1, 128, 32, 0, 0),
+]
+
+
+def _ids(c):
+    f, bh, g, s, m = c
+    return f"{'mx' if f else 'int4'}-bh{bh}-g{g}{'-search' if s else ''}{'-signs' if m else ''}"
+
+
+def _pools(w, cfg, dev, seed):
+    tb = kvq.page_tile_bytes_cfg(D, w.page_size, kvq.quant_config(*cfg))
+    assert tb == oracle.tile_bytes_cfg(D, w.page_size, oracle.qcfg(*cfg))
+    shape = (w.num_pages, w.num_kv_heads, tb)
+    return canary(shape, 500 + seed, dev), canary(shape, 600 + seed, dev)
+
+
+def _special_rows(L, hkv, seed):
+    """Rows that exercise the edges: zero vectors, tiny values (subnormal
+    fp16 scales), large values, exact ties of the code grids, single spikes."""
+    r = np.random.default_rng(seed)
+    k = (r.standard_normal((L, hkv, D)) * 2).astype(np.float32)
+    k[0] = 0
+    k[1] *= 1e-5
+    k[2] *= 300
+    k[3] = r.integers(-28, 29, size=(hkv, D)) / 4.0           # quarter steps: many exact ties
+    k[4] = 0
+    k[4, :, 7] = 5.0                                          # one spike per vector
+    k[5, :, :32] = 0                                          # an all-zero group
+    k[6] = np.where(r.random((hkv, D)) < 0.5, -0.0, 0.0)      # signed zeros
+    return k.astype(np.float16)
+
+
+def _build(cfg, w, dev, seed, special=False):
+    ocfg, gcfg = oracle.qcfg(*cfg), kvq.quant_config(*cfg)
+    kp, vp = _pools(w, cfg, dev, seed)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    pt = w.table(0)
+    pt_d = torch.as_tensor(pt, device=dev)
+    for b in range(w.batch):
+        L = int(w.prefill_lens[b])
+        if L <= 0:
+            continue
+        k, v = w.rows(0, b, 0, L, dev)
+        if special and b == 0 and L >= 8:
+            sk = _special_rows(L, w.num_kv_heads, seed)
+            k = torch.as_tensor(sk, device=dev)
+            v = torch.as_tensor(sk[::-1].copy(), device=dev)
+        seq = torch.full((L,), b, dtype=torch.int32, device=dev)
+        pos = torch.arange(L, dtype=torch.int32, device=dev)
+        kvq.kv_quant_append_cfg(k, v, seq, pos, pt_d, kp, vp, w.page_size, gcfg)
+        oracle.kv_quant_append_cfg(k.cpu().numpy(), v.cpu().numpy(), seq.cpu().numpy(), pos.cpu().numpy(), pt,
+                                   hk, hv, ocfg, w.page_size)
+    torch.cuda.synchronize()
+    return kp, vp, hk, hv
+
+
+@pytest.mark.parametrize("cfg", APPEND_CFGS, ids=_ids)
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_variant_append_bit_exact(dev, cfg, page_size):
+    lens = [130, 1, 0, 77, 64]
+    w = wl.small(len(lens), lens, cfg[1], page_size, cfg_id=400 + page_size)
+    say(f"variant append {_ids(cfg)} P={page_size}")
+    kp, vp, hk, hv = _build(cfg, w, dev, seed=cfg[1] + cfg[2] + page_size, special=True)
+    assert np.array_equal(kp.cpu().numpy(), hk), "K pool differs from the oracle's"
+    assert np.array_equal(vp.cpu().numpy(), hv), "V pool differs from the oracle's"
+
+
+def test_token_wise_config_is_the_plain_append(dev):
+    """{INT4, Bh, 128, no search, no signs} through the variant entry point
+    writes exactly what kv_quant_append writes."""
+    lens = [200, 33]
+    w = wl.small(len(lens), lens, 64, 16, cfg_id=420)
+    kp1, vp1 = _pools(w, (0, 64, 128, 0, 0), dev, 1)
+    kp2, vp2 = kp1.clone(), vp1.clone()
+    pt_d = torch.as_tensor(w.table(0), device=dev)
+    for b in range(w.batch):
+        L = int(w.prefill_lens[b])
+        k, v = w.rows(0, b, 0, L, dev)
+        seq = torch.full((L,), b, dtype=torch.int32, device=dev)
+        pos = torch.arange(L, dtype=torch.int32, device=dev)
+        kvq.kv_quant_append(k, v, seq, pos, pt_d, kp1, vp1, 16, 64)
+        kvq.kv_quant_append_cfg(k, v, seq, pos, pt_d, kp2, vp2, 16, kvq.quant_config(0, 64, 128, 0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(kp1, kp2) and torch.equal(vp1, vp2)
