@@ -63,6 +63,8 @@ SIGNATURES = {
     "kvq_page_tile_bytes_cfg": (_SZ, [_I32, _I32, _CFG]),
     "kv_quant_append_cfg": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _CFG,
                                            _P]),
+    "paged_decode_attn_cfg": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                             _CFG, _F32, _P, _P, _SZ, _I32, _P, _P]),
     "kv_append_fp16": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "paged_decode_attn_int4_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                       _I32, _I32, _I32, _F32, _P, _I32, _P, _P]),
@@ -222,10 +224,12 @@ def _event_handle(event):
 
 def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
             page_size: int, had_block: int, softmax_scale: float, max_context_len: int,
-            out=None, workspace=None, pages_per_split: int = 0, phase_event=None):
+            out=None, workspace=None, pages_per_split: int = 0, phase_event=None, cfg=None):
     import torch
     B, hq, d = q.shape
-    if int4:
+    if cfg is not None:
+        want = (int(num_kv_heads), page_tile_bytes_cfg(d, int(page_size), cfg))
+    elif int4:
         want = (int(num_kv_heads), page_tile_bytes(d, int(page_size)))
     else:
         want = (int(num_kv_heads), int(page_size), d)
@@ -251,13 +255,25 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
             _dev(page_table, torch.int32, "page_table", 2), page_table.shape[1],
             _dev(context_lens, torch.int32, "context_lens", 1), B, int(max_context_len), hq,
             int(num_kv_heads), d, int(page_size)]
-    if int4:
+    if cfg is not None:
+        args.append(ctypes.byref(cfg))
+    elif int4:
         args.append(int(had_block))
     args += [float(softmax_scale), _dev(out, torch.float32, "out", 3), ws_ptr, ws_bytes,
              int(pages_per_split), _event_handle(phase_event), _stream(q)]
-    fn = lib().paged_decode_attn_int4 if int4 else lib().paged_decode_attn_fp16
-    _check(fn(*args), "paged_decode_attn_int4" if int4 else "paged_decode_attn_fp16")
+    name = "paged_decode_attn_cfg" if cfg is not None else ("paged_decode_attn_int4" if int4
+                                                            else "paged_decode_attn_fp16")
+    _check(getattr(lib(), name)(*args), name)
     return out
+
+
+def paged_decode_attn_cfg(q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int, page_size: int,
+                          cfg: QuantConfig, softmax_scale: float, max_context_len: int, out=None, workspace=None,
+                          pages_per_split: int = 0, phase_event=None):
+    """One decode step over a cache written by kv_quant_append_cfg with the
+    same configuration; returns fp32 [B][Hq][D]."""
+    return _decode(True, q, k_pool, v_pool, page_table, context_lens, num_kv_heads, page_size, 0,
+                   softmax_scale, max_context_len, out, workspace, pages_per_split, phase_event, cfg)
 
 
 def paged_prefill_attn_int4(q, q_start, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,

@@ -79,8 +79,10 @@ __device__ __forceinline__ void add_round(const Round &r, const int base, const 
     M = Mr;
 }
 
-// Inverse rotation of 128 values held as (2t, 2t+1) by lane t, then store.
-__device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh, int t, float *out) {
+// Inverse rotation of 128 values held as (2t, 2t+1) by lane t (S R: the
+// block rotation, then the sign mask), then store.
+__device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh, int t, const uint32_t (&mask)[4],
+                                                      float *out) {
     if (bh > 0) {
         float u = o0 + o1, v = o0 - o1;          // span 1: inside the lane
         o0 = u;
@@ -97,6 +99,9 @@ __device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh
         o0 *= c;
         o1 *= c;
     }
+    const uint32_t bits = (mask[t >> 4] >> (2 * (t & 15))) & 3u;   // channels 2t, 2t + 1
+    o0 = (bits & 1u) ? -o0 : o0;
+    o1 = (bits & 2u) ? -o1 : o1;
     *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(o0, o1);
 }
 
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         return;
     }
     const float inv = 1.0f / lsum;
-    rotate_back_and_store(o0 * inv, o1 * inv, bh, t, out);
+    rotate_back_and_store(o0 * inv, o1 * inv, bh, t, a.sign_mask, out);
 }
 
 }  // namespace

@@ -80,6 +80,17 @@ __device__ __forceinline__ int row_sum16_i(int v) {
 // largest one.  -inf gives 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// fp16 query words holding dims 8j .. 8j + 7 with the channels set in byte
+// j of the 128-bit sign mask negated (exact: sign-bit flips).
+__device__ __forceinline__ uint4 sign_flip_query(uint4 w, const uint32_t (&mask)[4], int j) {
+    const uint32_t b = (mask[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    w.x ^= ((b & 1u) << 15) | ((b & 2u) << 30);
+    w.y ^= ((b & 4u) << 13) | ((b & 8u) << 28);
+    w.z ^= ((b & 16u) << 11) | ((b & 32u) << 26);
+    w.w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
+    return w;
+}
+
 // Orders LDS traffic between the lanes of one wave (no cross-wave sharing).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

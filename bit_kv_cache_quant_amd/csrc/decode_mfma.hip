@@ -333,11 +333,13 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     // ---- setup: rotated query as fixed-point limbs; row g = head g ----
     float qv[8];
     {
+        // randomized Hadamard: negate the masked channels (dims 8j..8j+7: byte j of the mask)
+        const uint4 rs = sign_flip_query(raw, a.sign_mask, j);
         if (g < nheads) {
-            qv[0] = half_to_float(raw.x); qv[1] = half_to_float(raw.x >> 16);
-            qv[2] = half_to_float(raw.y); qv[3] = half_to_float(raw.y >> 16);
-            qv[4] = half_to_float(raw.z); qv[5] = half_to_float(raw.z >> 16);
-            qv[6] = half_to_float(raw.w); qv[7] = half_to_float(raw.w >> 16);
+            qv[0] = half_to_float(rs.x); qv[1] = half_to_float(rs.x >> 16);
+            qv[2] = half_to_float(rs.y); qv[3] = half_to_float(rs.y >> 16);
+            qv[4] = half_to_float(rs.z); qv[5] = half_to_float(rs.z >> 16);
+            qv[6] = half_to_float(rs.w); qv[7] = half_to_float(rs.w >> 16);
         } else {
 #pragma unroll
             for (int r = 0; r < 8; ++r) qv[r] = 0.0f;

@@ -260,11 +260,12 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
                   int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale, float *out,
                   void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *phase_event,
-                  void *stream, bool use_scratch = false) {
+                  void *stream, bool use_scratch = false, const kvq_quant_config *cfg = nullptr) {
     int rc = validate_decode(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                              max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, out);
     if (rc != KVQ_OK) return rc;
     if (int4 && !valid_had_block(had_block)) return KVQ_ERR_UNSUPPORTED;
+    if (cfg && !valid_cfg(cfg)) return KVQ_ERR_UNSUPPORTED;
     if (pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
     if (batch == 0) return KVQ_OK;
     const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
@@ -307,7 +308,12 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     } else {
         a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * nsplit * kHeadDim;
     }
-    a.tile_bytes = int4 ? (int64_t)kvq_page_tile_bytes(head_dim, page_size) : (int64_t)page_size * head_dim * 2;
+    a.tile_bytes = !int4 ? (int64_t)page_size * head_dim * 2
+                         : cfg ? (int64_t)kvq_page_tile_bytes_cfg(head_dim, page_size, cfg)
+                               : (int64_t)kvq_page_tile_bytes(head_dim, page_size);
+    a.format = cfg ? cfg->format : KVQ_FORMAT_INT4;
+    a.scale_group = cfg ? cfg->scale_group : kHeadDim;
+    for (int i = 0; i < 4; ++i) a.sign_mask[i] = cfg ? cfg->sign_mask[i] : 0u;
     a.max_pages_per_seq = max_pages_per_seq;
     a.max_context_len = max_context_len;
     a.batch = batch;
@@ -321,11 +327,13 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.pages_per_split = pps;
     a.num_splits = nsplit;
     a.score_scale = softmax_scale * 1.4426950408889634f;
-    hipError_t e = int4 ? kvq::launch_decode_int4_mfma(a, st) : kvq::launch_decode_fp16(a, st);
+    const bool grouped = int4 && (a.format != KVQ_FORMAT_INT4 || a.scale_group != kHeadDim);
+    hipError_t e = !int4 ? kvq::launch_decode_fp16(a, st)
+                         : grouped ? kvq::launch_decode_grouped(a, st) : kvq::launch_decode_int4_mfma(a, st);
     if (e != hipSuccess) return KVQ_ERR_HIP;
     if (phase_event && hipEventRecord(static_cast<hipEvent_t>(phase_event), st) != hipSuccess)
         return KVQ_ERR_HIP;
-    e = kvq::launch_combine(a, int4 && had_block > 0, st);
+    e = kvq::launch_combine(a, int4 && a.had_block > 0, st);
     return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -528,6 +536,19 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
     return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                          max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
                          softmax_scale, out, workspace, workspace_bytes, pages_per_split, phase_event, stream);
+}
+
+int paged_decode_attn_cfg(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,
+                          const int32_t *page_table, int32_t max_pages_per_seq, const int32_t *context_lens,
+                          int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t page_size, const kvq_quant_config *cfg, float softmax_scale,
+                          float *out, void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                          void *phase_event, void *stream) {
+    if (!cfg) return KVQ_ERR_INVALID_ARG;
+    return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
+                         max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, cfg->had_block,
+                         softmax_scale, out, workspace, workspace_bytes, pages_per_split, phase_event, stream, false,
+                         cfg);
 }
 
 int paged_decode_attn_int4_noalloc(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,

@@ -64,6 +64,12 @@ struct DecodeArgs {
     int32_t pages_per_split;
     int32_t num_splits;
     float score_scale;         // softmax_scale * log2(e): scores are kept in log2 units
+    // Quantizer variant of the cache: KVQ_FMT_*, channels per scale, and the
+    // sign mask of the randomized Hadamard (bit i: channel i negated before
+    // the rotation; the query gets it too, the output gets it back).
+    int32_t format;
+    int32_t scale_group;
+    uint32_t sign_mask[4];
     // Balanced decode (sk_groups > 0): the concatenated chunk list of all
     // sequences is cut into equal ranges, one per block group; partial states
     // are indexed by (head quad, range + sequence, wave, head).
@@ -129,6 +135,7 @@ hipError_t launch_prefill_int4(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_append_fp16(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fp16(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_grouped(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream);
 
 }  // namespace kvq

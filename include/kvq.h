@@ -345,6 +345,25 @@ int kv_quant_append_cfg(const uint16_t *k_new, const uint16_t *v_new,
                         int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                         const kvq_quant_config *cfg, void *stream);
 
+/*
+ * paged_decode_attn_cfg — paged_decode_attn_int4 over a cache written by
+ * kv_quant_append_cfg with the same `cfg` (host pointer) in place of
+ * had_block: q' = R (S q) (S the sign mask, R the block rotation), keys and
+ * values dequantized with their group's scale (fp16, or 2^X for MXFP4
+ * E2M1 codes), z_j = softmax_scale * (q' . k_j), w = softmax(z),
+ * out = S R (sum_j w_j v_j).  Workspace, split, context contract and errors
+ * as paged_decode_attn_int4 (paged_decode_attn_workspace_bytes gives the
+ * size).  cfg = {INT4, Bh, 128, *, 0} is exactly paged_decode_attn_int4.
+ */
+int paged_decode_attn_cfg(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                          int64_t num_pages, const int32_t *page_table,
+                          int32_t max_pages_per_seq, const int32_t *context_lens,
+                          int32_t batch, int32_t max_context_len, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          const kvq_quant_config *cfg, float softmax_scale, float *out,
+                          void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                          void *phase_event, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,3 +107,64 @@ def test_token_wise_config_is_the_plain_append(dev):
         kvq.kv_quant_append_cfg(k, v, seq, pos, pt_d, kp2, vp2, 16, kvq.quant_config(0, 64, 128, 0, 0))
     torch.cuda.synchronize()
     assert torch.equal(kp1, kp2) and torch.equal(vp1, vp2)
+
+
+DECODE_CFGS = [
+    (0, 32, 32, 0, 0), (0, 64, 64, 0, 0), (0, 128, 32, 0, 0), (0, 0, 32, 0, 0), (0, 32, 32, 1, MASK),
+    (0, 64, 128, 0, MASK), (0, 0, 128, 0, MASK), (0, 128, 128, 1, MASK),
+    (1, 0, 32, 0, 0), (1, 32, 32, 0, 0), (1, 128, 32, 0, MASK),
+]
+
+
+@pytest.mark.parametrize("cfg", DECODE_CFGS, ids=_ids)
+@pytest.mark.parametrize("sched", ["split", "balanced"])
+def test_variant_decode_against_oracle(dev, cfg, sched):
+    """Ragged lengths (empty, one token, page and chunk tails); 5 sequences
+    run the per-sequence split schedule, 21 the batch-wide one.  Page size
+    16 for the split case, 32 for the batch-wide one."""
+    if sched == "split":
+        lens, P = [0, 1, 300, 65, 129], 16
+    else:
+        r = np.random.default_rng(31)
+        lens, P = [int(x) for x in r.integers(0, 350, size=21)], 32
+        lens[3] = 0
+        lens[4] = 1
+    w = wl.small(len(lens), lens, cfg[1], P, cfg_id=430 + P)
+    say(f"variant decode {_ids(cfg)} {sched} B={w.batch} P={P}")
+    kp, vp, hk, hv = _build(cfg, w, dev, seed=7)
+    assert np.array_equal(kp.cpu().numpy(), hk) and np.array_equal(vp.cpu().numpy(), hv)
+    q = w.query(0, dev)
+    maxctx = int(max(lens))
+    out = kvq.paged_decode_attn_cfg(q, kp, vp, torch.as_tensor(w.table(0), device=dev),
+                                    torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, P,
+                                    kvq.quant_config(*cfg), w.softmax_scale, maxctx)
+    torch.cuda.synchronize()
+    want = oracle.paged_decode_attn_cfg(q.cpu().numpy(), hk, hv, w.table(0), w.context_lens, w.num_kv_heads, P,
+                                        oracle.qcfg(*cfg), w.softmax_scale)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - want)))
+    say(f"  max-abs error {err:.3e}")
+    assert err <= ATOL
+    assert np.all(got[lens.index(0)] == 0)
+
+
+@pytest.mark.parametrize("cfg", [(0, 32, 32, 1, MASK), (1, 128, 32, 0, MASK)], ids=_ids)
+@pytest.mark.parametrize("mult", [4.0])
+def test_variant_decode_sharp_softmax(dev, cfg, mult):
+    """Four times the softmax scale (a few keys carry most of the weight):
+    the per-group score sums keep the 2e-3 bar."""
+    lens = [300, 150, 40]
+    w = wl.small(len(lens), lens, cfg[1], 16, cfg_id=440)
+    kp, vp, hk, hv = _build(cfg, w, dev, seed=9)
+    q = w.query(0, dev)
+    scale = float(np.float32(mult * w.softmax_scale))
+    out = kvq.paged_decode_attn_cfg(q, kp, vp, torch.as_tensor(w.table(0), device=dev),
+                                    torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, 16,
+                                    kvq.quant_config(*cfg), scale, 300)
+    torch.cuda.synchronize()
+    want = oracle.paged_decode_attn_cfg(q.cpu().numpy(), hk, hv, w.table(0), w.context_lens, w.num_kv_heads, 16,
+                                        oracle.qcfg(*cfg), scale)
+    err = float(np.max(np.abs(out.cpu().numpy() - want)))
+    say(f"variant decode {_ids(cfg)} at {mult}x scale: max-abs {err:.3e}")
+    assert err <= ATOL
