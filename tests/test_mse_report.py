@@ -68,3 +68,77 @@ def test_per_token_scale_limit_on_normal_channels(reports):
     raises the normal channels' error above that of naive INT4 (whose
     normal channels round to 0 or 1 step and keep a small error)."""
     assert reports[128]["k_mse_normal"] > reports[0]["k_mse_normal"]
+
+
+# ----------------------------------------------------------------------------
+# Quantizer variants on the same input structure (oracle only).
+# ----------------------------------------------------------------------------
+
+VARIANTS = {
+    "naive INT4 (token scale, no rotation)": (oracle.FMT_INT4, 0, 128, 0, 0),
+    "SAW-INT4 Bh128 (token scale)": (oracle.FMT_INT4, 128, 128, 0, 0),
+    "SAW-INT4 Bh128 + scale search": (oracle.FMT_INT4, 128, 128, 1, 0),
+    "SAW-INT4 Bh128 + random signs": (oracle.FMT_INT4, 128, 128, 0, 0x9E3779B97F4A7C15F39CC0605CEDC834),
+    "INT4 Bh32, scale per block": (oracle.FMT_INT4, 32, 32, 0, 0),
+    "INT4 Bh32, scale per block + search": (oracle.FMT_INT4, 32, 32, 1, 0),
+    "INT4 Bh64, scale per block + search": (oracle.FMT_INT4, 64, 64, 1, 0),
+    "INT4 Bh128, scale per 32 + search": (oracle.FMT_INT4, 128, 32, 1, 0),
+    "MXFP4 (no rotation)": (oracle.FMT_MXFP4, 0, 32, 0, 0),
+    "MXFP4 Bh32": (oracle.FMT_MXFP4, 32, 32, 0, 0),
+    "MXFP4 Bh128": (oracle.FMT_MXFP4, 128, 32, 0, 0),
+}
+
+LV = 1024   # positions of sequence 0 used for the variant table
+
+
+def _variant_report(cfg_args) -> dict:
+    w = wl.c5()
+    P = w.page_size
+    cfg = oracle.qcfg(*cfg_args)
+    k, v = w.rows(0, 0, 0, LV)
+    kk, vv = k.numpy(), v.numpy()
+    ch = w.outlier_channels(0, wl.K_TENSOR)
+    sums = {"all": [0.0, 0], "normal": [0.0, 0], "outlier": [0.0, 0]}
+    for h in range(w.num_kv_heads):
+        rec = np.stack([oracle.reconstruct_cfg(kk[t, h], cfg) for t in range(LV)])
+        err = (rec - kk[:, h, :].astype(np.float64)) ** 2
+        mask = np.zeros(D, bool)
+        mask[ch[h]] = True
+        for name, m in (("all", np.ones(D, bool)), ("normal", ~mask), ("outlier", mask)):
+            sums[name][0] += float(err[:, m].sum())
+            sums[name][1] += int(err[:, m].size)
+    res = {f"k_mse_{n}": s / c for n, (s, c) in sums.items()}
+    pages = LV // P
+    pt = np.arange(pages, dtype=np.int32).reshape(1, pages)
+    tb = oracle.tile_bytes_cfg(D, P, cfg)
+    kp = np.zeros((pages, w.num_kv_heads, tb), np.uint8)
+    vp = np.zeros_like(kp)
+    oracle.kv_quant_append_cfg(kk, vv, np.zeros(LV, np.int32), np.arange(LV, dtype=np.int32), pt, kp, vp, cfg, P)
+    q = w.query(0).numpy()[:1]
+    out = oracle.paged_decode_attn_cfg(q, kp, vp, pt, np.array([LV], np.int32), w.num_kv_heads, P, cfg,
+                                       w.softmax_scale)[0]
+    ref = oracle.dense_decode_f64(q[0], kk, vv, w.softmax_scale)
+    res["attn_out_mse"] = float(np.mean((out.astype(np.float64) - ref) ** 2))
+    res["bytes_per_token_head"] = 2 * tb // P
+    return res
+
+
+@pytest.fixture(scope="module")
+def variant_reports():
+    return {name: _variant_report(args) for name, args in VARIANTS.items()}
+
+
+def test_variant_table(variant_reports):
+    """Print the table (run with -s); the claims the variants are for: one
+    scale per Hadamard block of 32, with the clipping search, has under half
+    the method's key error on x50 outlier keys and a lower attention-output
+    error; the search never raises the key error of the same grouping."""
+    for name, r in variant_reports.items():
+        print(f"{name:40s} " + ", ".join(f"{k} {v:.4g}" for k, v in r.items()), flush=True)
+    base = variant_reports["SAW-INT4 Bh128 (token scale)"]
+    best = variant_reports["INT4 Bh32, scale per block + search"]
+    assert best["k_mse_all"] < 0.5 * base["k_mse_all"]
+    assert best["attn_out_mse"] < base["attn_out_mse"]
+    for a, b in (("SAW-INT4 Bh128 (token scale)", "SAW-INT4 Bh128 + scale search"),
+                 ("INT4 Bh32, scale per block", "INT4 Bh32, scale per block + search")):
+        assert variant_reports[b]["k_mse_all"] <= variant_reports[a]["k_mse_all"]
