@@ -167,6 +167,27 @@ def time_calls(fn, iters, warmup):
     return mean, ts[len(ts) // 2]
 
 
+def time_calls_cold(fn, iters, dev, flush_bytes=1 << 30):
+    """Mean GPU time (ms) of fn() with the last-level cache (256 MB MALL)
+    flushed before every call by writing flush_bytes of another buffer;
+    events bracket fn() alone."""
+    import torch
+    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    fn()
+    evs = []
+    for _ in range(iters):
+        junk.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del junk
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / iters
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload: the
     first S sequences' append + decode, timed on the host cores."""
@@ -246,6 +267,11 @@ def main(argv=None):
                     help="only the fp16 baseline decode on the main workload, one JSON line")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the causal prefill attention over a 32,768-token prompt, one JSON line")
+    ap.add_argument("--c3-only", action="store_true",
+                    help="only the batch-1, 32K-context, 36-layer decode step, one JSON line")
+    ap.add_argument("--no-graph", action="store_true", help="with --c3-only: no HIP-graph timing")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="only the quantizer-variant measurements, one JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB streaming kernel (counter calibration under rocprofv3 --pmc)")
@@ -271,6 +297,15 @@ def main(argv=None):
     if args.fp16_only:
         print(json.dumps({"decode_fp16_c4": fp16_measurement(dev, iters=args.steps, warmup=args.warmup)}),
               flush=True)
+        return 0
+
+    if args.c3_only:
+        print(json.dumps({"decode_b1_32k_36layers": c3_measurement(dev, iters=args.steps, warmup=args.warmup,
+                                                                   with_graph=not args.no_graph)}), flush=True)
+        return 0
+
+    if args.variants_only:
+        print(json.dumps({"variants": variant_measurements(dev, iters=args.steps, warmup=args.warmup)}), flush=True)
         return 0
 
     if args.prefill_only:
@@ -439,7 +474,7 @@ def append_measurements(dev, iters=20, warmup=3, with_decode_time=True):
     pt = torch.as_tensor(w.page_table, device=dev)
     T = int(w.append_seq.size)
     nb = append_bytes(T, w.num_kv_heads)
-    for bh in (64, 0):
+    for bh in (64, 0, 128, 32):
         ms, med = time_calls(lambda: kvq.kv_quant_append(k, v, seq, pos, pt, kp, vp, w.page_size, bh), iters, warmup)
         ex[f"append_65536tok_bh{bh}"] = {"ms": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
                                          "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
@@ -464,7 +499,15 @@ def append_measurements(dev, iters=20, warmup=3, with_decode_time=True):
     nb3 = append_bytes(L3, w3.num_kv_heads)
     ex["append_prompt_32768tok_bh128"] = {"ms": round(ms, 5), "tokens_per_s": round(L3 / (ms * 1e-3), 1),
                                           "GBps": round(nb3 / (ms * 1e-3) / 1e9, 2),
-                                          "pct_of_hbm_peak": round(100 * nb3 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+                                          "pct_of_hbm_peak": round(100 * nb3 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                          "timing": "back to back: the ~169 MB working set may stay in the "
+                                                    "256 MB last-level cache"}
+    ms_c = time_calls_cold(lambda: kvq.kv_quant_append(k3, v3, s3, p3, pt3, kp3, vp3, w3.page_size, w3.had_block),
+                           iters, dev)
+    ex["append_prompt_32768tok_bh128_cold"] = {
+        "ms": round(ms_c, 5), "GBps": round(nb3 / (ms_c * 1e-3) / 1e9, 2),
+        "pct_of_hbm_peak": round(100 * nb3 / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "timing": "1 GiB written to another buffer before each call (last-level cache flushed)"}
     del kp3, vp3, k3, v3
     # decode-time append (1 token per sequence)
     w2 = wl.c2()
@@ -505,7 +548,96 @@ def extra_measurements(dev, args):
         torch.cuda.empty_cache()
     ex["rotation_overhead_pct"] = round(100 * (rot[128] / rot[0] - 1), 2)
 
-    # Latency-sensitive: batch 1, 32K context, 36 layers with distinct pools.
+    ex["decode_b1_32k_36layers"] = c3_measurement(dev)
+
+    ex["decode_fp16_c4"] = fp16_measurement(dev, iters=10, warmup=2)
+    ex["prefill_b1_32k"] = prefill_measurement(dev, iters=5, warmup=1)
+    ex["variants"] = variant_measurements(dev)
+    return ex
+
+
+# (name, format, had_block, scale_group, scale_search, sign_mask)
+VARIANT_CFGS = [
+    ("int4_bh32_scale_per_block", 0, 32, 32, 0, 0),
+    ("int4_bh32_scale_per_block_search", 0, 32, 32, 1, 0),
+    ("int4_bh64_scale_per_block", 0, 64, 64, 0, 0),
+    ("int4_bh128_token_scale_random_signs", 0, 128, 128, 0, 0x9E3779B97F4A7C15F39CC0605CEDC834),
+    ("mxfp4_bh32", 1, 32, 32, 0, 0),
+    ("mxfp4_bh128", 1, 128, 32, 0, 0),
+]
+
+
+def variant_measurements(dev, iters=10, warmup=2):
+    """The quantizer variants (per-block INT4 scales, scale search, random
+    signs, MXFP4): append bandwidth on 65,536 tokens (256 sequences x 256
+    consecutive tokens, page size 16) and decode bandwidth at the
+    long-context shape (batch 8 x 131,072, page size 32) and the batch-256
+    shape, each as algorithmic bytes (codes + this format's scales)."""
+    import numpy as np
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
+    res = {}
+    w2 = wl.c2_stream()
+    k, v = w2.append_rows(0, dev)
+    seq = torch.as_tensor(w2.append_seq, device=dev)
+    pos = torch.as_tensor(w2.append_pos, device=dev)
+    pt2 = torch.as_tensor(w2.page_table, device=dev)
+    T = int(w2.append_seq.size)
+    for name, *args in VARIANT_CFGS:
+        cfg = kvq.quant_config(*args)
+        tb = kvq.page_tile_bytes_cfg(128, 16, cfg)
+        per = 2 * tb // 16                    # K and V bytes per token-head
+        kp = torch.zeros((w2.num_pages, 8, tb), dtype=torch.uint8, device=dev)
+        vp = torch.zeros_like(kp)
+        ms, _ = time_calls(lambda: kvq.kv_quant_append_cfg(k, v, seq, pos, pt2, kp, vp, 16, cfg), iters, warmup)
+        nb = T * 8 * (2 * 256 + per) + T * 12
+        res[name] = {"bytes_per_token_head": per,
+                     "append_65536tok": {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                                         "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}}
+        del kp, vp
+    del k, v
+    torch.cuda.empty_cache()
+    for wname, w in (("decode_8x128k", wl.c5()), ("decode_c4", wl.c4())):
+        pt = torch.as_tensor(w.table(0), device=dev)
+        cl = torch.as_tensor(w.context_lens, device=dev)
+        q = w.query(0, dev)
+        maxctx = int(w.context_lens.max())
+        out = torch.empty((w.batch, 32, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty(kvq.workspace_bytes(w.batch, 32, 8, maxctx, w.page_size), dtype=torch.uint8, device=dev)
+        ctx = np.maximum(w.context_lens.astype(np.int64), 0)
+        for name, *args in VARIANT_CFGS:
+            cfg = kvq.quant_config(*args)
+            tb = kvq.page_tile_bytes_cfg(128, w.page_size, cfg)
+            per = 2 * tb // w.page_size
+            kp = torch.zeros((w.num_pages, 8, tb), dtype=torch.uint8, device=dev)
+            vp = torch.zeros_like(kp)
+            for b in range(w.batch):
+                L = int(w.prefill_lens[b])
+                kk, vv = w.rows(0, b, 0, L, dev)
+                kvq.kv_quant_append_cfg(kk, vv, torch.full((L,), b, dtype=torch.int32, device=dev),
+                                        torch.arange(L, dtype=torch.int32, device=dev), pt, kp, vp, w.page_size, cfg)
+            ms, _ = time_calls(lambda: kvq.paged_decode_attn_cfg(q, kp, vp, pt, cl, 8, w.page_size, cfg,
+                                                                 w.softmax_scale, maxctx, out=out, workspace=ws),
+                               iters, warmup)
+            nb = int(ctx.sum()) * 8 * per + int(((ctx + w.page_size - 1) // w.page_size).sum()) * 4 \
+                + w.batch * 32 * 128 * 6
+            res[name][wname] = {"ms": round(ms, 5), "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                                "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+            del kp, vp
+            torch.cuda.empty_cache()
+    return res
+
+
+def c3_measurement(dev, iters=10, warmup=2, with_graph=True):
+    """Latency-sensitive decode: batch 1, 32K context, 36 layers with distinct
+    pools and page permutations (Hadamard block 128, page size 16); the
+    36-layer step timed eagerly and as one HIP graph (replays checked bit for
+    bit against the eager step)."""
+    import torch
+    import bit_kv_cache_quant_amd as kvq
+    import workloads as wl
+    ex = {}
     w3 = wl.c3()
     caches = [build_int4_cache(w3, dev, layer=l) for l in range(w3.layers)]
     qs = [w3.query(l, dev) for l in range(w3.layers)]
@@ -518,11 +650,15 @@ def extra_measurements(dev, args):
             kpl, vpl, ptl = caches[l]
             kvq.paged_decode_attn_int4(qs[l], kpl, vpl, ptl, cl, 8, 16, 128, w3.softmax_scale, 32768,
                                        out=out, workspace=ws)
-    ms, med = time_calls(all_layers, 10, 2)
+    ms, med = time_calls(all_layers, iters, warmup)
     nb = decode_bytes(w3) * w3.layers
     ex["decode_b1_32k_36layers"] = {"ms_per_step": round(ms, 5), "us_per_layer": round(1000 * ms / w3.layers, 3),
                                     "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
                                     "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    if not with_graph:
+        del caches
+        torch.cuda.empty_cache()
+        return ex["decode_b1_32k_36layers"]
     # The same 36-layer step captured once in a HIP graph and replayed; every
     # checked replay must give the eager step's output, with eager work and
     # synchronisations in between.
@@ -547,7 +683,7 @@ def extra_measurements(dev, args):
             raise RuntimeError("graph replay of the batch-1 decode step differs from the eager step")
         all_layers()
         torch.cuda.synchronize()
-    ms_g, _ = time_calls(graph.replay, 10, 2)
+    ms_g, _ = time_calls(graph.replay, iters, warmup)
     ex["decode_b1_32k_36layers"].update({"graph_ms_per_step": round(ms_g, 5),
                                          "graph_us_per_layer": round(1000 * ms_g / w3.layers, 3),
                                          "graph_pct_of_hbm_peak":
@@ -556,9 +692,7 @@ def extra_measurements(dev, args):
     del caches
     torch.cuda.empty_cache()
 
-    ex["decode_fp16_c4"] = fp16_measurement(dev, iters=10, warmup=2)
-    ex["prefill_b1_32k"] = prefill_measurement(dev, iters=5, warmup=1)
-    return ex
+    return ex["decode_b1_32k_36layers"]
 
 
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 matrix rate, published

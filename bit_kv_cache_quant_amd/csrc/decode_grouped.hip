@@ -1,7 +1,9 @@
 // Paged decode attention over a quantizer variant's cache: INT4 codes with
 // one fp16 scale per group of G channels (G = 32 or 64), or MXFP4 (E2M1
-// codes, one E8M0 scale per 32 channels); split-K partial kernel, on the
-// int8 matrix cores (v_mfma_i32_16x16x64_i8).
+// codes, one E8M0 scale per 32 channels); split-K partial kernel.  INT4 on
+// the int8 matrix cores (v_mfma_i32_16x16x64_i8); MXFP4's q.k on gfx950's
+// scaled FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4: keys straight
+// from the cache with their E8M0 scales), its p.v on the int8 ones.
 //
 // Method sources: "BitDecoding-FP4:FP4 KVキャッシュのネイティブ復号", section
 // 深掘り分析 (scales chosen per group after a Hadamard rotation) and its
@@ -25,11 +27,14 @@
 //         every group's partial dot product for 4 heads at once, and lane
 //         (g, j) receives rows (head g, groups 0..3) for token j.  INT4 keys
 //         enter as offset-binary nibbles (c + 8) with -8 sum(digits) per row
-//         as the accumulator's start; MXFP4 keys as the signed bytes 2 v
-//         (v the E2M1 value, so 2 v is an integer in [-12, 12]), mapped by a
-//         byte table.  Per group: (D0 2^8 + D1) exact in int32, then one fma
-//         with D2, times the group's key scale (fp16, or 2^(X-1) for MXFP4).
-//   p.v : per value group, P = p (value scale of the group) in 21-bit fixed
+//         as the accumulator's start.  Per group: (D0 2^8 + D1) exact in
+//         int32, then one fma with D2, times the group's fp16 key scale.
+//         MXFP4: see the set-up below (4-bit query digits as exact E4M3
+//         integers against the E2M1 keys, all scales in the instruction).
+//   p.v : values as INT4 offset-binary bytes, or MXFP4's signed bytes 2 v
+//         (v the E2M1 value, 2 v an integer in [-12, 12], by a byte table,
+//         with the scale 2^(X-1)); per value group, P = p (value scale of
+//         the group) in 21-bit fixed
 //         point relative to the group's largest P of the head in the chunk,
 //         three 7-bit limbs as in the token-wise kernel; groups are handed
 //         through LDS one after another.  The dims of MFMA m (16m..16m+15)
@@ -99,8 +104,25 @@ struct alignas(16) WaveValues {
 };
 typedef uint32_t QDigits[kH][3][2][4][4];   // [head][digit][parity][lane group][dword]
 struct alignas(16) WaveQuery {
-    QDigits qd;
+    union {
+        QDigits qd;                 // INT4 groups: 8-bit digits in the A-operand order
+        int32_t qx[kH][kHeadDim];   // MXFP4: the fixed-point query X per (head, dim)
+    };
 };
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// E4M3 bytes of 4 integers 0..15 held one per byte: 0 -> 0x00, 1 -> 0x38,
+// 2 -> 0x40, 3 -> 0x44, 4 -> 0x48, 5 -> 0x4A, 6 -> 0x4C, 7 -> 0x4E, 8 -> 0x50,
+// 9 .. 15 -> 0x51 .. 0x57 (exact: at most 4 significant bits).
+__device__ __forceinline__ uint32_t e4m3_of_small(uint32_t b) {
+    const uint32_t sel = b & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(0x57565554u, 0x53525150u, sel);
+    const uint32_t t = b & 0x08080808u;
+    const uint32_t m = (t << 5) - (t >> 3);   // 0xFF where the value is 8 or more
+    return (hi & m) | (lo & ~m);
+}
 struct alignas(16) WavePfix {
     uint32_t pfix[kH][kPfixPitch];
 };
@@ -297,7 +319,16 @@ __device__ __forceinline__ PartialState decode_range_grouped(const DecodeArgs &a
     if (amax > 0.0f) (void)frexpf(amax * 1.0078125f, &qexp);   // |X| < 127 (2^16 + 2^8 + 1)
     const float qmul = ldexpf(1.0f, 23 - qexp);
     int dsum[3] = {0, 0, 0};   // this lane's digit sums (its 8 dims lie in one scale group)
-    {
+    if constexpr (FMT == KVQ_FMT_MXFP4) {
+        // the fixed-point query to LDS, per (head, dim)
+        int4 xv0, xv1;
+        xv0.x = static_cast<int>(rintf(qv[0] * qmul)); xv0.y = static_cast<int>(rintf(qv[1] * qmul));
+        xv0.z = static_cast<int>(rintf(qv[2] * qmul)); xv0.w = static_cast<int>(rintf(qv[3] * qmul));
+        xv1.x = static_cast<int>(rintf(qv[4] * qmul)); xv1.y = static_cast<int>(rintf(qv[5] * qmul));
+        xv1.z = static_cast<int>(rintf(qv[6] * qmul)); xv1.w = static_cast<int>(rintf(qv[7] * qmul));
+        *reinterpret_cast<int4 *>(&sq.qx[g][8 * j]) = xv0;
+        *reinterpret_cast<int4 *>(&sq.qx[g][8 * j + 4]) = xv1;
+    } else {
         uint32_t w[3][2] = {{0, 0}, {0, 0}, {0, 0}};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -337,10 +368,48 @@ __device__ __forceinline__ PartialState decode_range_grouped(const DecodeArgs &a
     }
     const float score_mul = ldexpf(a.score_scale, qexp - 23);
     wave_lds_sync();
-    // A operands: row j = (head j/4, group j%4); lane group g's dims belong to
-    // group g / (G/32)
+    // MXFP4: q.k on the scaled FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4):
+    // B = the keys' E2M1 codes as stored (lane (g, j): token j, dims 32g ..
+    // 32g + 31) with their E8M0 block scales; A = the query's 24-bit X in six
+    // 4-bit digits, X = sum_{d<5} u_d 2^(4d) + t 2^20 (u_d in [0, 15], t in
+    // [-8, 7]), one row per (head, digit), each digit an exact E4M3 integer and
+    // its weight 2^(4d + E - 23) in the row's E8M0 scale; A's byte order
+    // (established by a layout probe): bytes 0-15 are dims 16g .. 16g + 15,
+    // bytes 16-31 dims 64 + 16g .. 64 + 16g + 15.  MFMA u holds digits 4u +
+    // (j % 4) of head j / 4 (rows with digit 6 or 7 are zero); the scores are
+    // the sums of a head's digit rows.
+    v8i qf[2];
+    int qsa[2];
+    if constexpr (FMT == KVQ_FMT_MXFP4) {
+        const int hh = j >> 2;
+        const int eh = __shfl(qexp, 16 * hh);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int d = 4 * u + (j & 3);
+            qsa[u] = d < 6 ? 127 + 4 * d + eh - 23 : 127;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int4 *src = reinterpret_cast<const int4 *>(&sq.qx[hh][64 * half + 16 * g]);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int4 x = src[q4];
+                    const int xs[4] = {x.x, x.y, x.z, x.w};
+                    uint32_t mag = 0, neg = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        int v = d < 5 ? ((xs[e] >> (4 * d)) & 15) : (d == 5 ? (xs[e] >> 20) : 0);
+                        neg |= (v < 0 ? 0x80u : 0u) << (8 * e);
+                        mag |= static_cast<uint32_t>(v < 0 ? -v : v) << (8 * e);
+                    }
+                    qf[u][4 * half + q4] = static_cast<int>(e4m3_of_small(mag) | neg);
+                }
+            }
+        }
+    }
+    // INT4 groups: A operands with row j = (head j/4, group j%4); lane group
+    // g's dims belong to group g / (G/32)
     v4i qa[3][2];
-    {
+    if constexpr (FMT == KVQ_FMT_INT4) {
         const bool mine = (j & 3) == g / kLaneGroupsPerGroup;
 #pragma unroll
         for (int d = 0; d < 3; ++d)
@@ -385,6 +454,17 @@ __device__ __forceinline__ PartialState decode_range_grouped(const DecodeArgs &a
         float zmax = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            if constexpr (FMT == KVQ_FMT_MXFP4) {
+                const v8i bk = {(int)cd.k[t].x, (int)cd.k[t].y, (int)cd.k[t].z, (int)cd.k[t].w, 0, 0, 0, 0};
+                const int sb = (int)__builtin_amdgcn_ubfe(ks[0][t], 8 * g, 8);   // E8M0 of (token j, block g)
+                const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                const v4f d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[0], bk, zero4, 0, 4, 0, qsa[0], 0, sb);
+                const v4f d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[1], bk, zero4, 0, 4, 0, qsa[1], 0, sb);
+                const float sc = (((d0[0] + d0[1]) + (d0[2] + d0[3])) + (d1[0] + d1[1])) * a.score_scale;
+                z[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? sc : -INFINITY;
+                zmax = fmaxf(zmax, z[t]);
+                continue;
+            }
             uint32_t lo[4], hi[4];
             split_codes<FMT>(cd.k[t].x, lo[0], hi[0]);
             split_codes<FMT>(cd.k[t].y, lo[1], hi[1]);

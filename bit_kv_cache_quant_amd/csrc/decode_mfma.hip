@@ -575,6 +575,77 @@ __global__ __launch_bounds__(kThreads) void decode_int4_mfma_kernel(DecodeArgs a
                   ((int64_t)it.b * a.num_q_heads + qh0) * a.num_splits + it.s, a.num_splits);
 }
 
+// Split mode with few work items (small batches, long contexts): each page
+// range is shared by WPR waves of one block, each taking a consecutive part
+// of its chunks, and their partial states are merged in LDS before the one
+// write to the workspace.  A range's chunks then stream in parallel instead
+// of one after another behind a single wave (with one wave per SIMD, every
+// chunk of a range exposed a whole memory latency), while the number of
+// partial states the merge kernel reads stays that of the plain split.
+template <int BH, int P, int WPR>
+__global__ __launch_bounds__(kThreads * WPR) void decode_int4_wide_kernel(DecodeArgs a) {
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wid % kWaves;        // head slot of the block's quad
+    const int part = wid / kWaves;        // part of the range
+    const int lane = threadIdx.x & 63;
+    const SplitItem it = split_item<P>(a, wave);
+    struct WideDecode {
+        WaveValues values[kWaves * WPR];
+    };
+    struct WideMerge {
+        float o[kWaves * WPR][8][64];
+        float ml[kWaves * WPR][2][64];
+    };
+    union WideShared {
+        WideDecode dec;
+        WideMerge mrg;
+    };
+    __shared__ WideShared sh;
+    __shared__ WavePfix pfix[kWaves * WPR];
+    __shared__ WaveQuery query[kWaves * WPR];
+    constexpr int kChunkPages = kChunk / P;
+    PartialState st;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.o[m] = 0.0f;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    if (it.live) {
+        const int nch = (it.p1 - it.p0 + kChunkPages - 1) / kChunkPages;
+        const int c0 = part * nch / WPR, c1 = (part + 1) * nch / WPR;
+        if (c0 < c1)
+            st = decode_range<BH, P>(a, sh.dec.values[wid], pfix[wid], query[wid], lane, it.b, it.hk, it.chunk_id,
+                                     it.L, it.p0 + c0 * kChunkPages, min(it.p0 + c1 * kChunkPages, it.p1));
+    }
+    __syncthreads();   // every wave is done with its value buffer: the merge space overlays them
+#pragma unroll
+    for (int m = 0; m < 8; ++m) sh.mrg.o[wid][m][lane] = st.o[m];
+    sh.mrg.ml[wid][0][lane] = st.m;
+    sh.mrg.ml[wid][1][lane] = st.l;
+    __syncthreads();
+    if (part != 0 || !it.live) return;
+    // merge the WPR parts of this head slot (a part with no chunk has max -inf)
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) M = fmaxf(M, sh.mrg.ml[w * kWaves + wave][0][lane]);
+    PartialState r;
+    r.m = M;
+    r.l = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) r.o[m] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) {
+        const int src = w * kWaves + wave;
+        const float mw = sh.mrg.ml[src][0][lane];
+        const float f = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
+        r.l = fmaf(sh.mrg.ml[src][1][lane], f, r.l);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) r.o[m] = fmaf(sh.mrg.o[src][m][lane], f, r.o[m]);
+    }
+    const int qh0 = it.hk * a.group + it.chunk_id * kH;
+    write_partial(a, r, lane, min(kH, a.group - it.chunk_id * kH),
+                  ((int64_t)it.b * a.num_q_heads + qh0) * a.num_splits + it.s, a.num_splits);
+}
+
 // Balanced mode (batch 16..4096): equal ranges of the batch's concatenated
 // chunks (dec::balanced_range); the block walks every sequence its range
 // meets, so every block streams the same amount of cache whatever the mix of
@@ -657,12 +728,16 @@ hipError_t launch_decode_int4_mfma(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid = balanced ? dim3((unsigned)(quads * a.sk_groups), 1, 1)
                                : dim3((unsigned)(a.batch * quads), (unsigned)a.num_splits, 1);
     const dim3 block(kThreads);
-#define KVQ_LAUNCH(BHV, PV)                                                                       \
-    do {                                                                                          \
-        if (balanced)                                                                             \
-            hipLaunchKernelGGL((decode_int4_balanced_kernel<BHV, PV>), grid, block, 0, stream, a); \
-        else                                                                                      \
-            hipLaunchKernelGGL((decode_int4_mfma_kernel<BHV, PV>), grid, block, 0, stream, a);     \
+#define KVQ_LAUNCH(BHV, PV)                                                                                  \
+    do {                                                                                                     \
+        if (balanced)                                                                                        \
+            hipLaunchKernelGGL((decode_int4_balanced_kernel<BHV, PV>), grid, block, 0, stream, a);            \
+        else if (a.range_waves == 4)                                                                         \
+            hipLaunchKernelGGL((decode_int4_wide_kernel<BHV, PV, 4>), grid, dim3(4 * kThreads), 0, stream, a); \
+        else if (a.range_waves == 2)                                                                         \
+            hipLaunchKernelGGL((decode_int4_wide_kernel<BHV, PV, 2>), grid, dim3(2 * kThreads), 0, stream, a); \
+        else                                                                                                 \
+            hipLaunchKernelGGL((decode_int4_mfma_kernel<BHV, PV>), grid, block, 0, stream, a);                \
     } while (0)
     if (a.page_size == 16) {
         switch (a.had_block) {

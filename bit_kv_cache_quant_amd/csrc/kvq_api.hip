@@ -51,6 +51,10 @@ bool valid_cfg(const kvq_quant_config *c) {
     return false;
 }
 
+bool grouped_cfg(const kvq_quant_config *c) {
+    return c && (c->format != KVQ_FORMAT_INT4 || c->scale_group != kHeadDim);
+}
+
 size_t scale_bytes_cfg(const kvq_quant_config *c) {
     return (size_t)(kHeadDim / c->scale_group) * (c->format == KVQ_FORMAT_MXFP4 ? 1 : 2);
 }
@@ -326,6 +330,16 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.had_block = int4 ? had_block : 0;
     a.pages_per_split = pps;
     a.num_splits = nsplit;
+    // Split mode with at most about one block per CU: share each range among
+    // 4 waves of a block (2 for up to two blocks per CU); the INT4 token-wise
+    // kernel only.  KVQ_RANGE_WAVES=1/2/4 overrides (measurement).
+    a.range_waves = 1;
+    if (!balanced && int4 && !grouped_cfg(cfg)) {
+        const int64_t blocks = (int64_t)batch * ((num_kv_heads * chunks + 3) / 4) * nsplit;
+        a.range_waves = blocks <= 256 ? 4 : (blocks <= 512 ? 2 : 1);
+        const char *e = getenv("KVQ_RANGE_WAVES");
+        if (e && (e[0] == '1' || e[0] == '2' || e[0] == '4') && e[1] == 0) a.range_waves = e[0] - '0';
+    }
     a.score_scale = softmax_scale * 1.4426950408889634f;
     const bool grouped = int4 && (a.format != KVQ_FORMAT_INT4 || a.scale_group != kHeadDim);
     hipError_t e = !int4 ? kvq::launch_decode_fp16(a, st)

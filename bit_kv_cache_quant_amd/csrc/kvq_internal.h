@@ -63,6 +63,7 @@ struct DecodeArgs {
     int32_t had_block;
     int32_t pages_per_split;
     int32_t num_splits;
+    int32_t range_waves;       // split mode: waves sharing one page range in a block (1, 2 or 4)
     float score_scale;         // softmax_scale * log2(e): scores are kept in log2 units
     // Quantizer variant of the cache: KVQ_FMT_*, channels per scale, and the
     // sign mask of the randomized Hadamard (bit i: channel i negated before

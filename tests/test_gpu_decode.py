@@ -223,3 +223,32 @@ def test_decode_context_len_above_max_is_clamped(dev, lens):
     want = oracle.paged_decode_attn_int4(q.cpu().numpy(), hk, hv, w.table(0), clamped, w.num_kv_heads,
                                          w.page_size, w.had_block, w.softmax_scale)
     _assert_close(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("lens,page_size,had_block", [([2100, 700, 1], 16, 128), ([300] * 9, 32, 64),
+                                                      ([4096], 16, 0)])
+def test_decode_range_shared_by_waves(dev, lens, page_size, had_block, monkeypatch):
+    """Split mode with few work items: a page range shared by 1, 2 or 4 waves
+    of one block (their partial states merged in LDS) gives the oracle's
+    result, and the three agree to fp32 reordering."""
+    w = wl.small(len(lens), lens, had_block, page_size, cfg_id=180 + page_size + had_block)
+    kp, vp = int4_pools(w, dev)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    prefill(w, 0, dev, kp, vp, had_block, host_pools=(hk, hv))
+    q = w.query(0, dev)
+    pt = torch.as_tensor(w.table(0), device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    want = oracle.paged_decode_attn_int4(q.cpu().numpy(), hk, hv, w.table(0), w.context_lens, w.num_kv_heads,
+                                         page_size, had_block, w.softmax_scale)
+    outs = {}
+    for wpr in ("1", "2", "4"):
+        monkeypatch.setenv("KVQ_RANGE_WAVES", wpr)
+        say(f"range waves {wpr}: B={w.batch} P={page_size} bh={had_block}")
+        o = kvq.paged_decode_attn_int4(q, kp, vp, pt, cl, w.num_kv_heads, page_size, had_block, w.softmax_scale,
+                                       int(max(lens)))
+        torch.cuda.synchronize()
+        outs[wpr] = o.cpu().numpy()
+        _assert_close(outs[wpr], want)
+    bound = 1e-5 * max(1.0, float(np.max(np.abs(outs["1"]))))
+    assert np.max(np.abs(outs["2"] - outs["1"])) <= bound
+    assert np.max(np.abs(outs["4"] - outs["1"])) <= bound
