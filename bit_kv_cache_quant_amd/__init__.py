@@ -58,6 +58,8 @@ SIGNATURES = {
     "paged_decode_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attn_int4": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _F32, _P, _P, _SZ, _I32, _P, _P]),
+    "paged_decode_step_int4": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
+                                              _I32, _I32, _I32, _F32, _P, _P, _SZ, _I32, _P, _P]),
     "paged_prefill_attn_int4": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                _I32, _I32, _F32, _P, _P]),
     "kvq_page_tile_bytes_cfg": (_SZ, [_I32, _I32, _CFG]),
@@ -224,9 +226,14 @@ def _event_handle(event):
 
 def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
             page_size: int, had_block: int, softmax_scale: float, max_context_len: int,
-            out=None, workspace=None, pages_per_split: int = 0, phase_event=None, cfg=None):
+            out=None, workspace=None, pages_per_split: int = 0, phase_event=None, cfg=None,
+            k_new=None, v_new=None):
     import torch
     B, hq, d = q.shape
+    if k_new is not None:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t is None or tuple(t.shape) != (B, int(num_kv_heads), d):
+                raise ValueError(f"{name} must be [{B}][{num_kv_heads}][{d}]")
     if cfg is not None:
         want = (int(num_kv_heads), page_tile_bytes_cfg(d, int(page_size), cfg))
     elif int4:
@@ -250,7 +257,10 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
         raise ValueError(f"workspace must be on {q.device}, got {workspace.device}")
     ws_bytes = workspace.numel()
     pool_dtype = torch.uint8 if int4 else torch.float16
-    args = [_dev(q, torch.float16, "q", 3), _dev(k_pool, pool_dtype, "k_pool"),
+    args = [_dev(q, torch.float16, "q", 3)]
+    if k_new is not None:
+        args += [_dev(k_new, torch.float16, "k_new", 3), _dev(v_new, torch.float16, "v_new", 3)]
+    args += [_dev(k_pool, pool_dtype, "k_pool"),
             _dev(v_pool, pool_dtype, "v_pool"), k_pool.shape[0],
             _dev(page_table, torch.int32, "page_table", 2), page_table.shape[1],
             _dev(context_lens, torch.int32, "context_lens", 1), B, int(max_context_len), hq,
@@ -261,8 +271,11 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
         args.append(int(had_block))
     args += [float(softmax_scale), _dev(out, torch.float32, "out", 3), ws_ptr, ws_bytes,
              int(pages_per_split), _event_handle(phase_event), _stream(q)]
-    name = "paged_decode_attn_cfg" if cfg is not None else ("paged_decode_attn_int4" if int4
-                                                            else "paged_decode_attn_fp16")
+    if k_new is not None:
+        name = "paged_decode_step_int4"
+    else:
+        name = "paged_decode_attn_cfg" if cfg is not None else ("paged_decode_attn_int4" if int4
+                                                                else "paged_decode_attn_fp16")
     _check(getattr(lib(), name)(*args), name)
     return out
 
@@ -312,6 +325,18 @@ def paged_decode_attn_int4(q, k_pool, v_pool, page_table, context_lens, num_kv_h
     recorded between the split-K partial kernel and the merge."""
     return _decode(True, q, k_pool, v_pool, page_table, context_lens, num_kv_heads, page_size,
                    had_block, softmax_scale, max_context_len, out, workspace, pages_per_split, phase_event)
+
+
+def paged_decode_step_int4(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,
+                           page_size: int, had_block: int, softmax_scale: float, max_context_len: int,
+                           out=None, workspace=None, pages_per_split: int = 0, phase_event=None):
+    """One decode step with its append: the new token of sequence b
+    (k_new[b], v_new[b], fp16 [B][Hkv][D]) goes into the INT4 pools at
+    position context_lens[b] - 1, and attention runs over positions
+    0 .. context_lens[b] - 1; returns fp32 [B][Hq][D]."""
+    return _decode(True, q, k_pool, v_pool, page_table, context_lens, num_kv_heads, page_size,
+                   had_block, softmax_scale, max_context_len, out, workspace, pages_per_split, phase_event,
+                   k_new=k_new, v_new=v_new)
 
 
 def paged_decode_attn_fp16(q, k_pool, v_pool, page_table, context_lens, num_kv_heads: int,

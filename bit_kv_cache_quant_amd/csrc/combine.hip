@@ -19,6 +19,16 @@
 // sequence (batch 1, long context) 4 or 16 waves share one (sequence, head):
 // each merges every 4th (16th) split, and their states are merged once more
 // through LDS.
+//
+// Fused decode step (APPEND): each sequence's new last token arrives as fp16
+// K/V rows instead of being in the cache.  The partial kernels take it in
+// the range that ends at the sequence's last cached token; only a sequence
+// whose context is the new token alone reaches the merge without a partial
+// state.  For it the merge wave rotates and quantizes the rows with the
+// append's arithmetic (the same fp32 operations in the same order, so the
+// same codes and scale bit for bit), stores them in the cache (the unit of
+// the first query head of each KV head writes), and takes the token as the
+// only state: max = its score, sum = 1, output = its dequantized value row.
 #include "decode_common.h"
 
 namespace kvq {
@@ -79,22 +89,81 @@ __device__ __forceinline__ void add_round(const Round &r, const int base, const 
     M = Mr;
 }
 
+// The two results of v_permlane16_swap (SPAN 16) or v_permlane32_swap
+// (SPAN 32) applied to x: lo = the value x holds in the lower row (rows 0,
+// 2) or half of the lane's pair, hi = the upper one's.  (Copied to scalars
+// before any bit cast: a bit cast applied directly to an element of the
+// builtin's two-element vector reads element 0 for both.)
+template <int SPAN>
+__device__ __forceinline__ void swap_pair(float x, float &lo, float &hi) {
+    const uint32_t a = __builtin_bit_cast(uint32_t, x);
+    const auto r = SPAN == 16 ? __builtin_amdgcn_permlane16_swap(a, a, false, false)
+                              : __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    lo = __builtin_bit_cast(float, r0);
+    hi = __builtin_bit_cast(float, r1);
+}
+
+// Value of lane t ^ M (M = 1, 2, 4, ..., 32) without going through LDS:
+// DPP within rows of 16 lanes (quad permutes, and the row mirrors: lane i
+// of a row takes lane 15 - i, or 7 - i within each half row, so two of
+// them compose to xor 4 or xor 8), v_permlane16_swap across the two rows of
+// each half, v_permlane32_swap across the halves.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int t) {
+    const int x = __builtin_bit_cast(int, v);
+    if constexpr (M == 1) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+    } else if constexpr (M == 2) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+    } else if constexpr (M == 4) {   // xor 7 (half-row mirror), then xor 3
+        const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, true));
+    } else if constexpr (M == 8) {   // xor 15 (row mirror), then xor 7
+        const int y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, true));
+    } else {
+        static_assert(M == 16 || M == 32, "lane distance is a power of two below 64");
+        float lo, hi;
+        swap_pair<M>(v, lo, hi);
+        return (t & M) ? lo : hi;
+    }
+}
+
+// One butterfly stage of span 2M between lanes t and t ^ M on the pairs
+// (2t, 2t+1): the lower entry gets u + v, the upper one u - v (u the lower
+// entry's value), one fp32 rounding each.
+template <int M>
+__device__ __forceinline__ void lane_butterfly(float &y0, float &y1, int t) {
+    const bool upper = (t & M) != 0;
+    const float p0 = xor_lane<M>(y0, t);
+    const float p1 = xor_lane<M>(y1, t);
+    y0 = upper ? (p0 - y0) : (y0 + p0);
+    y1 = upper ? (p1 - y1) : (y1 + p1);
+}
+
+// The unnormalised block transform (spans 1 .. bh/2 in ascending order) of
+// 128 values held as (2t, 2t+1) by lane t; bh = 0 leaves them alone.
+__device__ __forceinline__ void fwht_pairs(float &y0, float &y1, int bh, int t) {
+#pragma clang fp contract(off)
+    if (bh <= 0) return;
+    const float u = y0 + y1, v = y0 - y1;   // span 1: inside the lane
+    y0 = u;
+    y1 = v;
+    if (bh > 2) lane_butterfly<1>(y0, y1, t);
+    if (bh > 4) lane_butterfly<2>(y0, y1, t);
+    if (bh > 8) lane_butterfly<4>(y0, y1, t);
+    if (bh > 16) lane_butterfly<8>(y0, y1, t);
+    if (bh > 32) lane_butterfly<16>(y0, y1, t);
+    if (bh > 64) lane_butterfly<32>(y0, y1, t);
+}
+
 // Inverse rotation of 128 values held as (2t, 2t+1) by lane t (S R: the
 // block rotation, then the sign mask), then store.
 __device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh, int t, const uint32_t (&mask)[4],
                                                       float *out) {
     if (bh > 0) {
-        float u = o0 + o1, v = o0 - o1;          // span 1: inside the lane
-        o0 = u;
-        o1 = v;
-        for (int span = 2; span < bh; span <<= 1) {
-            const int m = span >> 1;              // partner lane for dims 2t ^ span
-            const bool upper = (t & m) != 0;
-            const float p0 = __shfl_xor(o0, m);
-            const float p1 = __shfl_xor(o1, m);
-            o0 = upper ? (p0 - o0) : (o0 + p0);
-            o1 = upper ? (p1 - o1) : (o1 + p1);
-        }
+        fwht_pairs(o0, o1, bh, t);
         const float c = rsqrtf(static_cast<float>(bh));
         o0 *= c;
         o1 *= c;
@@ -105,9 +174,124 @@ __device__ __forceinline__ void rotate_back_and_store(float o0, float o1, int bh
     *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(o0, o1);
 }
 
+// ---- fused decode step: the new token ----
+
+// Wave-wide max and sum: rows of 16 by DPP, then across rows by the
+// permlane swaps (no LDS).  The max is exact in any order.
+__device__ __forceinline__ float wave_max(float v) {
+    float lo, hi;
+    swap_pair<16>(dec::row_max16(v), lo, hi);
+    swap_pair<32>(fmaxf(lo, hi), lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    float lo, hi;
+    swap_pair<16>(dec::row_sum16(v), lo, hi);
+    swap_pair<32>(lo + hi, lo, hi);
+    return lo + hi;
+}
+
+// fp32 nearest 1/sqrt(bh) for the supported blocks.
+__device__ __forceinline__ float block_scale(int bh) {
+    return __builtin_bit_cast(float, bh == 32 ? 0x3E3504F3u : bh == 64 ? 0x3E000000u : 0x3DB504F3u);
+}
+
+// Block rotation (transform, then the product with the fp32 nearest
+// 1/sqrt(bh)) of a 128-entry fp16 vector held as entries (2t, 2t+1) by lane
+// t, the entries widened exactly to fp32 first.
+__device__ __forceinline__ void rotate_pair(uint32_t w, int bh, int t, float &y0, float &y1) {
+#pragma clang fp contract(off)
+    y0 = dec::half_to_float(w);
+    y1 = dec::half_to_float(w >> 16);
+    if (bh <= 0) return;
+    fwht_pairs(y0, y1, bh, t);
+    const float c = block_scale(bh);
+    y0 = y0 * c;
+    y1 = y1 * c;
+}
+
+// Token-wise INT4 of the rotated entries (y0, y1) of lane t: m = max |y| over
+// the wave (exact), s = fp16(m / 7) (IEEE quotient, then round to nearest
+// even), code = clamp(rint(y / s), -8, 7) with the IEEE quotient (0 when s =
+// 0).  Gives the code byte of entries 2t (low nibble) and 2t + 1, the
+// dequantized entries code * s (exact) and the fp16 scale bits.
+struct NewRow {
+    uint32_t byte;
+    float d0, d1;
+    uint16_t s16;
+};
+__device__ __forceinline__ NewRow quantize_pair(float y0, float y1) {
+#pragma clang fp contract(off)
+    const float m = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
+    float s32 = m / 7.0f;
+    asm("" : "+v"(s32));   // two roundings (fp32, then fp16), as written
+    const _Float16 h = static_cast<_Float16>(s32);
+    const float s = static_cast<float>(h);
+    float c0 = 0.0f, c1 = 0.0f;
+    if (s > 0.0f) {
+        c0 = fminf(fmaxf(rintf(y0 / s), -8.0f), 7.0f);
+        c1 = fminf(fmaxf(rintf(y1 / s), -8.0f), 7.0f);
+    }
+    NewRow r;
+    r.byte = (static_cast<uint32_t>(static_cast<int>(c0)) & 15u) |
+             ((static_cast<uint32_t>(static_cast<int>(c1)) & 15u) << 4);
+    r.d0 = c0 * s;
+    r.d1 = c1 * s;
+    r.s16 = __builtin_bit_cast(uint16_t, h);
+    return r;
+}
+
+// The new token of one (sequence, query head): its K and V rows quantized,
+// and its score against the query (log2 units).
+struct NewToken {
+    NewRow k, v;
+    float z;
+};
+__device__ __forceinline__ NewToken new_token(uint32_t kw, uint32_t vw, uint32_t qw, int bh, float score_scale,
+                                              int t) {
+    float k0, k1, v0, v1, q0, q1;
+    rotate_pair(kw, bh, t, k0, k1);
+    rotate_pair(vw, bh, t, v0, v1);
+    rotate_pair(qw, bh, t, q0, q1);
+    NewToken n;
+    n.k = quantize_pair(k0, k1);
+    n.v = quantize_pair(v0, v1);
+    n.z = wave_sum(fmaf(q0, n.k.d0, q1 * n.k.d1)) * score_scale;
+    return n;
+}
+
+// Folds the new token into (M, lsum, o0, o1) as one more partial state:
+// max z, sum 1, output its value row.
+__device__ __forceinline__ void fold(const NewToken &n, float &M, float &lsum, float &o0, float &o1) {
+    const float Mn = fmaxf(M, n.z);
+    const float corr = M == -INFINITY ? 0.0f : dec::fast_exp2(M - Mn);
+    const float w = dec::fast_exp2(n.z - Mn);
+    lsum = fmaf(lsum, corr, w);
+    o0 = fmaf(o0, corr, n.v.d0 * w);
+    o1 = fmaf(o1, corr, n.v.d1 * w);
+    M = Mn;
+}
+
+// Stores the new token's codes and scales at slot `slot` of page `page` for
+// KV head hk (the append's page layout).
+__device__ __forceinline__ void store_new_token(const DecodeArgs &a, const NewToken &n, int32_t page, int slot,
+                                                int hk, int t) {
+    const int64_t page_off = (int64_t)page * a.num_kv_heads * a.tile_bytes;
+    const int64_t row = (int64_t)hk * a.page_size + slot;
+    const int64_t scale_off = (int64_t)a.num_kv_heads * a.page_size * kCodeBytesPerRow + row * 2;
+    uint8_t *kp = static_cast<uint8_t *>(const_cast<void *>(a.k_pool)) + page_off;
+    uint8_t *vp = static_cast<uint8_t *>(const_cast<void *>(a.v_pool)) + page_off;
+    kp[row * kCodeBytesPerRow + t] = static_cast<uint8_t>(n.k.byte);
+    vp[row * kCodeBytesPerRow + t] = static_cast<uint8_t>(n.v.byte);
+    if (t == 0) {
+        *reinterpret_cast<uint16_t *>(kp + scale_off) = n.k.s16;
+        *reinterpret_cast<uint16_t *>(vp + scale_off) = n.v.s16;
+    }
+}
+
 // NW = 1: 4 units per block, one wave each.  NW = 4 or 16: one unit per block,
 // NW waves each merging every NW-th split.
-template <int NW>
+template <int NW, bool APPEND>
 __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(DecodeArgs a, int rotate_back) {
     constexpr bool WIDE = NW > 1;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loads below
@@ -117,35 +301,52 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
     const int b = unit / a.num_q_heads;
     float *out = a.out + (int64_t)unit * kHeadDim;
     const int qh = unit - b * a.num_q_heads;
+    const int hk = qh / a.group;
     const int s0 = WIDE ? wave : 0, step = WIDE ? NW : 1;
-    int nsplit, limit;
+    const int bh = rotate_back ? a.had_block : 0;
+
+    // Fused step: a sequence whose context is the new token alone has no
+    // partial state (the partial kernels take each sequence's new token in
+    // the range that ends at its last cached token); its rows and slot are
+    // loaded first.
+    int Lnew = 0;
+    uint32_t kw = 0, vw = 0, qw = 0;
+    int32_t page = 0;
+    if constexpr (APPEND) {
+        Lnew = full_len(a, b);
+        if (Lnew == 1) {
+            kw = reinterpret_cast<const uint32_t *>(a.k_new + ((int64_t)b * a.num_kv_heads + hk) * kHeadDim)[t];
+            vw = reinterpret_cast<const uint32_t *>(a.v_new + ((int64_t)b * a.num_kv_heads + hk) * kHeadDim)[t];
+            qw = reinterpret_cast<const uint32_t *>(a.q + ((int64_t)b * a.num_q_heads + qh) * kHeadDim)[t];
+            page = a.page_table[(int64_t)b * a.max_pages_per_seq + ((Lnew - 1) >> a.page_shift)];
+        }
+    }
+
+    int nsplit = 0, limit = 1;
     Round r0;   // the first round of this wave's states
-    const float *ml, *po;
+    const float *ml = a.ws_ml, *po = a.ws_o;
     if (a.sk_groups > 0) {
         // Balanced decode: the partial states of (b, qh) come from the ranges
         // g_first .. g_last that meet sequence b, at positions
         // ((quad * 4 + wave) * 4 + head) * (sk_groups + batch) + g + b.  A
-        // sequence with no chunks (context length <= 0) has none.
+        // sequence with no chunks has none.
         const int tot = a.sk_prefix[a.batch];
         const int pb = a.sk_prefix[b], pb1 = a.sk_prefix[b + 1];
-        if (pb1 == pb || tot <= 0) {   // (tot > 0 whenever pb1 > pb: the test only orders the loads)
-            if (!WIDE || wave == 0) *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
-            return;
+        if (pb1 > pb && tot > 0) {   // (tot > 0 whenever pb1 > pb: the test only orders the loads)
+            const int G = balanced_groups(a.sk_min, a.sk_target, tot);
+            const int g_first = (int)((((int64_t)pb + 1) * G - 1) / tot);
+            const int g_last = (int)(((int64_t)pb1 * G - 1) / tot);
+            const int chunk_id = (qh - hk * a.group) / kHeadsPerChunk;
+            const int slot = hk * a.head_chunks + chunk_id;
+            const int local = (slot % kWaves) * kHeadsPerChunk + (qh - hk * a.group) % kHeadsPerChunk;
+            nsplit = g_last - g_first + 1;
+            limit = nsplit;
+            const int64_t first =
+                ((int64_t)(slot / kWaves) * kWaves * kHeadsPerChunk + local) * (a.sk_groups + a.batch) + g_first + b;
+            ml = a.ws_ml + first * 2;
+            po = a.ws_o + first * kHeadDim;
+            r0 = load_round(ml, po, s0, step, limit, t);
         }
-        const int G = balanced_groups(a.sk_min, a.sk_target, tot);
-        const int g_first = (int)((((int64_t)pb + 1) * G - 1) / tot);
-        const int g_last = (int)(((int64_t)pb1 * G - 1) / tot);
-        const int hk = qh / a.group;
-        const int chunk_id = (qh - hk * a.group) / kHeadsPerChunk;
-        const int slot = hk * a.head_chunks + chunk_id;
-        const int local = (slot % kWaves) * kHeadsPerChunk + (qh - hk * a.group) % kHeadsPerChunk;
-        nsplit = g_last - g_first + 1;
-        limit = nsplit;
-        const int64_t first =
-            ((int64_t)(slot / kWaves) * kWaves * kHeadsPerChunk + local) * (a.sk_groups + a.batch) + g_first + b;
-        ml = a.ws_ml + first * 2;
-        po = a.ws_o + first * kHeadDim;
-        r0 = load_round(ml, po, s0, step, limit, t);
     } else {
         // Split mode: the unit owns num_splits positions, the first nsplit of
         // them written (none if the context is empty); the first round of
@@ -159,12 +360,17 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         const int npages = (L + a.page_size - 1) >> a.page_shift;
         nsplit = L > 0 ? (npages + a.pages_per_split - 1) / a.pages_per_split : 0;
     }
-    const int bh = rotate_back ? a.had_block : 0;
+    NewToken nt{};
+    if constexpr (APPEND) {
+        if (Lnew == 1) nt = new_token(kw, vw, qw, a.had_block, a.score_scale, t);
+    }
 
     float M = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    add_round(r0, s0, step, nsplit, M, lsum, o0, o1);
-    for (int base = s0 + kRound * step; base < nsplit; base += kRound * step)
-        add_round(load_round(ml, po, base, step, limit, t), base, step, nsplit, M, lsum, o0, o1);
+    if (nsplit > 0) {
+        add_round(r0, s0, step, nsplit, M, lsum, o0, o1);
+        for (int base = s0 + kRound * step; base < nsplit; base += kRound * step)
+            add_round(load_round(ml, po, base, step, limit, t), base, step, nsplit, M, lsum, o0, o1);
+    }
     if constexpr (WIDE) {
         __shared__ float sm[NW], sl[NW];
         __shared__ float so[NW][kHeadDim];
@@ -190,7 +396,15 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
             o1 = fmaf(so[w][2 * t + 1], f, o1);
         }
     }
-    if (nsplit == 0) {   // empty context: a zero row
+    bool empty = nsplit == 0;
+    if constexpr (APPEND) {
+        if (Lnew == 1) {
+            fold(nt, M, lsum, o0, o1);
+            if (qh % a.group == 0) store_new_token(a, nt, page, 0, hk, t);
+            empty = false;
+        }
+    }
+    if (empty) {   // no context: a zero row
         *reinterpret_cast<float2 *>(out + 2 * t) = make_float2(0.0f, 0.0f);
         return;
     }
@@ -207,13 +421,23 @@ hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t str
     // splits over 4 or 16 waves, so that a wave merges about one round
     // (kRound states); otherwise one wave per unit.
     const int per_unit = a.sk_groups > 0 ? a.sk_groups / a.batch + 2 : a.num_splits;
-    if (per_unit > 4 * kRound) {
-        hipLaunchKernelGGL(combine_kernel<kWideWaves>, dim3((unsigned)units), dim3(64 * kWideWaves), 0, stream, a, rb);
-    } else if (per_unit > kRound) {
-        hipLaunchKernelGGL(combine_kernel<kWaves>, dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
+    const dim3 one_grid((unsigned)((units + kWaves - 1) / kWaves));
+    if (a.k_new) {
+        if (per_unit > 4 * kRound)
+            hipLaunchKernelGGL((combine_kernel<kWideWaves, true>), dim3((unsigned)units), dim3(64 * kWideWaves), 0,
+                               stream, a, rb);
+        else if (per_unit > kRound)
+            hipLaunchKernelGGL((combine_kernel<kWaves, true>), dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
+        else
+            hipLaunchKernelGGL((combine_kernel<1, true>), one_grid, dim3(kThreads), 0, stream, a, rb);
     } else {
-        hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
-                           stream, a, rb);
+        if (per_unit > 4 * kRound)
+            hipLaunchKernelGGL((combine_kernel<kWideWaves, false>), dim3((unsigned)units), dim3(64 * kWideWaves), 0,
+                               stream, a, rb);
+        else if (per_unit > kRound)
+            hipLaunchKernelGGL((combine_kernel<kWaves, false>), dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
+        else
+            hipLaunchKernelGGL((combine_kernel<1, false>), one_grid, dim3(kThreads), 0, stream, a, rb);
     }
     return hipGetLastError();
 }

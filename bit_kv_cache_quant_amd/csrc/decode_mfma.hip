@@ -213,9 +213,161 @@ __device__ __forceinline__ const uint8_t *tile_addr(const uint8_t *base, uint32_
     return base + (uint64_t)phys * stride;
 }
 
+// Value of lane j ^ M of the same row of 16 (M = 1, 2, 4, 8) by DPP: quad
+// permutes, and the row mirrors (lane i takes lane 15 - i, or 7 - i within
+// each half row), two of which compose to xor 4 or xor 8.
+template <int M>
+__device__ __forceinline__ float row_xor(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    if constexpr (M == 1) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+    } else if constexpr (M == 2) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+    } else if constexpr (M == 4) {
+        const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, true));
+    } else {
+        static_assert(M == 8, "lane distance inside a row of 16");
+        const int y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, true));
+    }
+}
+
+// Butterflies of spans 8 .. BH/2 over 8 entries per lane (dims 8j .. 8j + 7)
+// between lanes j and j ^ span/8, in ascending order: the lower entry gets
+// u + v, the upper one u - v (u the lower entry's value).
+template <int M, int BH>
+__device__ __forceinline__ void row_butterflies(float (&y)[8], int j) {
+    if constexpr (M < BH / 8) {
+        const bool upper = (j & M) != 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float p = row_xor<M>(y[r]);
+            y[r] = upper ? (p - y[r]) : (y[r] + p);
+        }
+        row_butterflies<2 * M, BH>(y, j);
+    }
+}
+
+// Rotated query of lane (g, j): dims 8j .. 8j + 7 of one head from its fp16
+// words (zero if !live), with the sign mask of the randomized Hadamard
+// (byte j of the mask) applied first: R (S q) in fp32.
+template <int BH>
+__device__ __forceinline__ void rotate_query(uint4 raw, const uint32_t (&mask)[4], int j, bool live,
+                                             float (&qv)[8]) {
+    const uint4 rs = sign_flip_query(raw, mask, j);
+    if (live) {
+        qv[0] = half_to_float(rs.x); qv[1] = half_to_float(rs.x >> 16);
+        qv[2] = half_to_float(rs.y); qv[3] = half_to_float(rs.y >> 16);
+        qv[4] = half_to_float(rs.z); qv[5] = half_to_float(rs.z >> 16);
+        qv[6] = half_to_float(rs.w); qv[7] = half_to_float(rs.w >> 16);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) qv[r] = 0.0f;
+    }
+    if constexpr (BH > 0) {
+#pragma unroll
+        for (int span = 1; span < 8; span <<= 1) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (r & span) continue;
+                const float u = qv[r], v = qv[r + span];
+                qv[r] = u + v;
+                qv[r + span] = u - v;
+            }
+        }
+        row_butterflies<1, BH>(qv, j);
+        const float c = rsqrtf(static_cast<float>(BH));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) qv[r] *= c;
+    }
+}
+
+// ---- fused decode step: the sequence's new token ----
+//
+// Rotation and token-wise INT4 of one fp16 row (K or V of the new token),
+// held as lane (g, j) = dims 8j .. 8j + 7 (every row g of 16 lanes holds the
+// whole vector, the layout of the query set-up), with the append's
+// arithmetic: fp32 butterflies of ascending span (spans 1, 2, 4 inside the
+// lane, 8 .. Bh/2 between lanes j and j ^ span/8; lower entry u + v, upper
+// u - v), the product with the fp32 nearest 1/sqrt(Bh), m = max |y| (exact),
+// s = fp16(m / 7) (IEEE quotient, then round to nearest even), code =
+// clamp(rint(y / s), -8, 7) with the IEEE quotient and rint rounding half
+// to even.  Gives the lane's four
+// code bytes (dims 8j + 2i in the low nibble of byte i), the dequantized
+// entries and the scale.
+struct NewRow {
+    uint32_t bytes;
+    float d[8];
+    float s;
+    uint16_t s16;
+};
+template <int BH>
+__device__ __forceinline__ NewRow quantize_new_row(uint4 w, int j) {
+#pragma clang fp contract(off)
+    float y[8] = {half_to_float(w.x), half_to_float(w.x >> 16), half_to_float(w.y), half_to_float(w.y >> 16),
+                  half_to_float(w.z), half_to_float(w.z >> 16), half_to_float(w.w), half_to_float(w.w >> 16)};
+    if constexpr (BH > 0) {
+#pragma unroll
+        for (int span = 1; span < 8; span <<= 1) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (r & span) continue;
+                const float u = y[r], v = y[r + span];
+                y[r] = u + v;
+                y[r + span] = u - v;
+            }
+        }
+        row_butterflies<1, BH>(y, j);
+        const float c = __builtin_bit_cast(float, BH == 32 ? 0x3E3504F3u : BH == 64 ? 0x3E000000u : 0x3DB504F3u);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) y[r] = y[r] * c;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(y[r]));
+    m = row_max16(m);
+    // m / 7 and y / s as the IEEE quotients without a division: q0 = x r,
+    // e = fma(-q0, d, x), q = fma(e, r, q0), with r the fp32 nearest 1/7 for
+    // m / 7 (exact for every non-negative finite m) and the correctly
+    // rounded 1/s for y / s (exact for every fp16 divisor s over the
+    // quotients that decide a code; smaller ones give code 0, larger ones
+    // clamp either way) -- the append kernel's arithmetic.
+    const float r7 = __builtin_bit_cast(float, 0x3E124925u);
+    const float m0 = m * r7;
+    float s32 = __builtin_fmaf(__builtin_fmaf(-m0, 7.0f, m), r7, m0);
+    asm("" : "+v"(s32));   // two roundings (fp32, then fp16), as written
+    const _Float16 h = static_cast<_Float16>(s32);
+    NewRow nr;
+    nr.s = static_cast<float>(h);
+    nr.s16 = __builtin_bit_cast(uint16_t, h);
+    float sd = 0.0f, rcp = 0.0f;   // zero scale: every code is 0
+    if (nr.s > 0.0f && nr.s <= 65504.0f) {
+        const float r0 = __builtin_amdgcn_rcpf(nr.s);
+        rcp = __builtin_fmaf(__builtin_fmaf(-nr.s, r0, 1.0f), r0, r0);
+        sd = nr.s;
+    }
+    nr.bytes = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float q0 = y[r] * rcp;
+        const float e = __builtin_fmaf(-q0, sd, y[r]);
+        const float qt = __builtin_amdgcn_fmed3f(__builtin_fmaf(e, rcp, q0), -8.0f, 7.0f);
+        // round half to even at unit spacing: the low byte of the sum is code + 8
+        const uint32_t u = __builtin_bit_cast(uint32_t, qt + 12582920.0f) & 15u;
+        nr.d[r] = static_cast<float>(static_cast<int>(u) - 8) * nr.s;
+        nr.bytes |= (u ^ 8u) << (4 * r);
+    }
+    return nr;
+}
+
 // One work range: tokens [p0 P, min(p1 P, L)) of sequence b (p0 on a chunk
 // boundary) for head slot (KV head hk, query-head chunk chunk_id); returns
-// its partial softmax state.
+// its partial softmax state.  In the fused decode step (a.k_new set) the
+// range that ends at the sequence's last cached token also takes the new
+// token at position L: it quantizes the token's K and V rows, stores them
+// (head chunk 0 of the KV head), and starts its online softmax from that
+// token (max = its score, sum = 1, output = its value row).
 template <int BH, int P>
 __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveValues &sv, WavePfix &sp,
                                                      WaveQuery &sq, const int lane, const int b, const int hk,
@@ -332,43 +484,7 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
 
     // ---- setup: rotated query as fixed-point limbs; row g = head g ----
     float qv[8];
-    {
-        // randomized Hadamard: negate the masked channels (dims 8j..8j+7: byte j of the mask)
-        const uint4 rs = sign_flip_query(raw, a.sign_mask, j);
-        if (g < nheads) {
-            qv[0] = half_to_float(rs.x); qv[1] = half_to_float(rs.x >> 16);
-            qv[2] = half_to_float(rs.y); qv[3] = half_to_float(rs.y >> 16);
-            qv[4] = half_to_float(rs.z); qv[5] = half_to_float(rs.z >> 16);
-            qv[6] = half_to_float(rs.w); qv[7] = half_to_float(rs.w >> 16);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) qv[r] = 0.0f;
-        }
-        if constexpr (BH > 0) {
-#pragma unroll
-            for (int span = 1; span < 8; span <<= 1) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    if (r & span) continue;
-                    const float u = qv[r], v = qv[r + span];
-                    qv[r] = u + v;
-                    qv[r + span] = u - v;
-                }
-            }
-#pragma unroll
-            for (int m = 1; m < BH / 8; m <<= 1) {
-                const bool upper = (j & m) != 0;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float p = __shfl_xor(qv[r], m, 16);
-                    qv[r] = upper ? (p - qv[r]) : (qv[r] + p);
-                }
-            }
-            const float c = rsqrtf(static_cast<float>(BH));
-#pragma unroll
-            for (int r = 0; r < 8; ++r) qv[r] *= c;
-        }
-    }
+    rotate_query<BH>(raw, a.sign_mask, j, g < nheads, qv);
     float amax = 0.0f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(qv[r]));
@@ -410,6 +526,19 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
         qa0 = v4i{(int)e0.x, (int)e0.y, (int)e0.z, (int)e0.w};
         qa1 = v4i{(int)e1.x, (int)e1.y, (int)e1.z, (int)e1.w};
     }
+    // Fused step: this range ends at the sequence's last cached token, so it
+    // also takes the new token (position L) at its end.  The rotated query
+    // then waits in the query space (free once the A operands are built) and
+    // the new K/V rows load during the last chunk, by direct-to-LDS loads
+    // into the value buffer the next chunk's values would use.
+    const bool take_new = a.k_new != nullptr && tok_end == L && nchunks > 0;
+    float *qstash = reinterpret_cast<float *>(&sq.qlimb[0][0][0][0][0]);
+    if (take_new) {
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < 8; ++r) qstash[128 * g + 8 * j + r] = qv[r];
+    }
+    int32_t new_page = 0;
 
     // ---- main loop state ----
     float m_run = -INFINITY;     // running max (log2 units) of head g, uniform in row g
@@ -468,7 +597,18 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
             z[t] = (!TAIL || T0 + 16 * t + j < tok_end) ? sc : -INFINITY;
             zmax = fmaxf(zmax, z[t]);
         }
-        if constexpr (PF) load_k(ta, cd);
+        if constexpr (PF) {
+            load_k(ta, cd);
+        } else if (take_new) {
+            // lanes 0-15: the K row's 16-byte pieces, 16-31: the V row's (bytes
+            // 0-255 and 256-511 of the buffer); lanes 32-63 repeat them
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the value reads above are done
+            const uint16_t *src = (lane & 16) ? a.v_new : a.k_new;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(src + ((int64_t)b * a.num_kv_heads + hk) * kHeadDim + 8 * (lane & 15)),
+                (__attribute__((address_space(3))) void *)&sv.vbuf[0], 16, 0, 0);
+            new_page = a.page_table[(int64_t)b * a.max_pages_per_seq + (L >> a.page_shift)];
+        }
 
         // online softmax for head g (row g)
         zmax = row_max16_fast(zmax);
@@ -546,6 +686,57 @@ __device__ __forceinline__ PartialState decode_range(const DecodeArgs &a, WaveVa
     for (; c + 1 < nchunks; ++c) compute(c, buf, std::false_type{}, std::true_type{});
     if (c < nfull) compute(c, buf, std::false_type{}, std::false_type{});
     else if (c < nchunks) compute(c, buf, std::true_type{}, std::false_type{});
+
+    if (take_new) {
+        // Fused step: quantize and store the new token's K and V rows (lane
+        // (g, j): dims 8j..8j+7), score it against head g's rotated query,
+        // move its value row to the output layout (dims 16m + j) through the
+        // P buffer, and fold it into the running state.  (Lane indices go
+        // through an opaque copy, so that nothing derived from them is
+        // computed ahead of the loop and kept live through it.)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int gg = ln >> 4, jj = ln & 15;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the rows are in LDS
+        const uint4 kraw = *reinterpret_cast<const uint4 *>(&sv.vbuf[16 * jj]);
+        const uint4 vraw = *reinterpret_cast<const uint4 *>(&sv.vbuf[256 + 16 * jj]);
+        const NewRow kr = quantize_new_row<BH>(kraw, jj);
+        const NewRow vr = quantize_new_row<BH>(vraw, jj);
+        if (chunk_id == 0) {
+            const uint32_t slot = (uint32_t)(L & (P - 1));
+            uint8_t *kt = const_cast<uint8_t *>(tile_addr(kbase, (uint32_t)new_page, page_stride));
+            uint8_t *vt = const_cast<uint8_t *>(tile_addr(vbase, (uint32_t)new_page, page_stride));
+            if (gg == 0) {
+                *reinterpret_cast<uint32_t *>(kt + slot * kCodeBytesPerRow + 4 * jj) = kr.bytes;
+                *reinterpret_cast<uint32_t *>(vt + slot * kCodeBytesPerRow + 4 * jj) = vr.bytes;
+            }
+            if (ln == 0) {
+                *reinterpret_cast<uint16_t *>(
+                    const_cast<uint8_t *>(tile_addr(ksbase, (uint32_t)new_page, page_stride)) + 2 * slot) = kr.s16;
+                *reinterpret_cast<uint16_t *>(
+                    const_cast<uint8_t *>(tile_addr(vsbase, (uint32_t)new_page, page_stride)) + 2 * slot) = vr.s16;
+            }
+        }
+        float dot = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) dot = fmaf(qstash[128 * gg + 8 * jj + r], kr.d[r], dot);
+        const float z = row_sum16(dot) * a.score_scale;
+        float *vbuf = reinterpret_cast<float *>(&sp.pfix[0][0]);
+        wave_lds_sync();
+        if (gg == 0) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) vbuf[8 * jj + r] = vr.d[r];
+        }
+        wave_lds_sync();
+        const float mn = fmaxf(m_run, z);
+        const float corr = fast_exp2(m_run - mn);
+        const float w = fast_exp2(z - mn);
+        l_lane = fmaf(l_lane, corr, jj == 0 ? w : 0.0f);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o_acc[m] = fmaf(o_acc[m], corr, vbuf[16 * m + jj] * w);
+        m_run = mn;
+        wave_lds_sync();
+    }
 
     PartialState st;
 #pragma unroll

@@ -264,7 +264,8 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
                   int32_t batch, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t page_size, int32_t had_block, float softmax_scale, float *out,
                   void *workspace, size_t workspace_bytes, int32_t pages_per_split, void *phase_event,
-                  void *stream, bool use_scratch = false, const kvq_quant_config *cfg = nullptr) {
+                  void *stream, bool use_scratch = false, const kvq_quant_config *cfg = nullptr,
+                  const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr) {
     int rc = validate_decode(q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                              max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, out);
     if (rc != KVQ_OK) return rc;
@@ -341,6 +342,9 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
         if (e && (e[0] == '1' || e[0] == '2' || e[0] == '4') && e[1] == 0) a.range_waves = e[0] - '0';
     }
     a.score_scale = softmax_scale * 1.4426950408889634f;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.len_offset = k_new ? 1 : 0;
     const bool grouped = int4 && (a.format != KVQ_FORMAT_INT4 || a.scale_group != kHeadDim);
     hipError_t e = !int4 ? kvq::launch_decode_fp16(a, st)
                          : grouped ? kvq::launch_decode_grouped(a, st) : kvq::launch_decode_int4_mfma(a, st);
@@ -550,6 +554,19 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
     return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
                          max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
                          softmax_scale, out, workspace, workspace_bytes, pages_per_split, phase_event, stream);
+}
+
+int paged_decode_step_int4(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool,
+                           uint8_t *v_pool, int64_t num_pages, const int32_t *page_table, int32_t max_pages_per_seq,
+                           const int32_t *context_lens, int32_t batch, int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t had_block,
+                           float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                           int32_t pages_per_split, void *phase_event, void *stream) {
+    if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID_ARG;
+    return decode_common(true, q, k_pool, v_pool, num_pages, page_table, max_pages_per_seq, context_lens, batch,
+                         max_context_len, num_q_heads, num_kv_heads, head_dim, page_size, had_block,
+                         softmax_scale, out, workspace, workspace_bytes, pages_per_split, phase_event, stream, false,
+                         nullptr, k_new, v_new);
 }
 
 int paged_decode_attn_cfg(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool, int64_t num_pages,

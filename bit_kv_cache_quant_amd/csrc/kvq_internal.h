@@ -79,6 +79,14 @@ struct DecodeArgs {
     int32_t sk_min;            // block groups wanted for parallelism
     int32_t sk_target;         // most block groups wanted
     int32_t quads;             // head quads (groups of kHeadsPerChunk head slots) per sequence
+    // Fused decode step (k_new != nullptr): sequence b's last context token
+    // (position context_lens[b] - 1) arrives here as fp16 K/V rows
+    // [batch][num_kv_heads][kHeadDim].  The partial kernel then covers the
+    // positions before it (len_offset = 1), and the merge kernel quantizes
+    // the new rows into the cache and folds them into the output.
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    int32_t len_offset;        // 0, or 1 in the fused step
 };
 
 // Number of ranges the balanced decode cuts `tot` chunks into: ranges of
@@ -124,8 +132,13 @@ struct PrefillArgs {
 // clamped to the largest length the caller sized the page table and the
 // workspace for, so a length past that contract can give a wrong row but
 // never an access outside the buffers.
-__device__ __forceinline__ int32_t decode_len(const DecodeArgs &a, int b) {
+__device__ __forceinline__ int32_t full_len(const DecodeArgs &a, int b) {
     return min(a.context_lens[b], a.max_context_len);
+}
+// Tokens the partial kernels read from the cache: all of them, or (fused
+// step) all but the new last one.
+__device__ __forceinline__ int32_t decode_len(const DecodeArgs &a, int b) {
+    return full_len(a, b) - a.len_offset;
 }
 __device__ __forceinline__ int32_t prefill_len(const PrefillArgs &a, int b) {
     return min(a.context_lens[b], a.max_pages_per_seq * a.page_size);

@@ -10,6 +10,8 @@
  *   - paged_decode_attn_int4: one decode step of grouped-query attention over
  *     that cache, dequantizing in registers; the query is rotated instead of
  *     the keys, and the output is rotated back;
+ *   - paged_decode_step_int4: the two fused for a decode step (each
+ *     sequence's new token appended, then attention over its context);
  *   - kv_append_fp16 / paged_decode_attn_fp16: the same two operations on an
  *     unquantized fp16 paged cache, as the baseline.
  *
@@ -191,6 +193,41 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
                            int32_t had_block, float softmax_scale, float *out,
                            void *workspace, size_t workspace_bytes,
                            int32_t pages_per_split, void *phase_event, void *stream);
+
+/*
+ * paged_decode_step_int4 — one whole decode step: append each sequence's new
+ * token to the INT4 cache and attend over the context that ends with it.
+ * [EXPL] "システムこそが設計である — 融合カーネル" (the new token's K,V in fp16 go
+ * through rotation and token-wise INT4 into the paged block) together with
+ * "KVキャッシュこそが..." (every decode step then attends over the whole paged
+ * cache).
+ *
+ * Same result as kv_quant_append of k_new[b], v_new[b] at position
+ * L_b - 1 of sequence b (L_b = context_lens[b], for every b with L_b > 0,
+ * the same had_block), followed by paged_decode_attn_int4 with the same
+ * arguments: the cache bytes written are identical, and so is the output up
+ * to fp32 rounding order.  The work is done in two kernels instead of three:
+ * the partial kernel reads positions 0 .. L_b - 2 from the cache, and the
+ * merge kernel quantizes the new token, stores it and folds it into the
+ * softmax, so no kernel waits for a separate append.
+ *
+ *   k_new, v_new   fp16 [batch][num_kv_heads][head_dim], 16-byte aligned:
+ *                  the K and V rows of each sequence's new token (the rows of
+ *                  a sequence with L_b <= 0 are not read)
+ *   k_pool, v_pool written at the new tokens' slots only
+ *   other arguments, workspace and errors as for paged_decode_attn_int4.
+ * Contract (not checked): the slot of a new token lies in no other
+ * sequence's context of this call (in the unfused order the other sequence
+ * would read the new codes, here the old ones).
+ */
+int paged_decode_step_int4(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                           uint8_t *k_pool, uint8_t *v_pool, int64_t num_pages,
+                           const int32_t *page_table, int32_t max_pages_per_seq,
+                           const int32_t *context_lens, int32_t batch, int32_t max_context_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t had_block, float softmax_scale, float *out,
+                           void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                           void *phase_event, void *stream);
 
 /*
  * paged_prefill_attn_int4 — causal attention of a prompt's queries over the

@@ -146,6 +146,30 @@ def test_decode_host_validation_rejects_before_launch():
     assert _decode(B=0, q=None, out=None) == kvq.KVQ_OK       # empty batch: no-op
 
 
+def _step(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, npages=8, pt=FAKE, maxp=4, cl=FAKE, B=2, maxctx=64,
+             hq=32, hkv=8, d=128, P=16, bh=64, scale=0.088, out=FAKE, ws=FAKE, wsb=1 << 20, pps=0, ev=None,
+             stream=None)
+    a.update(kw)
+    return kvq.lib().paged_decode_step_int4(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["npages"], a["pt"],
+                                            a["maxp"], a["cl"], a["B"], a["maxctx"], a["hq"], a["hkv"], a["d"],
+                                            a["P"], a["bh"], a["scale"], a["out"], a["ws"], a["wsb"], a["pps"],
+                                            a["ev"], a["stream"])
+
+
+def test_fused_step_host_validation_rejects_before_launch():
+    """The fused step checks its new-token rows and then everything the
+    decode checks."""
+    assert _step(kn=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _step(vn=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _step(kn=FAKE + 2) == kvq.KVQ_ERR_INVALID_ARG       # misaligned rows
+    assert _step(bh=48) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _step(P=64) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _step(maxctx=65) == kvq.KVQ_ERR_INVALID_ARG
+    assert _step(ws=None) == kvq.KVQ_ERR_WORKSPACE
+    assert _step(B=0, q=None, out=None) == kvq.KVQ_OK           # empty batch: no-op
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(kvq, "_lib", None)

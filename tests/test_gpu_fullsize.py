@@ -17,10 +17,10 @@ from gpu_util import ATOL, say
 pytestmark = pytest.mark.gpu
 
 
-def _build_both(w, dev, layer, bh, fp16=False):
+def _build_both(w, dev, layer, bh, fp16=False, gpu_append=True):
     """GPU pools built through the C ABI and host pools built by the oracle,
     both from zero, from the same rows: every sequence's prefill, then the
-    workload's own append step."""
+    workload's own append step (on the host only, if not gpu_append)."""
     if fp16:
         shape = (w.num_pages, w.num_kv_heads, w.page_size, wl.HEAD_DIM)
         kp = torch.zeros(shape, dtype=torch.float16, device=dev)
@@ -33,8 +33,11 @@ def _build_both(w, dev, layer, bh, fp16=False):
     pt = w.table(layer)
     pt_d = torch.as_tensor(pt, device=dev)
 
-    def both(k, v, seq, pos):
-        if fp16:
+    def both(k, v, seq, pos, gpu=True):
+        if not gpu:
+            oracle.kv_quant_append(k.cpu().numpy(), v.cpu().numpy(), seq.cpu().numpy(), pos.cpu().numpy(), pt,
+                                   hk, hv, bh, w.page_size)
+        elif fp16:
             kvq.kv_append_fp16(k, v, seq, pos, pt_d, kp, vp, w.page_size)
             oracle.kv_append_fp16(k.cpu().numpy(), v.cpu().numpy(), seq.cpu().numpy(), pos.cpu().numpy(), pt,
                                   hk, hv, w.page_size)
@@ -53,7 +56,8 @@ def _build_both(w, dev, layer, bh, fp16=False):
              torch.arange(L, dtype=torch.int32, device=dev))
     if w.append_seq.size:
         k, v = w.append_rows(layer, dev)
-        both(k, v, torch.as_tensor(w.append_seq, device=dev), torch.as_tensor(w.append_pos, device=dev))
+        both(k, v, torch.as_tensor(w.append_seq, device=dev), torch.as_tensor(w.append_pos, device=dev),
+             gpu=gpu_append)
     torch.cuda.synchronize()
     return kp, vp, hk, hv, pt, pt_d
 
@@ -109,6 +113,35 @@ def test_c4_decode_step_full(dev):
     in the batch-wide balanced schedule the benchmark times; all 256
     sequences' tiles and output rows."""
     _check_full(wl.c4(), dev, 0, 64)
+
+
+def test_c4_fused_step_full(dev):
+    """The fused step (paged_decode_step_int4) as the benchmark times it, on
+    the batch-256 workload: the GPU pools hold the prefill only, the
+    oracle's also the step's append; after the step both pools must match
+    byte for byte and all 256 output rows lie within 2e-3."""
+    w = wl.c4()
+    kp, vp, hk, hv, pt, pt_d = _build_both(w, dev, 0, 64, gpu_append=False)
+    assert np.array_equal(w.append_seq, np.arange(w.batch)) and np.array_equal(w.append_pos, w.context_lens - 1)
+    k_new, v_new = w.append_rows(0, dev)       # row b: sequence b's new token
+    q = w.query(0, dev)
+    maxctx = int(w.context_lens.max())
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    say(f"{w.name}: fused step B={w.batch} maxctx={maxctx}")
+    out = kvq.paged_decode_step_int4(q, k_new, v_new, kp, vp, pt_d, cl, w.num_kv_heads, w.page_size, 64,
+                                     w.softmax_scale, maxctx)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    _compare_pools(kp, vp, hk, hv, False)
+    del kp, vp
+    torch.cuda.empty_cache()
+    say(f"{w.name}: oracle decode of all {w.batch} sequences")
+    want = oracle.paged_decode_attn_int4(q.cpu().numpy(), hk, hv, pt, w.context_lens, w.num_kv_heads,
+                                         w.page_size, 64, w.softmax_scale)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got.astype(np.float64) - want)))
+    say(f"{w.name}: fused step max-abs error {err:.3e} over all {w.batch} sequences")
+    assert err <= ATOL
 
 
 @pytest.mark.parametrize("bh", [128, 0])
