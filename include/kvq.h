@@ -207,9 +207,10 @@ int paged_decode_attn_int4(const uint16_t *q, const uint8_t *k_pool, const uint8
  * the same had_block), followed by paged_decode_attn_int4 with the same
  * arguments: the cache bytes written are identical, and so is the output up
  * to fp32 rounding order.  The work is done in two kernels instead of three:
- * the partial kernel reads positions 0 .. L_b - 2 from the cache, and the
- * merge kernel quantizes the new token, stores it and folds it into the
- * softmax, so no kernel waits for a separate append.
+ * the split-K partial kernel reads positions 0 .. L_b - 2 from the cache, and
+ * the work range that ends at position L_b - 2 also quantizes the new token,
+ * stores it and takes it into its softmax state (a sequence with L_b = 1 is
+ * handled by the merge kernel), so no kernel waits for a separate append.
  *
  *   k_new, v_new   fp16 [batch][num_kv_heads][head_dim], 16-byte aligned:
  *                  the K and V rows of each sequence's new token (the rows of
