@@ -197,14 +197,17 @@ def time_calls(fn, iters, warmup):
 
 def time_calls_cold(fn, iters, dev, flush_bytes=1 << 30):
     """Mean GPU time (ms) of fn() with the last-level cache (256 MB MALL)
-    flushed before every call by writing flush_bytes of another buffer;
+    flushed before every call by reading flush_bytes of another buffer (a
+    read leaves clean lines behind: a written flush buffer would leave the
+    cache full of dirty lines that the timed call then pays to write back);
     events bracket fn() alone."""
     import torch
-    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
-    fn()
+    junk = torch.ones(flush_bytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    settle(fn, 20.0)
     evs = []
     for _ in range(iters):
-        junk.fill_(1.0)
+        torch.sum(junk, dtype=torch.float32, out=sink)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -551,7 +554,7 @@ def append_measurements(dev, iters=20, warmup=3, with_decode_time=True):
     ex["append_prompt_32768tok_bh128_cold"] = {
         "ms": round(ms_c, 5), "GBps": round(nb3 / (ms_c * 1e-3) / 1e9, 2),
         "pct_of_hbm_peak": round(100 * nb3 / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-        "timing": "1 GiB written to another buffer before each call (last-level cache flushed)"}
+        "timing": "1 GiB of another buffer read before each call (last-level cache flushed)"}
     del kp3, vp3, k3, v3
     # decode-time append (1 token per sequence)
     w2 = wl.c2()
