@@ -73,22 +73,32 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kQRows = 16;        // query positions per block
 constexpr int kKeys = kChunkTokens;   // keys per step
-constexpr int kKPitch = 80;       // LDS bytes per key row of codes (64 + 16: conflict-free 16-byte reads)
 constexpr int kVRow = 2 * kHeadDim;   // bytes per fp16 value row
 
+// LDS of one chunk.  Every access but the transposed value reads is
+// lane-contiguous (lane l at 16 l of a 1 KiB block): measured, the earlier
+// row-major key layout (80-byte rows, read as lane (g, j) = row 16t + j,
+// piece g) and value stores of one 16-byte piece per row for 16 rows each
+// cost as many LDS bank-conflict cycles as they had instructions.
 struct alignas(16) PrefillShared {
-    uint8_t kev[kKeys * kKPitch];        // key codes, even dims' nibbles at the top of each byte
-    uint8_t kod[kKeys * kKPitch];        // key codes, odd dims' nibbles at the top (low nibble 0)
+    // key codes as the q.k A operand wants them: key 16t + j, 16-byte piece g
+    // (dims 32g .. 32g + 31) at 16 ((4t + g) 16 + j); even dims' nibbles at the
+    // top of each byte, or the odd dims' kept there (low nibble 0)
+    uint8_t kev[kKeys * kCodeBytesPerRow];
+    uint8_t kod[kKeys * kCodeBytesPerRow];
     // values as fp16; row T's 16-byte piece p at piece slot p ^ vswz(T)
     uint8_t v[kKeys * kVRow];
     float ks[kKeys], vs[kKeys];          // scales
 };
 
-// Piece swizzle of value row T: bits 1-3 (2 (T & 7)) give the 8 rows a
-// half-wave reads transposed 8 different 32-byte piece pairs (all 64 banks
-// once); bit 0 ((T >> 1) & 1) with bit 1 gives the 4 rows of one staging
-// write pass 4 different piece positions mod 4 (16 lanes, 16 bank groups).
-__host__ __device__ constexpr int vswz(int T) { return (2 * (T & 7)) | ((T >> 1) & 1); }
+// Piece swizzle of value row T (16-byte piece p of the row at slot
+// p ^ vswz(T)).  Bits 1-3 (2 (T & 7)) give the 8 rows a half-wave reads
+// transposed 8 different 32-byte piece pairs (all 64 banks once).  Bit 0
+// makes vswz a permutation of 0..15 over any 16 consecutive rows whose low
+// 3 bits are also distinct over any 8 of them: the staging stores (lane
+// (j, g) writes piece 4g + s of row 16w + j) then hit 8 or 16 distinct slots
+// in every group of 8 or 16 lanes.
+__host__ __device__ constexpr int vswz(int T) { return (2 * (T & 7)) | (((T >> 2) ^ (T >> 3)) & 1); }
 
 __device__ __forceinline__ v4f mfma(v8h a, v8h b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -314,36 +324,42 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const int64_t scale_off = (int64_t)a.num_kv_heads * (P * kCodeBytesPerRow) + (int64_t)hk * (2 * P);
     const int32_t *pt = a.page_table + (int64_t)b * a.max_pages_per_seq;
     const int last_page = (L - 1) / P;
-    const int ln = lane >> 2, lp = lane & 3;   // key row, 16-byte piece of this lane's loads
+    // Wave w stages keys 16w .. 16w + 15 of a chunk: lane l loads the
+    // 16-byte piece l / 16 (dims 32 (l / 16) .. + 31) of key 16w + l % 16, of
+    // the key and of the value codes.  Its key bytes land at 16 l of the
+    // wave's 1 KiB block, its values as fp16 pieces 4 (l / 16) .. + 3 of row
+    // 16w + l % 16.
+    const int kj = lane & 15, kg = lane >> 4;
     struct Raw { uint4 k, v; uint32_t s; };
     auto load = [&](int c, Raw &r) {
         const int key0 = kKeys * c + 16 * wave;
         const int64_t page = pt[min(key0 / P, last_page)];
         const int slot0 = key0 % P;
-        const uint8_t *kt = kpool + page * page_stride + code_off + (int64_t)(slot0 + ln) * kCodeBytesPerRow + 16 * lp;
-        const uint8_t *vt = vpool + page * page_stride + code_off + (int64_t)(slot0 + ln) * kCodeBytesPerRow + 16 * lp;
-        r.k = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u *>(kt)));
-        r.v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u *>(vt)));
-        const uint8_t *sp = (lane < 16 ? kpool : vpool) + page * page_stride + scale_off + 2 * (slot0 + (lane & 15));
+        const uint8_t *tile_k = kpool + page * page_stride + code_off + (int64_t)slot0 * kCodeBytesPerRow;
+        const uint8_t *tile_v = vpool + page * page_stride + code_off + (int64_t)slot0 * kCodeBytesPerRow;
+        r.k = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                            reinterpret_cast<const v4u *>(tile_k + kj * kCodeBytesPerRow + 16 * kg)));
+        r.v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                            reinterpret_cast<const v4u *>(tile_v + kj * kCodeBytesPerRow + 16 * kg)));
+        const uint8_t *sp = (lane < 16 ? kpool : vpool) + page * page_stride + scale_off + 2 * (slot0 + kj);
         r.s = lane < 32 ? *reinterpret_cast<const uint16_t *>(sp) : 0u;
     };
     auto stage = [&](const Raw &r) {
-        const int T = 16 * wave + ln;
         const uint32_t kw[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
         uint32_t ev[4], od[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            ev[s] = (kw[s] << 4) & 0xF0F0F0F0u;
-            od[s] = kw[s] & 0xF0F0F0F0u;
+        for (int s4 = 0; s4 < 4; ++s4) {
+            ev[s4] = (kw[s4] << 4) & 0xF0F0F0F0u;
+            od[s4] = kw[s4] & 0xF0F0F0F0u;
         }
-        *reinterpret_cast<uint4 *>(&sh.kev[T * kKPitch + 16 * lp]) = make_uint4(ev[0], ev[1], ev[2], ev[3]);
-        *reinterpret_cast<uint4 *>(&sh.kod[T * kKPitch + 16 * lp]) = make_uint4(od[0], od[1], od[2], od[3]);
-        // value codes of dims 32 lp + 8 s .. + 7 -> fp16 piece 4 lp + s of row T
+        *reinterpret_cast<uint4 *>(&sh.kev[1024 * wave + 16 * lane]) = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+        *reinterpret_cast<uint4 *>(&sh.kod[1024 * wave + 16 * lane]) = make_uint4(od[0], od[1], od[2], od[3]);
         const uint32_t vw[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+        const int T = 16 * wave + kj;
         const int vx = vswz(T);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * lp + s) ^ vx)]) = nibbles_to_half(vw[s]);
+        for (int s4 = 0; s4 < 4; ++s4)
+            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * kg + s4) ^ vx)]) = nibbles_to_half(vw[s4]);
         if (lane < 16) sh.ks[16 * wave + lane] = half_to_float(r.s);
         else if (lane < 32) sh.vs[16 * wave + lane - 16] = half_to_float(r.s);
     };
@@ -365,8 +381,8 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
         float z[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const v4i ke = *reinterpret_cast<const v4i *>(&sh.kev[(16 * t + j) * kKPitch + 16 * g]);
-            const v4i ko = *reinterpret_cast<const v4i *>(&sh.kod[(16 * t + j) * kKPitch + 16 * g]);
+            const v4i ke = *reinterpret_cast<const v4i *>(&sh.kev[1024 * t + 16 * lane]);
+            const v4i ko = *reinterpret_cast<const v4i *>(&sh.kod[1024 * t + 16 * lane]);
             const v4i zero = {0, 0, 0, 0};
             v4i dl[3];
 #pragma unroll
