@@ -335,6 +335,40 @@ def test_placement_golden_and_nothing_else_changes():
             assert int(flat[sa]) | (int(flat[sa + 1]) << 8) == s16
 
 
+def test_fp16_append_placement_matches_hand_worked_golden():
+    """The fp16 baseline append writes each token's rows exactly at the byte
+    ranges worked by hand in tests/golden/placement_fp16_small.txt (pool
+    [num_pages][Hkv][P][D] fp16), as the rows' own fp16 bytes, and touches no
+    other byte of a canary-filled pool."""
+    g = _golden("placement_fp16_small.txt")
+    hkv, P, npg = int(g["num_kv_heads"][0]), int(g["page_size"][0]), int(g["num_pages"][0])
+    pt = np.array([int(v) for v in g["page_table"]], np.int32).reshape(2, 2)
+    seqs = [int(v) for v in g["token_seq"]]
+    poss = [int(v) for v in g["token_pos"]]
+    T = len(seqs)
+    r = np.random.default_rng(2)
+    nbytes = npg * hkv * P * D * 2
+    canary_k = r.integers(0, 256, nbytes).astype(np.uint8)
+    canary_v = r.integers(0, 256, nbytes).astype(np.uint8)
+    kp = canary_k.copy().view(np.float16).reshape(npg, hkv, P, D)
+    vp = canary_v.copy().view(np.float16).reshape(npg, hkv, P, D)
+    k = (r.standard_normal((T, hkv, D)) * 3).astype(np.float16)
+    v = (r.standard_normal((T, hkv, D)) * 3).astype(np.float16)
+    oracle.kv_append_fp16(k, v, np.array(seqs, np.int32), np.array(poss, np.int32), pt, kp, vp, P)
+    rng_ = [int(x) for x in g["changed_ranges"]]
+    mask = np.zeros(nbytes, bool)
+    for a, b in zip(rng_[0::2], rng_[1::2]):
+        assert b - a == 2 * D
+        mask[a:b] = True
+    for pool, canary, src in ((kp, canary_k, k), (vp, canary_v, v)):
+        flat = pool.reshape(-1).view(np.uint8)
+        assert np.array_equal(flat[~mask], canary[~mask])
+        for t in range(T):
+            for h in range(hkv):
+                a = rng_[2 * (t * hkv + h)]
+                assert np.array_equal(flat[a:a + 2 * D], src[t, h].view(np.uint8))
+
+
 def test_append_under_permuted_page_table_matches_vector_quantizer():
     """Every token of every sequence lands in the slot its page table names,
     holding exactly its quantized vector and scale."""
