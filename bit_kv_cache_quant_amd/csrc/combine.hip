@@ -296,24 +296,40 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
     constexpr bool WIDE = NW > 1;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loads below
     const int t = threadIdx.x & 63;
-    const int unit = WIDE ? blockIdx.x : blockIdx.x * kWaves + wave;   // b * num_q_heads + qh
-    if (unit >= a.batch * a.num_q_heads) return;
-    const int b = unit / a.num_q_heads;
-    float *out = a.out + (int64_t)unit * kHeadDim;
-    const int qh = unit - b * a.num_q_heads;
-    const int hk = qh / a.group;
+    // The launch parameters the first addresses depend on, fetched at once
+    // (one wait, instead of one per branch that needs the next of them).
+    const int nq = a.num_q_heads, gshift = a.group_shift, group = a.group, skg = a.sk_groups, B = a.batch;
+    const int32_t *skp = a.sk_prefix;
+    asm volatile("" ::"s"(nq), "s"(gshift), "s"(group), "s"(skg), "s"(B), "s"(skp));
+    // grid: x = sequence, y = query head (NW > 1) or quad of query heads
+    const int b = blockIdx.x;
+    const int qh = WIDE ? (int)blockIdx.y : (int)blockIdx.y * kWaves + wave;
+    if (qh >= nq) return;
+    const int64_t unit = (int64_t)b * nq + qh;
+    float *out = a.out + unit * kHeadDim;
+    const int hk = gshift >= 0 ? (qh >> gshift) : qh / group;
     const int s0 = WIDE ? wave : 0, step = WIDE ? NW : 1;
     const int bh = rotate_back ? a.had_block : 0;
+
+    // Balanced schedule: the chunk prefix sums this unit's state addresses
+    // depend on.
+    int tot = 0, pb = 0, pb1 = 0;
+    if (skg > 0) {
+        tot = skp[B];
+        pb = skp[b];
+        pb1 = skp[b + 1];
+    }
 
     // Fused step: a sequence whose context is the new token alone has no
     // partial state (the partial kernels take each sequence's new token in
     // the range that ends at its last cached token); its rows and slot are
-    // loaded first.
+    // loaded first.  In the balanced schedule only a sequence without chunks
+    // can be one, so only such a sequence waits for its context length.
     int Lnew = 0;
     uint32_t kw = 0, vw = 0, qw = 0;
     int32_t page = 0;
     if constexpr (APPEND) {
-        Lnew = full_len(a, b);
+        if (a.sk_groups == 0 || pb1 == pb) Lnew = full_len(a, b);
         if (Lnew == 1) {
             kw = reinterpret_cast<const uint32_t *>(a.k_new + ((int64_t)b * a.num_kv_heads + hk) * kHeadDim)[t];
             vw = reinterpret_cast<const uint32_t *>(a.v_new + ((int64_t)b * a.num_kv_heads + hk) * kHeadDim)[t];
@@ -330,12 +346,16 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         // g_first .. g_last that meet sequence b, at positions
         // ((quad * 4 + wave) * 4 + head) * (sk_groups + batch) + g + b.  A
         // sequence with no chunks has none.
-        const int tot = a.sk_prefix[a.batch];
-        const int pb = a.sk_prefix[b], pb1 = a.sk_prefix[b + 1];
         if (pb1 > pb && tot > 0) {   // (tot > 0 whenever pb1 > pb: the test only orders the loads)
             const int G = balanced_groups(a.sk_min, a.sk_target, tot);
-            const int g_first = (int)((((int64_t)pb + 1) * G - 1) / tot);
-            const int g_last = (int)(((int64_t)pb1 * G - 1) / tot);
+            int g_first, g_last;
+            if (a.sk_div32) {
+                g_first = (int)(((uint32_t)(pb + 1) * (uint32_t)G - 1u) / (uint32_t)tot);
+                g_last = (int)(((uint32_t)pb1 * (uint32_t)G - 1u) / (uint32_t)tot);
+            } else {
+                g_first = (int)((((int64_t)pb + 1) * G - 1) / tot);
+                g_last = (int)(((int64_t)pb1 * G - 1) / tot);
+            }
             const int chunk_id = (qh - hk * a.group) / kHeadsPerChunk;
             const int slot = hk * a.head_chunks + chunk_id;
             const int local = (slot % kWaves) * kHeadsPerChunk + (qh - hk * a.group) % kHeadsPerChunk;
@@ -351,7 +371,7 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
         // Split mode: the unit owns num_splits positions, the first nsplit of
         // them written (none if the context is empty); the first round of
         // loads is issued before the context length is known.
-        const int64_t first = (int64_t)unit * a.num_splits;
+        const int64_t first = unit * a.num_splits;
         ml = a.ws_ml + first * 2;
         po = a.ws_o + first * kHeadDim;
         limit = a.num_splits;
@@ -415,27 +435,26 @@ __global__ __launch_bounds__(NW == 1 ? kThreads : 64 * NW) void combine_kernel(D
 }  // namespace
 
 hipError_t launch_combine(const DecodeArgs &a, bool rotate_back, hipStream_t stream) {
-    const int units = a.batch * a.num_q_heads;
     const int rb = rotate_back ? 1 : 0;
     // Many splits per sequence (long context, small batch): spread each unit's
     // splits over 4 or 16 waves, so that a wave merges about one round
-    // (kRound states); otherwise one wave per unit.
+    // (kRound states); otherwise one wave per unit.  Grid: x = sequence,
+    // y = query head, or quad of query heads with one wave per unit.
     const int per_unit = a.sk_groups > 0 ? a.sk_groups / a.batch + 2 : a.num_splits;
-    const dim3 one_grid((unsigned)((units + kWaves - 1) / kWaves));
+    const dim3 one_grid((unsigned)a.batch, (unsigned)((a.num_q_heads + kWaves - 1) / kWaves));
+    const dim3 wide_grid((unsigned)a.batch, (unsigned)a.num_q_heads);
     if (a.k_new) {
         if (per_unit > 4 * kRound)
-            hipLaunchKernelGGL((combine_kernel<kWideWaves, true>), dim3((unsigned)units), dim3(64 * kWideWaves), 0,
-                               stream, a, rb);
+            hipLaunchKernelGGL((combine_kernel<kWideWaves, true>), wide_grid, dim3(64 * kWideWaves), 0, stream, a, rb);
         else if (per_unit > kRound)
-            hipLaunchKernelGGL((combine_kernel<kWaves, true>), dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
+            hipLaunchKernelGGL((combine_kernel<kWaves, true>), wide_grid, dim3(kThreads), 0, stream, a, rb);
         else
             hipLaunchKernelGGL((combine_kernel<1, true>), one_grid, dim3(kThreads), 0, stream, a, rb);
     } else {
         if (per_unit > 4 * kRound)
-            hipLaunchKernelGGL((combine_kernel<kWideWaves, false>), dim3((unsigned)units), dim3(64 * kWideWaves), 0,
-                               stream, a, rb);
+            hipLaunchKernelGGL((combine_kernel<kWideWaves, false>), wide_grid, dim3(64 * kWideWaves), 0, stream, a, rb);
         else if (per_unit > kRound)
-            hipLaunchKernelGGL((combine_kernel<kWaves, false>), dim3((unsigned)units), dim3(kThreads), 0, stream, a, rb);
+            hipLaunchKernelGGL((combine_kernel<kWaves, false>), wide_grid, dim3(kThreads), 0, stream, a, rb);
         else
             hipLaunchKernelGGL((combine_kernel<1, false>), one_grid, dim3(kThreads), 0, stream, a, rb);
     }

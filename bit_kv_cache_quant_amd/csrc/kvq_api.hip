@@ -276,7 +276,7 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
     int32_t pps = 0, nsplit = 0;
     choose_split(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &pps, &nsplit);
-    if (nsplit > 65535 || (int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (nsplit > 65535 || (int64_t)num_kv_heads * chunks > 65535 || num_q_heads > 65535) return KVQ_ERR_UNSUPPORTED;
     BalancedPlan bp;
     const bool balanced = balanced_plan(batch, num_kv_heads, chunks, max_context_len, page_size, pages_per_split, &bp);
     const size_t need = balanced ? balanced_workspace_bytes(bp, batch) : workspace_bytes_for(batch, num_q_heads, nsplit);
@@ -345,6 +345,10 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.k_new = k_new;
     a.v_new = v_new;
     a.len_offset = k_new ? 1 : 0;
+    a.group_shift = -1;
+    if ((a.group & (a.group - 1)) == 0) a.group_shift = log2i(a.group);
+    a.sk_div32 = balanced && ((int64_t)batch * ((max_context_len + kvq::kChunkTokens - 1) / kvq::kChunkTokens) + 1) *
+                                     (int64_t)bp.gmax < (1ll << 31);
     const bool grouped = int4 && (a.format != KVQ_FORMAT_INT4 || a.scale_group != kHeadDim);
     hipError_t e = !int4 ? kvq::launch_decode_fp16(a, st)
                          : grouped ? kvq::launch_decode_grouped(a, st) : kvq::launch_decode_int4_mfma(a, st);

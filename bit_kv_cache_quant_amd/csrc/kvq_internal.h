@@ -87,6 +87,11 @@ struct DecodeArgs {
     const uint16_t *k_new;
     const uint16_t *v_new;
     int32_t len_offset;        // 0, or 1 in the fused step
+    // Merge-kernel shortcuts set by the host: log2(group) when group is a
+    // power of two (else -1), and whether the balanced schedule's range
+    // arithmetic ((chunk + 1) * groups) fits 31 bits (32-bit divisions).
+    int32_t group_shift;
+    int32_t sk_div32;
 };
 
 // Number of ranges the balanced decode cuts `tot` chunks into: ranges of
