@@ -70,3 +70,54 @@ def test_step_replays_under_hip_graph(dev, lens, fp16):
         step()   # eager work between replays
         torch.cuda.synchronize()
     del graph
+
+
+@pytest.mark.parametrize("lens", [[300, 17, 1, 0, 129, 2],                                      # split mode
+                                  [int(x) for x in np.random.default_rng(9).integers(0, 400, 24)]])  # balanced
+def test_fused_step_replays_under_hip_graph(dev, lens):
+    """paged_decode_step_int4 captured in a graph: every replay rewrites the
+    same new-token bytes and gives the eager output exactly."""
+    w = wl.small(len(lens), lens, 128, 16, cfg_id=230 + len(lens))
+    kp, vp = int4_pools(w, dev)
+    prefill(w, 0, dev, kp, vp, w.had_block)
+    k_new = torch.zeros((w.batch, w.num_kv_heads, w.head_dim), dtype=torch.float16, device=dev)
+    v_new = torch.zeros_like(k_new)
+    for b in range(w.batch):
+        if lens[b] > 0:
+            k, v = w.rows(0, b, lens[b] - 1, 1, dev)
+            k_new[b], v_new[b] = k[0], v[0]
+    pt = torch.as_tensor(w.table(0), device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    q = w.query(0, dev)
+    maxctx = int(max(lens))
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, maxctx, w.page_size),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        kvq.paged_decode_step_int4(q, k_new, v_new, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.had_block,
+                                   w.softmax_scale, maxctx, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    pools = (kp.clone(), vp.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager step"
+        assert torch.equal(kp, pools[0]) and torch.equal(vp, pools[1]), f"replay {r} changed other cache bytes"
+        step()
+        torch.cuda.synchronize()
+    del graph
