@@ -455,7 +455,11 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_grouped_kernel(App
                                                        ((int64_t)t * a.num_kv_heads + h) * kHeadDim) + q;
     uint4 raw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = sign_flip_words(src[4 * i], a.sign_mask, 4 * i + q);
+    for (int i = 0; i < 4; ++i) raw[i] = src[4 * i];
+    if ((a.sign_mask[0] | a.sign_mask[1] | a.sign_mask[2] | a.sign_mask[3]) != 0u) {   // uniform
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = sign_flip_words(raw[i], a.sign_mask, 4 * i + q);
+    }
 
     // y = R (S x), times the lane's sign (see rotate_chunks)
     float y[32];
@@ -509,18 +513,28 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_grouped_kernel(App
             }
             const float s = static_cast<float>(s16);
             sbits[gi] = __builtin_bit_cast(uint16_t, s16);
+            // zero scale: every code is 0 (divisor and reciprocal 0)
+            float sd = 0.0f, rcp = 0.0f;
             if (s > 0.0f) {
-                const float sd = s * sign, rcp = rcp_fp16(s) * sign;
+                sd = s * sign;
+                rcp = rcp_fp16(s) * sign;
+            }
+            // With the plain scale fp16(m / 7), normal, |y / s| <= 7 (1 +
+            // 2^-11) < 7.5, so the codes need no clamp; a wave clamps only if
+            // one of its groups has a subnormal scale (the token-wise
+            // kernel's argument).  A searched scale clips: always clamp.
+            auto codes = [&](auto clamp) {
+                constexpr bool kClamp = decltype(clamp)::value;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float qt = __builtin_amdgcn_fmed3f(div_fp16(yg[r], sd, rcp), -8.0f, 7.0f);
+                    float qt = div_fp16(yg[r], sd, rcp);
+                    if constexpr (kClamp) qt = __builtin_amdgcn_fmed3f(qt, -8.0f, 7.0f);
                     // round half to even, low nibble = code + 8; xor 8: two's complement
                     nib[R * gi + r] = (__builtin_bit_cast(uint32_t, qt + 12582920.0f) & 0xFu) ^ 8u;
                 }
-            } else {
-#pragma unroll
-                for (int r = 0; r < R; ++r) nib[R * gi + r] = 0u;
-            }
+            };
+            if (!SEARCH && __all(!(s > 0.0f && s < 6.103515625e-05f))) codes(std::false_type{});
+            else codes(std::true_type{});
         } else {
             // MXFP4: X = floor(log2 m) - 2, element = nearest E2M1 value to
             // y / 2^X (ties to the even code, saturating at 6), sign bit set
@@ -574,9 +588,10 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_grouped_kernel(App
     const uint4 w4 = *reinterpret_cast<const uint4 *>(&my_words[4 * q]);
     __builtin_nontemporal_store(v4u{w4.x, w4.y, w4.z, w4.w}, reinterpret_cast<v4u *>(code_row + 16 * q));
     if (q == 0) {
-        if constexpr (NG * SB == 8) {
-            const uint2 v2 = make_uint2(sbits[0] | (sbits[1] << 16), sbits[2] | (sbits[3] << 16));
-            *reinterpret_cast<uint2 *>(scale_at) = v2;
+        if constexpr (NG * SB == 8) {   // non-temporal, as the codes
+            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(v2u{sbits[0] | (sbits[1] << 16), sbits[2] | (sbits[3] << 16)},
+                                        reinterpret_cast<v2u *>(scale_at));
         } else if constexpr (NG * SB == 4) {
             const uint32_t v1 = SB == 2 ? (sbits[0] | (sbits[NG - 1] << 16))
                                         : (sbits[0] | (sbits[NG > 1 ? 1 : 0] << 8) | (sbits[NG > 2 ? 2 : 0] << 16) |
