@@ -207,7 +207,7 @@ def time_calls_cold(fn, iters, dev, flush_bytes=1 << 30):
     settle(fn, 20.0)
     evs = []
     for _ in range(iters):
-        torch.sum(junk, dtype=torch.float32, out=sink)
+        torch.sum(junk, dim=0, dtype=torch.float32, out=sink)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
