@@ -63,7 +63,7 @@ def test_decode_ragged_lengths(dev, had_block, page_size):
     assert np.all(got[0] == 0), "a zero-length sequence gives a zero row"
 
 
-@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 8])
 def test_decode_gqa_groups(dev, group):
     lens = [50, 200, 17]
     w = wl.small(len(lens), lens, 64, 16, cfg_id=80 + group, num_kv_heads=2, num_q_heads=2 * group)
@@ -71,7 +71,7 @@ def test_decode_gqa_groups(dev, group):
     _assert_close(got, want)
 
 
-@pytest.mark.parametrize("pages_per_split,group", [(0, 4), (4, 4), (9, 4), (0, 1), (3, 8), (5, 2)])
+@pytest.mark.parametrize("pages_per_split,group", [(0, 4), (4, 4), (9, 4), (0, 1), (3, 8), (5, 2), (0, 3), (2, 6)])
 def test_decode_ranges_cross_sequences(dev, pages_per_split, group):
     """Many short, ragged sequences (some empty): with batches of 16 or more
     the decode cuts the concatenated chunks of all sequences into equal
@@ -139,7 +139,7 @@ def test_decode_fp16_baseline(dev, page_size):
     assert np.all(got[0] == 0), "a zero-length sequence gives a zero row"
 
 
-@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 6, 8])
 def test_decode_fp16_gqa_groups(dev, group):
     lens = [50, 200, 17]
     w = wl.small(len(lens), lens, 0, 16, cfg_id=180 + group, num_kv_heads=2, num_q_heads=2 * group)

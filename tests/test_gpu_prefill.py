@@ -135,7 +135,7 @@ def test_prefill_graph_replay(dev):
     say("prefill graph: 3 replays equal to the eager call")
 
 
-@pytest.mark.parametrize("group", [1, 2, 8])
+@pytest.mark.parametrize("group", [1, 2, 3, 6, 8])
 def test_prefill_gqa_groups(dev, group):
     lens = [70, 40]
     w = wl.small(len(lens), lens, 32, 16, cfg_id=260 + group, num_kv_heads=2, num_q_heads=2 * group)

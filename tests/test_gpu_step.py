@@ -89,7 +89,7 @@ def test_step_many_ranges(dev, lens, pps):
     _step_case(dev, lens, 128, 16, cfg_id=380 + len(lens) + pps, pages_per_split=pps)
 
 
-@pytest.mark.parametrize("group", [1, 2, 8])
+@pytest.mark.parametrize("group", [1, 2, 3, 6, 8])
 def test_step_gqa_groups(dev, group):
     """One writer per KV head whatever the group size."""
     hkv = 2

@@ -149,6 +149,31 @@ def test_variant_decode_against_oracle(dev, cfg, sched):
     assert np.all(got[lens.index(0)] == 0)
 
 
+@pytest.mark.parametrize("cfg", [(0, 64, 32, 0, MASK), (1, 32, 32, 0, 0)], ids=_ids)
+@pytest.mark.parametrize("group,lens", [(3, [0, 1, 300, 65, 129]), (6, [int(x) for x in np.random.default_rng(37).integers(0, 300, 19)])])
+def test_variant_decode_odd_groups(dev, cfg, group, lens):
+    """GQA groups that are not a power of two and leave the last head chunk
+    of each KV head partly filled (6 = 4 + 2), in both schedules (5
+    sequences: per-sequence splits; 19: batch-wide ranges)."""
+    hkv = 8 if group == 3 else 2
+    w = wl.small(len(lens), lens, cfg[1], 16, cfg_id=470 + group, num_kv_heads=hkv, num_q_heads=hkv * group)
+    say(f"variant decode {_ids(cfg)} group {group} B={w.batch}")
+    kp, vp, hk, hv = _build(cfg, w, dev, seed=11)
+    assert np.array_equal(kp.cpu().numpy(), hk) and np.array_equal(vp.cpu().numpy(), hv)
+    q = w.query(0, dev)
+    out = kvq.paged_decode_attn_cfg(q, kp, vp, torch.as_tensor(w.table(0), device=dev),
+                                    torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, 16,
+                                    kvq.quant_config(*cfg), w.softmax_scale, int(max(lens)))
+    torch.cuda.synchronize()
+    want = oracle.paged_decode_attn_cfg(q.cpu().numpy(), hk, hv, w.table(0), w.context_lens, w.num_kv_heads, 16,
+                                        oracle.qcfg(*cfg), w.softmax_scale)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - want)))
+    say(f"  max-abs error {err:.3e}")
+    assert err <= ATOL
+
+
 @pytest.mark.parametrize("cfg", [(0, 32, 32, 1, MASK), (1, 128, 32, 0, MASK)], ids=_ids)
 @pytest.mark.parametrize("mult", [4.0])
 def test_variant_decode_sharp_softmax(dev, cfg, mult):
