@@ -375,6 +375,12 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const int tr_piece = (j & 3) >> 1;
     const int tr_x = vswz(tr_key);          // the row's piece swizzle (rows + 16, + 32 share it)
 
+    // -1 in a register the compiler cannot see through: fma(x, -1, y) with
+    // a literal would become y - x, whose widening of x costs an extra
+    // conversion instead of the mixed-precision fma
+    float neg_one = -1.0f;
+    asm("" : "+v"(neg_one));
+
     auto compute = [&](int c, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
         // q.k: z[t][i] = score of key 16t + 4g + i before the position's factor
@@ -440,9 +446,13 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const v2h hi = __builtin_convertvector((v2f){pv[2 * u], pv[2 * u + 1]}, v2h);
-                const v2f back = __builtin_convertvector(hi, v2f);
                 ph[t][u] = hi;
-                pl[t][u] = __builtin_convertvector((v2f){pv[2 * u] - back[0], pv[2 * u + 1] - back[1]}, v2h);
+                // pv - hi, exact (|pv - hi| is at most half an fp16 ulp of pv),
+                // as one mixed-precision fma per entry (the fp16 operand is
+                // widened inside the instruction)
+                const float d0 = fmaf(static_cast<float>(hi[0]), neg_one, pv[2 * u]);
+                const float d1 = fmaf(static_cast<float>(hi[1]), neg_one, pv[2 * u + 1]);
+                pl[t][u] = __builtin_convertvector((v2f){d0, d1}, v2h);
             }
         }
         v8h pb_hi[2], pb_lo[2];   // element 4 (t & 1) + i of half t / 2
