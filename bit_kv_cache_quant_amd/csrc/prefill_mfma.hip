@@ -193,7 +193,7 @@ __device__ __forceinline__ bool find_tile(const int32_t *q_start, const int B, c
 }
 
 template <int BH, int P>
-__global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
@@ -374,6 +374,8 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
     const uint32_t tr_base = tr_key * kVRow + 8 * (j & 1);
     const int tr_piece = (j & 3) >> 1;
     const int tr_x = vswz(tr_key);          // the row's piece swizzle (rows + 16, + 32 share it)
+    const uint32_t tr_b = tr_base + 16u * (uint32_t)(tr_piece ^ (tr_x & 1));
+    const uint32_t tr_c = 32u * (uint32_t)(tr_x >> 1);
 
     // -1 in a register the compiler cannot see through: fma(x, -1, y) with
     // a literal would become y - x, whose widening of x costs an extra
@@ -465,22 +467,36 @@ __global__ __launch_bounds__(kThreads) void prefill_int4_kernel(PrefillArgs a) {
                                                __builtin_shufflevector(pl[2 * h + 1][0], pl[2 * h + 1][1], 0, 1, 2, 3),
                                                0, 1, 2, 3, 4, 5, 6, 7);
         }
-        // p.v: dim tile m, key half h
+        // p.v: dim tile m, both key halves h; tile m + 1's values are read
+        // while tile m's products run.  Piece (2m + tr_piece) ^ tr_x of the
+        // row is 2 (m ^ (tr_x >> 1)) + (tr_piece ^ (tr_x & 1)).
+        auto read_tile = [&](const int m, v8h (&va)[2]) {
+            const uint32_t addr = tr_b + (tr_c ^ (32u * (uint32_t)m));
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const uint32_t addr = tr_base + 32 * h * kVRow + 16 * ((2 * m + tr_piece) ^ tr_x);
+            for (int h = 0; h < 2; ++h) {
                 const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s *)&sh.v[addr]);
+                    (__attribute__((address_space(3))) v4s *)&sh.v[addr + 32 * h * kVRow]);
                 const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s *)&sh.v[addr + 16 * kVRow]);
-                const v8h va = __builtin_bit_cast(
+                    (__attribute__((address_space(3))) v4s *)&sh.v[addr + 32 * h * kVRow + 16 * kVRow]);
+                va[h] = __builtin_bit_cast(
                     v8h, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
                                     __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
-                o[m] = mfma(va, pb_hi[h], o[m]);
-                o[m] = mfma(va, pb_lo[h], o[m]);
             }
+        };
+        // (scheduling barriers that only vector and scalar ALU work may
+        // cross keep each tile's reads ahead of the previous tile's products)
+        v8h va[2][2];
+        read_tile(0, va[0]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            if (m + 1 < 8) read_tile(m + 1, va[(m + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0x6);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                o[m] = mfma(va[m & 1][h], pb_hi[h], o[m]);
+                o[m] = mfma(va[m & 1][h], pb_lo[h], o[m]);
+            }
+            __builtin_amdgcn_sched_barrier(0x6);
         }
     };
 
