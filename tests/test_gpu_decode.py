@@ -11,7 +11,7 @@ import torch
 import bit_kv_cache_quant_amd as kvq
 import oracle
 import workloads as wl
-from gpu_util import ATOL, append_step, fp16_pools, int4_pools, prefill, say
+from gpu_util import ATOL, append_step, fp16_pools, int4_pools, prefill, prefill_batched, say
 
 pytestmark = pytest.mark.gpu
 D = wl.HEAD_DIM
@@ -252,3 +252,34 @@ def test_decode_range_shared_by_waves(dev, lens, page_size, had_block, monkeypat
     bound = 1e-5 * max(1.0, float(np.max(np.abs(outs["1"]))))
     assert np.max(np.abs(outs["2"] - outs["1"])) <= bound
     assert np.max(np.abs(outs["4"] - outs["1"])) <= bound
+
+
+
+@pytest.mark.parametrize("batch", [15, 16, 4096, 4097])
+def test_decode_batch_schedule_edges(dev, batch):
+    """Batches at the edges of the decode schedules: 15 (the largest batch
+    of per-sequence splits below the batch-wide ranges), 16 (the smallest
+    with them), 4096 (the largest: one block scans every context length)
+    and 4097 (per-sequence splits again, over a grid of 4097 sequences).
+    Every output row is compared."""
+    r = np.random.default_rng(500 + batch)
+    hi = 300 if batch < 100 else 40
+    lens = [int(x) for x in r.integers(0, hi, size=batch)]
+    lens[1] = 0
+    lens[-1] = hi + 17
+    w = wl.small(batch, lens, 64, 16, cfg_id=500 + batch % 97)
+    kp, vp = int4_pools(w, dev)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    say(f"schedule edge B={batch}")
+    prefill_batched(w, 0, dev, kp, vp, 64, host_pools=(hk, hv))
+    assert np.array_equal(kp.cpu().numpy(), hk) and np.array_equal(vp.cpu().numpy(), hv)
+    q = w.query(0, dev)
+    out = kvq.paged_decode_attn_int4(q, kp, vp, torch.as_tensor(w.table(0), device=dev),
+                                     torch.as_tensor(w.context_lens, device=dev), w.num_kv_heads, w.page_size, 64,
+                                     w.softmax_scale, int(max(lens)))
+    torch.cuda.synchronize()
+    want = oracle.paged_decode_attn_int4(q.cpu().numpy(), hk, hv, w.table(0), w.context_lens, w.num_kv_heads,
+                                         w.page_size, 64, w.softmax_scale)
+    got = out.cpu().numpy()
+    _assert_close(got, want)
+    assert np.all(got[1] == 0)

@@ -14,13 +14,13 @@ import torch
 import bit_kv_cache_quant_amd as kvq
 import oracle
 import workloads as wl
-from gpu_util import ATOL, int4_pools, prefill, say
+from gpu_util import ATOL, int4_pools, prefill, prefill_batched, say
 
 pytestmark = pytest.mark.gpu
 D = wl.HEAD_DIM
 
 
-def _step_case(dev, lens, bh, P, cfg_id, pages_per_split=0, hkv=8, hq=32, scale_mult=1.0):
+def _step_case(dev, lens, bh, P, cfg_id, pages_per_split=0, hkv=8, hq=32, scale_mult=1.0, batched=False):
     """Cache positions 0 .. L_b - 2 of every sequence (GPU and oracle), then
     the fused step on the GPU against the oracle's append + decode."""
     lens = np.asarray(lens, np.int32)
@@ -29,14 +29,23 @@ def _step_case(dev, lens, bh, P, cfg_id, pages_per_split=0, hkv=8, hq=32, scale_
     kp, vp = int4_pools(w, dev, seed=cfg_id)
     hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
     say(f"fused step B={w.batch} bh={bh} P={P} pps={pages_per_split} lens[:8]={lens[:8].tolist()}")
-    prefill(w, 0, dev, kp, vp, bh, host_pools=(hk, hv))
+    if batched:
+        prefill_batched(w, 0, dev, kp, vp, bh, host_pools=(hk, hv))
+    else:
+        prefill(w, 0, dev, kp, vp, bh, host_pools=(hk, hv))
     assert np.array_equal(kp.cpu().numpy(), hk) and np.array_equal(vp.cpu().numpy(), hv)
     k_new = torch.zeros((w.batch, hkv, D), dtype=torch.float16)
     v_new = torch.zeros_like(k_new)
     live = [b for b in range(w.batch) if lens[b] > 0]
-    for b in live:
-        k, v = w.rows(0, b, int(lens[b]) - 1, 1)
-        k_new[b], v_new[b] = k[0], v[0]
+    if batched:   # seeded N(0, 1) rows from one generator
+        g = torch.Generator()
+        g.manual_seed(0x5EED1000 + cfg_id)
+        k_new = torch.randn((w.batch, hkv, D), generator=g).to(torch.float16)
+        v_new = torch.randn((w.batch, hkv, D), generator=g).to(torch.float16)
+    else:
+        for b in live:
+            k, v = w.rows(0, b, int(lens[b]) - 1, 1)
+            k_new[b], v_new[b] = k[0], v[0]
     pt = w.table(0)
     if live:
         sel = np.asarray(live)
@@ -94,6 +103,19 @@ def test_step_gqa_groups(dev, group):
     """One writer per KV head whatever the group size."""
     hkv = 2
     _step_case(dev, [50, 200, 17, 1], 64, 16, cfg_id=390 + group, hkv=hkv, hq=hkv * group)
+
+
+@pytest.mark.parametrize("batch", [15, 16, 4096, 4097])
+def test_step_batch_schedule_edges(dev, batch):
+    """The fused step at the edges of the decode schedules (15 / 16: split
+    and batch-wide ranges; 4096: the largest batch-wide schedule; 4097:
+    splits again), with empty and one-token sequences among them."""
+    r = np.random.default_rng(600 + batch)
+    hi = 300 if batch < 100 else 40
+    lens = [int(x) for x in r.integers(0, hi, size=batch)]
+    lens[1] = 0
+    lens[2] = 1
+    _step_case(dev, lens, 64, 16, cfg_id=600 + batch % 89, batched=True)
 
 
 @pytest.mark.parametrize("mult", [2.0, 4.0])
