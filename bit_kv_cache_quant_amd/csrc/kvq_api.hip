@@ -331,13 +331,19 @@ int decode_common(bool int4, const uint16_t *q, const void *k_pool, const void *
     a.had_block = int4 ? had_block : 0;
     a.pages_per_split = pps;
     a.num_splits = nsplit;
-    // Split mode with at most about one block per CU: share each range among
-    // 4 waves of a block (2 for up to two blocks per CU); the INT4 token-wise
-    // kernel only.  KVQ_RANGE_WAVES=1/2/4 overrides (measurement).
+    // Split mode with few work items (at most two 8-wave blocks per CU): a
+    // range of 4 chunks or more is shared by 2 waves of a block, each taking
+    // half of its chunks; shorter ranges stay with one wave.  Measured in HIP
+    // graphs, batch 1-12, contexts 2K-128K: 2 waves beat one by 7-13% once a
+    // range has 4 chunks or more and lose with 1-3 (the second wave then
+    // idles or gets a single chunk); 4 waves per range were never the
+    // fastest (each wave's set-up then serves one chunk).  The INT4
+    // token-wise kernel only.  KVQ_RANGE_WAVES=1/2/4 overrides (measurement).
     a.range_waves = 1;
     if (!balanced && int4 && !grouped_cfg(cfg)) {
         const int64_t blocks = (int64_t)batch * ((num_kv_heads * chunks + 3) / 4) * nsplit;
-        a.range_waves = blocks <= 256 ? 4 : (blocks <= 512 ? 2 : 1);
+        const int32_t range_chunks = pps / (kvq::kChunkTokens / page_size);
+        a.range_waves = (blocks <= 512 && range_chunks >= 4) ? 2 : 1;
         const char *e = getenv("KVQ_RANGE_WAVES");
         if (e && (e[0] == '1' || e[0] == '2' || e[0] == '4') && e[1] == 0) a.range_waves = e[0] - '0';
     }
