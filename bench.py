@@ -309,7 +309,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the hot path is "
-              "per-GPU data-parallel and no multi-GPU run is part of this build.", file=sys.stderr)
+              "per-GPU data-parallel (each GPU serves its own sequences and caches), and this "
+              "benchmark has no multi-GPU mode.", file=sys.stderr)
         return 2
 
     import numpy as np
