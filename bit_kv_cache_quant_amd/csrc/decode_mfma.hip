@@ -833,7 +833,7 @@ __global__ __launch_bounds__(kThreads * WPR) void decode_int4_wide_kernel(Decode
         for (int m = 0; m < 8; ++m) r.o[m] = fmaf(sh.mrg.o[src][m][lane], f, r.o[m]);
     }
     const int qh0 = it.hk * a.group + it.chunk_id * kH;
-    write_partial(a, r, lane, min(kH, a.group - it.chunk_id * kH),
+    write_partial<true>(a, r, lane, min(kH, a.group - it.chunk_id * kH),
                   ((int64_t)it.b * a.num_q_heads + qh0) * a.num_splits + it.s, a.num_splits);
 }
 
