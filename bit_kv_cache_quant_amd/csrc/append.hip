@@ -198,15 +198,38 @@ __device__ __forceinline__ uint4 sign_flip_words(uint4 w, const uint32_t (&mask)
     return w;
 }
 
-// A block covers 64 consecutive tokens of one (KV head, K or V): quad g takes
-// token base + g, so consecutive quads write consecutive slots of a page.
+// Block b of the launch covers 64 consecutive tokens of one (KV head, K or
+// V): token block b / (2 Hkv), then K heads 0 .. Hkv - 1 and V heads 0 ..
+// Hkv - 1 in turn, so consecutive blocks read the adjacent 256-byte rows of
+// the same tokens and write the adjacent code rows of the same pages
+// (measured against blocks ordered head by head over the whole call: 52.7 ->
+// 48.7 us for 65,536 tokens without rotation, 52.0 -> 50.6 us at Bh 64);
+// quad g takes token base + g, so consecutive quads write consecutive slots
+// of a page.
+struct AppendBlock {
+    int32_t token0, h;
+    bool is_v;
+};
+__device__ __forceinline__ AppendBlock append_block(const AppendArgs &a) {
+    const int32_t per_tokens = 2 * a.num_kv_heads;
+    const int32_t bid = (int32_t)blockIdx.x;
+    const int32_t tb = bid / per_tokens;
+    const int32_t r = bid - tb * per_tokens;
+    AppendBlock ab;
+    ab.token0 = tb * kTokensPerBlock;
+    ab.is_v = r >= a.num_kv_heads;
+    ab.h = ab.is_v ? r - a.num_kv_heads : r;
+    return ab;
+}
+
 template <int BH, bool SIGNS>
 __global__ __launch_bounds__(kBlockThreads) void quant_append_kernel(AppendArgs a) {
     const int q = threadIdx.x & 3;
-    const int32_t t = (int32_t)blockIdx.x * kTokensPerBlock + (int32_t)(threadIdx.x >> 2);
+    const AppendBlock ab = append_block(a);
+    const int32_t t = ab.token0 + (int32_t)(threadIdx.x >> 2);
     if (t >= a.num_tokens) return;  // the whole quad leaves together
-    const int32_t h = (int32_t)blockIdx.y;
-    const bool is_v = blockIdx.z != 0;
+    const int32_t h = ab.h;
+    const bool is_v = ab.is_v;
 
     // Issue the address loads first; their latency overlaps the arithmetic.
     const int32_t seq = a.token_seq[t];
@@ -441,10 +464,11 @@ __global__ __launch_bounds__(kBlockThreads) void quant_append_grouped_kernel(App
     constexpr int R = G / 4;               // registers of one group in each lane of the quad
     constexpr int SB = FMT == KVQ_FMT_MXFP4 ? 1 : 2;   // bytes per scale
     const int q = threadIdx.x & 3;
-    const int32_t t = (int32_t)blockIdx.x * kTokensPerBlock + (int32_t)(threadIdx.x >> 2);
+    const AppendBlock ab = append_block(a);
+    const int32_t t = ab.token0 + (int32_t)(threadIdx.x >> 2);
     if (t >= a.num_tokens) return;  // the whole quad leaves together
-    const int32_t h = (int32_t)blockIdx.y;
-    const bool is_v = blockIdx.z != 0;
+    const int32_t h = ab.h;
+    const bool is_v = ab.is_v;
 
     const int32_t seq = a.token_seq[t];
     const int32_t pos = a.token_pos[t];
@@ -632,7 +656,10 @@ dim3 grid_for(const AppendArgs &a) {
 }  // namespace
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock), (unsigned)a.num_kv_heads, 2);
+    // one dimension: (token block, K or V, head), see append_block
+    const int64_t blocks = (int64_t)((a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock) * 2 * a.num_kv_heads;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks, 1, 1);
     const bool signs = (a.sign_mask[0] | a.sign_mask[1] | a.sign_mask[2] | a.sign_mask[3]) != 0;
     if (a.format != KVQ_FMT_INT4 || a.scale_group != kHeadDim || a.scale_search) {
         // per-group scales, scale search, MXFP4

@@ -239,6 +239,8 @@ int validate_append(const void *k_new, const void *v_new, const int32_t *token_s
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
         return KVQ_ERR_INVALID_ARG;
     if ((int64_t)num_tokens * num_kv_heads * 2 / 16 + 1 >= 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+    // the INT4 appends launch one block per (64 tokens, K or V, KV head)
+    if ((int64_t)((num_tokens + 63) / 64) * 2 * num_kv_heads > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
 }
 
