@@ -373,8 +373,9 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     def step(mid_ev=None):
-        # one call: partial kernel over every cached token, then the merge,
-        # which also rotates, quantizes and appends each sequence's new token
+        # one call: the partial kernel over every cached token, whose range
+        # that ends at a sequence's last cached token also rotates, quantizes,
+        # stores and attends to the sequence's new token, then the merge
         kvq.paged_decode_step_int4(q, k_new, v_new, kp, vp, pt, cl, w.num_kv_heads, w.page_size, w.had_block,
                                    w.softmax_scale, maxctx, out=out, workspace=ws, phase_event=mid_ev)
 
@@ -434,6 +435,10 @@ def main(argv=None):
     # The same step as two calls (append kernel, then partial + merge), for comparison.
     settle(step_two_calls, 20.0)
     two_mean, two_med = time_calls(step_two_calls, args.steps, 3)
+    # The step with the last-level cache (256 MB) flushed before each call:
+    # the 1.23 GB cache does not fit it, so this differs from the steady
+    # state only by what the cache kept between steps.
+    cold_ms = time_calls_cold(step, min(args.steps, 20), dev)
 
     # the partial kernel moves the tiles of every cached token but the new one,
     # the page table and the queries (outputs go via the workspace)
@@ -474,6 +479,9 @@ def main(argv=None):
             "two_calls_ms_per_step": round(two_mean, 5),
             "two_calls_GBps": round(step_bytes / (two_mean * 1e-3) / 1e9, 2),
             "two_calls": "kv_quant_append then paged_decode_attn_int4, the same K steps back to back",
+            "cold_ms_per_step": round(cold_ms, 5),
+            "cold_GBps": round(step_bytes / (cold_ms * 1e-3) / 1e9, 2),
+            "cold": "the step with 1 GiB of another buffer read before each call (last-level cache flushed)",
             "host_wall_s": round(wall, 4),
             "settle_ms": round(settle_ms, 1),
             "timing": "steady state: the step runs untimed for settle_ms of GPU time (clock ramp), then "
