@@ -120,6 +120,7 @@ def test_append_host_validation_rejects_before_launch():
     assert _append(T=-1) == kvq.KVQ_ERR_INVALID_ARG
     assert _append(hkv=0) == kvq.KVQ_ERR_INVALID_ARG
     assert _append(T=0, k=None, v=None) == kvq.KVQ_OK          # empty call: no-op
+    assert _append(T=1, hkv=1 << 30) == kvq.KVQ_ERR_UNSUPPORTED  # 2^31 blocks: beyond one grid dimension
 
 
 def _decode(**kw):
