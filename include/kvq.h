@@ -34,8 +34,9 @@
  * Conventions for every entry point
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
  *     The caller allocates and frees every buffer; the library allocates
- *     nothing and keeps no state between calls.  All entry points are
- *     re-entrant.
+ *     nothing and keeps no state between calls, and its entry points are
+ *     re-entrant, with one exception: paged_decode_attn_int4_noalloc keeps
+ *     its partial states in a static per-GPU buffer (see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it and return; they never synchronize.
  *   - Return value: KVQ_OK (0) on success, a negative KVQ_ERR_* code
@@ -272,12 +273,6 @@ int kv_append_fp16(const uint16_t *k_new, const uint16_t *v_new,
                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, void *stream);
 
 /*
- * paged_decode_attn_fp16 — baseline decode over fp16 pools: the same
- * computation as paged_decode_attn_int4 with unquantized keys and values and
- * no rotation.  Same arguments, split and workspace as paged_decode_attn_int4
- * without had_block.
- */
-/*
  * paged_decode_attn_int4_noalloc — paged_decode_attn_int4 for callers that
  * cannot allocate device memory (code under HIP-graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the same computation, kernels and
@@ -306,6 +301,12 @@ int paged_decode_attn_int4_noalloc(const uint16_t *q, const uint8_t *k_pool, con
                                    int32_t had_block, float softmax_scale, float *out,
                                    int32_t pages_per_split, void *phase_event, void *stream);
 
+/*
+ * paged_decode_attn_fp16 — baseline decode over fp16 pools: the same
+ * computation as paged_decode_attn_int4 with unquantized keys and values and
+ * no rotation.  Same arguments, split and workspace as paged_decode_attn_int4
+ * without had_block.
+ */
 int paged_decode_attn_fp16(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                            int64_t num_pages, const int32_t *page_table,
                            int32_t max_pages_per_seq, const int32_t *context_lens,
