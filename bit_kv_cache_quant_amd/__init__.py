@@ -103,8 +103,15 @@ def status_string(status: int) -> str:
     return lib().kvq_status_string(int(status)).decode()
 
 
+_tile_bytes_cache: dict = {}
+
+
 def page_tile_bytes(head_dim: int, page_size: int) -> int:
-    return int(lib().kvq_page_tile_bytes(head_dim, page_size))
+    key = (int(head_dim), int(page_size))
+    v = _tile_bytes_cache.get(key)
+    if v is None:
+        v = _tile_bytes_cache[key] = int(lib().kvq_page_tile_bytes(key[0], key[1]))
+    return v
 
 
 def workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
@@ -115,7 +122,12 @@ def workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_context
 
 # --------------------------------------------------------------------------
 def _stream(t) -> int:
+    """The raw handle of the current stream of t's GPU (torch's own accessor
+    for it when present: building a Stream object costs ~3 us per call)."""
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(t.get_device()))
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -123,7 +135,7 @@ def _dev(t, dtype, name: str, ndim: int | None = None):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -249,8 +261,8 @@ def _decode(int4: bool, q, k_pool, v_pool, page_table, context_lens, num_kv_head
         raise ValueError(f"out must be [{B}][{hq}][{d}]")
     if out is None:
         out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
-    need = workspace_bytes(B, hq, num_kv_heads, max_context_len, page_size, pages_per_split, d) if B else 0
-    if workspace is None:
+    if workspace is None:   # (a caller's workspace is checked against the need by the library)
+        need = workspace_bytes(B, hq, num_kv_heads, max_context_len, page_size, pages_per_split, d) if B else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, torch.uint8, "workspace")
     if workspace.device != q.device:
