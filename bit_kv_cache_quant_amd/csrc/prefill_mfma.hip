@@ -86,7 +86,8 @@ struct alignas(16) PrefillShared {
     // top of each byte, or the odd dims' kept there (low nibble 0)
     uint8_t kev[kKeys * kCodeBytesPerRow];
     uint8_t kod[kKeys * kCodeBytesPerRow];
-    // values as fp16; row T's 16-byte piece p at piece slot p ^ vswz(T)
+    // values as fp16; row T's 16-byte piece p (dims 8p .. 8p + 7, in the
+    // order 8p + 0, 2, 4, 6, 1, 3, 5, 7) at piece slot p ^ vswz(T)
     uint8_t v[kKeys * kVRow];
     float ks[kKeys], vs[kKeys];          // scales
 };
@@ -107,19 +108,23 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// 8 two's-complement nibbles (nibble e = element e) -> 8 fp16 values: the
-// offset-binary nibble u = c + 8 goes into the mantissa of 1024 (fp16 1024 + u,
-// exact) and 1032 is subtracted (exact).
-__device__ __forceinline__ v8h nibbles_to_half(uint32_t w) {
+// 8 two's-complement nibbles (nibble e = element e) -> 8 fp16 values in the
+// order e = 0, 2, 4, 6, 1, 3, 5, 7: the offset-binary nibble u = c + 8 goes
+// into the mantissa of 1024 (fp16 1024 + u, exact; the exponent byte 0x64 is
+// taken from a constant by the byte permute itself) and 1032 is subtracted
+// (exact).  Pairing each byte's low nibbles (or its high nibbles) in one
+// word is what lets the permute draw the exponent bytes from one source.
+__device__ __forceinline__ v8h nibbles_to_half_eo(uint32_t w) {
     const uint32_t x = w ^ 0x88888888u;
     const uint32_t lo = x & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6 (one per byte)
     const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
-    // v_perm_b32(a, b, sel): selector bytes 0-3 pick bytes of b, 4-7 bytes of a, 0x0c gives 0
+    const uint32_t e64 = 0x64646464u;
+    // v_perm_b32(a, b, sel): selector bytes 0-3 pick bytes of b, 4-7 bytes of a
     uint32_t d[4];
-    d[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;   // (lo byte 0, hi byte 0)
-    d[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-    d[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-    d[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
+    d[0] = __builtin_amdgcn_perm(e64, lo, 0x04010400u);   // (element 0, element 2)
+    d[1] = __builtin_amdgcn_perm(e64, lo, 0x04030402u);   // (4, 6)
+    d[2] = __builtin_amdgcn_perm(e64, hi, 0x04010400u);   // (1, 3)
+    d[3] = __builtin_amdgcn_perm(e64, hi, 0x04030402u);   // (5, 7)
     const v8h biased = __builtin_bit_cast(v8h, make_uint4(d[0], d[1], d[2], d[3]));
     const _Float16 off = static_cast<_Float16>(1032.0f);
     return biased - v8h{off, off, off, off, off, off, off, off};
@@ -359,16 +364,18 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
         const int vx = vswz(T);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
-            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * kg + s4) ^ vx)]) = nibbles_to_half(vw[s4]);
+            *reinterpret_cast<v8h *>(&sh.v[T * kVRow + 16 * ((4 * kg + s4) ^ vx)]) = nibbles_to_half_eo(vw[s4]);
         if (lane < 16) sh.ks[16 * wave + lane] = half_to_float(r.s);
         else if (lane < 32) sh.vs[16 * wave + lane - 16] = half_to_float(r.s);
     };
 
     float m_run = -INFINITY, l_lane = 0.0f;   // this lane's position
-    v4f o[8];                                   // dims 16m + 4g + i of position j
+    // o[m][i]: position j, value slot 16m + 4g + i, which holds dim
+    // 16m + 8 (g >> 1) + 2i + (g & 1) (the staging's element order)
+    v4f o[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    // transposed-read address of dims 16m + 4 (j & 3) of key row 4g + j / 4
+    // transposed-read address of value slots 16m + 4 (j & 3) of key row 4g + j / 4
     // (+ 32 h for half h, + 16 for its second read): piece 2m + (j & 3) / 2
     const int tr_key = 4 * g + (j >> 2);
     const uint32_t tr_base = tr_key * kVRow + 8 * (j & 1);
@@ -377,9 +384,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
     const uint32_t tr_b = tr_base + 16u * (uint32_t)(tr_piece ^ (tr_x & 1));
     const uint32_t tr_c = 32u * (uint32_t)(tr_x >> 1);
 
-    // -1 in a register the compiler cannot see through: fma(x, -1, y) with
-    // a literal would become y - x, whose widening of x costs an extra
-    // conversion instead of the mixed-precision fma
+    // -1 as the multiplier operand of the weight split's mixed-precision fmas
     float neg_one = -1.0f;
     asm("" : "+v"(neg_one));
 
@@ -413,11 +418,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[t][i]);
-        zm = rows_max4(zm);
-        const float m_new = fmaxf(m_run, zm * rm);   // finite from the first chunk on (key 0 is visible)
         // rescale only when some position of the wave has a new maximum (a
-        // wave-uniform branch; alpha is exactly 1 for the others)
-        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+        // wave-uniform branch; alpha is exactly 1 for the others).  A
+        // position's maximum is over its 4 lanes, and it exceeds m_run
+        // exactly when one of those lanes' own maxima does (rm > 0), so the
+        // lane exchange is needed only inside the branch.
+        if (__builtin_amdgcn_ballot_w64(zm * rm > m_run)) {
+            const float m_new = fmaxf(m_run, rows_max4(zm) * rm);   // finite from the first chunk on (key 0 is visible)
             const float alpha = fast_exp2(m_run - m_new);
             l_lane *= alpha;
 #pragma unroll
@@ -449,12 +456,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
             for (int u = 0; u < 2; ++u) {
                 const v2h hi = __builtin_convertvector((v2f){pv[2 * u], pv[2 * u + 1]}, v2h);
                 ph[t][u] = hi;
-                // pv - hi, exact (|pv - hi| is at most half an fp16 ulp of pv),
-                // as one mixed-precision fma per entry (the fp16 operand is
-                // widened inside the instruction)
-                const float d0 = fmaf(static_cast<float>(hi[0]), neg_one, pv[2 * u]);
-                const float d1 = fmaf(static_cast<float>(hi[1]), neg_one, pv[2 * u + 1]);
-                pl[t][u] = __builtin_convertvector((v2f){d0, d1}, v2h);
+                // lo = fp16(pv - hi): pv - hi is exact in fp32 (|pv - hi| is at
+                // most half an fp16 ulp of pv), so one mixed-precision fma that
+                // rounds straight to fp16 gives the same bits as an fp32 fma
+                // and a conversion; mixlo / mixhi fill the two halves of the
+                // pair (the fp16 operand is hi's low or high half, widened
+                // inside the instruction)
+                const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+                uint32_t lb;
+                asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]"
+                    : "=v"(lb) : "v"(hb), "v"(neg_one), "v"(pv[2 * u]));
+                asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                    : "+v"(lb) : "v"(hb), "v"(neg_one), "v"(pv[2 * u + 1]));
+                pl[t][u] = __builtin_bit_cast(v2h, lb);
             }
         }
         v8h pb_hi[2], pb_lo[2];   // element 4 (t & 1) + i of half t / 2
@@ -525,8 +539,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] *= inv;
     if constexpr (BH > 0) {
+        // the spans in increasing order, each where its dim bit lives
 #pragma unroll
-        for (int s = 1; s < 4; s <<= 1) {                          // spans 1, 2: registers i ^ s
+        for (int m = 0; m < 8; ++m)                                // span 1: lane rows g ^ 1
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[m][i] = rows_butterfly<1>(o[m][i], g);
+#pragma unroll
+        for (int s = 1; s < 4; s <<= 1) {                          // spans 2, 4: registers i ^ s
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -538,12 +557,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
                 }
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m)                                // spans 4, 8: lane rows g ^ 1, g ^ 2
+        for (int m = 0; m < 8; ++m)                                // span 8: lane rows g ^ 2
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[m][i] = rows_butterfly<1>(o[m][i], g);
-                o[m][i] = rows_butterfly<2>(o[m][i], g);
-            }
+            for (int i = 0; i < 4; ++i) o[m][i] = rows_butterfly<2>(o[m][i], g);
 #pragma unroll
         for (int s = 1; s < 8 && 16 * s < BH; s <<= 1) {           // spans 16, 32, 64: registers m ^ s
 #pragma unroll
@@ -560,6 +576,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_int4_kernel(PrefillArgs a
         const float cb = rsqrtf(static_cast<float>(BH));
 #pragma unroll
         for (int m = 0; m < 8; ++m) o[m] *= cb;
+    }
+    // Regroup lane rows g and g ^ 1 so that lane (g, j) holds dims
+    // 16m + 4g .. 16m + 4g + 3: the even row (dims 8h + 0, 2, 4, 6) keeps
+    // 0, 2 and takes the odd row's 1, 3; the odd row (8h + 1, 3, 5, 7) keeps
+    // 5, 7 and takes the even row's 4, 6.
+    const bool odd = (g & 1) != 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        float lo0, hi0, lo1, hi1;
+        swap_rows<1>(odd ? o[m][0] : o[m][2], lo0, hi0);   // even gets the odd row's dim 1, odd the even row's 4
+        swap_rows<1>(odd ? o[m][1] : o[m][3], lo1, hi1);   // dims 3 and 6
+        const float r0 = odd ? lo0 : hi0, r1 = odd ? lo1 : hi1;
+        o[m] = odd ? v4f{r0, o[m][2], r1, o[m][3]} : v4f{o[m][0], r0, o[m][1], r1};
     }
     if (j < rows) {
         float *dst = a.out + ((int64_t)(row0 + j) * a.num_q_heads + qh) * kHeadDim + 4 * g;
