@@ -61,3 +61,48 @@ def test_noalloc_decode_rejects_a_request_beyond_the_scratch(dev):
     with pytest.raises(kvq.KVQError) as e:
         kvq.paged_decode_attn_int4_noalloc(q, pool, pool, pt, cl, 8, 16, 64, 0.088, 8192, out=out)
     assert e.value.status == kvq.KVQ_ERR_TOO_LARGE
+
+
+def test_noalloc_decode_replays_under_hip_graph(dev):
+    """Callers that cannot allocate capture it: a captured call replays to the
+    eager output, with eager calls of another shape between replays (they
+    overwrite the shared static scratch, which each call fully rewrites
+    before reading)."""
+    r = np.random.default_rng(12)
+    lens = [int(x) for x in r.integers(0, 700, size=20)]    # batch-wide ranges
+    w, kp, vp, _, _ = _case(dev, lens, 64, 16, 320)
+    w2, kp2, vp2, _, _ = _case(dev, [300, 17, 64], 128, 32, 321)   # per-sequence splits
+
+    def args(wk, k, v):
+        return (wk.query(0, dev), k, v, torch.as_tensor(wk.table(0), device=dev),
+                torch.as_tensor(wk.context_lens, device=dev), wk.num_kv_heads, wk.page_size, wk.had_block,
+                wk.softmax_scale, int(max(wk.context_lens)))
+
+    a1, a2 = args(w, kp, vp), args(w2, kp2, vp2)
+    out1 = torch.empty((w.batch, w.num_q_heads, wl.HEAD_DIM), dtype=torch.float32, device=dev)
+    out2 = torch.empty((w2.batch, w2.num_q_heads, wl.HEAD_DIM), dtype=torch.float32, device=dev)
+    say(f"no-alloc decode under graph capture: B={w.batch}, eager B={w2.batch} between replays")
+    kvq.paged_decode_attn_int4_noalloc(*a1, out=out1)
+    kvq.paged_decode_attn_int4_noalloc(*a2, out=out2)
+    torch.cuda.synchronize()
+    eager1, eager2 = out1.clone(), out2.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kvq.paged_decode_attn_int4_noalloc(*a1, out=out1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kvq.paged_decode_attn_int4_noalloc(*a1, out=out1)
+    for rep in range(4):
+        out1.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out1, eager1), f"replay {rep} differs from the eager call"
+        out2.fill_(float("nan"))
+        kvq.paged_decode_attn_int4_noalloc(*a2, out=out2)   # eager work on the same scratch
+        torch.cuda.synchronize()
+        assert torch.equal(out2, eager2), f"the eager call after replay {rep} changed"
+    del graph
