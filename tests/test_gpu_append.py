@@ -104,6 +104,24 @@ def test_append_edge_values_all_block_sizes(dev, had_block, page_size):
     _assert_pools_equal(gv, hv, "V pool")
 
 
+@pytest.mark.parametrize("hkv,bh", [(1, 128), (2, 64), (3, 32), (5, 128), (6, 0), (7, 64), (12, 32), (16, 128)])
+def test_append_rows_over_kv_head_counts(dev, hkv, bh):
+    # Every token in one shuffled call, for KV-head counts from 1 to 16
+    # (powers of two and not), token counts that leave a ragged last block,
+    # and each block size: whole canary-filled pools against the oracle.
+    lens = [29, 64, 3, 50]
+    w = wl.small(len(lens), lens, bh, 16, cfg_id=90 + hkv, num_kv_heads=hkv, num_q_heads=4 * hkv)
+    seq = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(lens)])
+    pos = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+    order = np.random.default_rng(hkv).permutation(seq.size)
+    w.append_seq, w.append_pos = seq[order], pos[order]
+    k = torch.as_tensor(_edge_rows(seq.size, hkv, 30 + hkv), device=dev)
+    v = torch.as_tensor(_edge_rows(seq.size, hkv, 40 + hkv), device=dev)
+    gk, gv, hk, hv = _run_append(w, dev, k=k, v=v)
+    _assert_pools_equal(gk, hk, f"K pool (Hkv {hkv})")
+    _assert_pools_equal(gv, hv, f"V pool (Hkv {hkv})")
+
+
 def test_append_zero_tokens_is_a_noop(dev):
     w = wl.c1()
     kp, vp = int4_pools(w, dev)

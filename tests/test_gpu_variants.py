@@ -90,6 +90,31 @@ def test_variant_append_bit_exact(dev, cfg, page_size):
     assert np.array_equal(vp.cpu().numpy(), hv), "V pool differs from the oracle's"
 
 
+@pytest.mark.parametrize("cfg", [(0, 32, 32, 0, 0), (0, 128, 32, 1, MASK), (1, 64, 32, 0, 0)], ids=_ids)
+@pytest.mark.parametrize("hkv", [1, 3, 6])
+def test_variant_append_rows_over_kv_head_counts(dev, cfg, hkv):
+    """Every token in one shuffled call, for 1, 3 and 6 KV heads, with a
+    ragged last block of tokens: whole pools against the oracle."""
+    lens = [45, 64, 2]
+    w = wl.small(len(lens), lens, cfg[1], 16, cfg_id=430 + hkv, num_kv_heads=hkv, num_q_heads=4 * hkv)
+    kp, vp = _pools(w, cfg, dev, hkv)
+    hk, hv = kp.cpu().numpy(), vp.cpu().numpy()
+    seq = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(lens)])
+    pos = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+    order = np.random.default_rng(7 + hkv).permutation(seq.size)
+    seq, pos = seq[order], pos[order]
+    k = _special_rows(seq.size, hkv, 50 + hkv)
+    v = np.ascontiguousarray(k[::-1])
+    say(f"variant append {_ids(cfg)} Hkv={hkv}")
+    kvq.kv_quant_append_cfg(torch.as_tensor(k, device=dev), torch.as_tensor(v, device=dev),
+                            torch.as_tensor(seq, device=dev), torch.as_tensor(pos, device=dev),
+                            torch.as_tensor(w.table(0), device=dev), kp, vp, 16, kvq.quant_config(*cfg))
+    torch.cuda.synchronize()
+    oracle.kv_quant_append_cfg(k, v, seq, pos, w.table(0), hk, hv, oracle.qcfg(*cfg), 16)
+    assert np.array_equal(kp.cpu().numpy(), hk), "K pool differs from the oracle's"
+    assert np.array_equal(vp.cpu().numpy(), hv), "V pool differs from the oracle's"
+
+
 def test_token_wise_config_is_the_plain_append(dev):
     """{INT4, Bh, 128, no search, no signs} through the variant entry point
     writes exactly what kv_quant_append writes."""
