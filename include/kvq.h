@@ -167,7 +167,10 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * one sequence into the next; otherwise each sequence is cut into equal
  * ranges of at most 2048 tokens.  Partial softmax states go to `workspace`
  * and a second kernel merges them, so the result does not depend on the
- * split beyond fp32 rounding.
+ * split beyond fp32 rounding.  (For tests and measurement, the environment
+ * variable KVQ_RANGE_WAVES = 1, 2 or 4, read at each call, sets how many
+ * waves of a block share one page range in the per-sequence split schedule
+ * of this token-wise INT4 decode; the default chooses by the launch size.)
  *
  *   q              fp16 [batch][num_q_heads][head_dim]
  *   k_pool, v_pool uint8 [num_pages][num_kv_heads][tile]
