@@ -153,15 +153,12 @@ size_t balanced_workspace_bytes(const BalancedPlan &pl, int32_t batch) {
     return floats * sizeof(float) + (((size_t)batch + 1) * sizeof(int32_t) + 15) / 16 * 16;
 }
 
-// Optional debug mode (environment variable KVQ_CHECK=1): copy the page table
-// and lengths to the host (this synchronises the stream) and range-check them.
+// Optional debug mode (environment variable KVQ_CHECK=1, read at each call):
+// copy the page table and lengths to the host (this synchronises the stream)
+// and range-check them.
 bool debug_checks_enabled() {
-    static int enabled = -1;
-    if (enabled < 0) {
-        const char *e = getenv("KVQ_CHECK");
-        enabled = (e && e[0] == '1') ? 1 : 0;
-    }
-    return enabled == 1;
+    const char *e = getenv("KVQ_CHECK");
+    return e && e[0] == '1';
 }
 
 int check_append_indices(const int32_t *token_seq, const int32_t *token_pos, int32_t num_tokens,
