@@ -223,6 +223,29 @@ int check_decode_indices(const int32_t *page_table, int32_t max_pages_per_seq, c
     return rc;
 }
 
+// Debug check of a prefill call (KVQ_CHECK=1): q_start starts at 0, never
+// decreases and ends at num_q; every context length fits the page table;
+// every page entry a sequence's context reads lies in [0, num_pages).
+int check_prefill_indices(const int32_t *q_start, int32_t num_q, const int32_t *page_table, int32_t max_pages_per_seq,
+                          const int32_t *context_lens, int32_t batch, int64_t num_pages, int32_t page_size,
+                          hipStream_t stream) {
+    int32_t *qs = (int32_t *)malloc(sizeof(int32_t) * ((size_t)batch + 1));
+    int rc = qs ? KVQ_OK : KVQ_ERR_INVALID_ARG;
+    if (rc == KVQ_OK && (hipMemcpyAsync(qs, q_start, sizeof(int32_t) * ((size_t)batch + 1), hipMemcpyDeviceToHost,
+                                        stream) != hipSuccess ||
+                         hipStreamSynchronize(stream) != hipSuccess))
+        rc = KVQ_ERR_HIP;
+    if (rc == KVQ_OK && (qs[0] != 0 || qs[batch] != num_q)) rc = KVQ_ERR_INVALID_ARG;
+    for (int32_t b = 0; rc == KVQ_OK && b < batch; ++b)
+        if (qs[b + 1] < qs[b]) rc = KVQ_ERR_INVALID_ARG;
+    free(qs);
+    if (rc != KVQ_OK) return rc;
+    // the decode's check with the largest length the page table holds
+    const int64_t cap = (int64_t)max_pages_per_seq * page_size;
+    return check_decode_indices(page_table, max_pages_per_seq, context_lens, batch,
+                                cap > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int32_t)cap, num_pages, page_size, stream);
+}
+
 int validate_append(const void *k_new, const void *v_new, const int32_t *token_seq, const int32_t *token_pos,
                     int32_t num_tokens, const int32_t *page_table, int32_t max_pages_per_seq,
                     const void *k_pool, const void *v_pool, int64_t num_pages, int32_t num_kv_heads,
@@ -532,6 +555,11 @@ int paged_prefill_attn_int4(const uint16_t *q, const int32_t *q_start, int32_t n
     if ((int64_t)max_pages_per_seq * page_size > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
     const int32_t chunks = head_chunks_of(num_q_heads, num_kv_heads);
     if ((int64_t)num_kv_heads * chunks > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (debug_checks_enabled()) {
+        const int rc = check_prefill_indices(q_start, num_q, page_table, max_pages_per_seq, context_lens, batch,
+                                             num_pages, page_size, static_cast<hipStream_t>(stream));
+        if (rc != KVQ_OK) return rc;
+    }
     kvq::PrefillArgs a{};
     a.q = q;
     a.q_start = q_start;

@@ -51,10 +51,12 @@
  *     [0, num_pages); (seq, pos) pairs are unique within one append call;
  *     context_lens[b] <= max_context_len <= max_pages_per_seq * page_size.
  *     With the environment variable KVQ_CHECK=1 (read at each call) the
- *     appends and decodes copy these indices to the host (synchronising the
- *     stream) and return KVQ_ERR_INVALID_ARG, before any launch, for a
- *     page-table entry outside [0, num_pages), a position past
- *     max_pages_per_seq pages or a context length above max_context_len.
+ *     appends, decodes and the prefill copy these indices to the host
+ *     (synchronising the stream) and return KVQ_ERR_INVALID_ARG, before any
+ *     launch, for a page-table entry outside [0, num_pages), a position past
+ *     max_pages_per_seq pages, a context length above max_context_len (the
+ *     prefill: above max_pages_per_seq * page_size) or a prefill q_start
+ *     that does not run from 0 to num_q without decreasing.
  *
  * Layouts
  *   K/V input:      fp16 [num_tokens][num_kv_heads][head_dim] (row-major).

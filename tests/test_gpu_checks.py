@@ -112,3 +112,30 @@ def test_checked_append_rejects_position_past_the_table(dev, monkeypatch):
         kvq.kv_quant_append(k, v, seq, pos, table, kp, vp, P, BH)
     assert e.value.status == kvq.KVQ_ERR_INVALID_ARG
     assert table.data_ptr() == full.data_ptr() and np.array_equal(table.cpu().numpy(), pt.cpu().numpy())
+
+
+def test_checked_prefill(dev, monkeypatch):
+    """The prefill under KVQ_CHECK=1: valid indices give the unchecked result
+    bit for bit; a page outside the declared pool is rejected."""
+    w, kp, vp, q, pt, cl = _setup(dev)
+    qlens = [40, 5, 33]
+    qs = torch.as_tensor(np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32), device=dev)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(620)
+    qp = torch.randn((int(sum(qlens)), w.num_q_heads, wl.HEAD_DIM), generator=g).to(torch.float16).to(dev)
+
+    def run(kpool, vpool, table):
+        out = kvq.paged_prefill_attn_int4(qp, qs, kpool, vpool, table, cl, w.num_kv_heads, P, BH, w.softmax_scale)
+        torch.cuda.synchronize()
+        return out
+    monkeypatch.delenv("KVQ_CHECK", raising=False)
+    plain = run(kp, vp, pt).clone()
+    monkeypatch.setenv("KVQ_CHECK", "1")
+    say("KVQ_CHECK=1: prefill with valid indices, then with a page past the declared pool")
+    assert torch.equal(run(kp, vp, pt), plain)
+    n = kp.shape[0]
+    bad = pt.clone()
+    bad[2, 3] = n - 1
+    with pytest.raises(kvq.KVQError) as e:
+        run(kp[:n - 1], vp[:n - 1], bad)
+    assert e.value.status == kvq.KVQ_ERR_INVALID_ARG
