@@ -79,10 +79,30 @@ __device__ __forceinline__ uint32_t nib_bytes(uint32_t n) {
 }
 
 // Even / odd dims of 8 packed codes (one word) as two operand words.
+// MXFP4: the magnitudes by table from the low 3 bits of each nibble, the
+// sign (bit 3 of the nibble) as a 0xFF byte mask straight from v_perm_b32's
+// sign-fill selectors (8, 9 replicate bit 15, 31 of the second source; 10,
+// 11 bit 15, 31 of the first), fed with shifted copies of w that put each
+// nibble's sign bit at one of those positions, and one bitwise select
+// between the negative and the positive table entry: 14 instructions per
+// word instead of 21.
 template <int FMT>
 __device__ __forceinline__ void split_codes(uint32_t w, uint32_t &lo, uint32_t &hi) {
-    lo = nib_bytes<FMT>(w & 0x0F0F0F0Fu);
-    hi = nib_bytes<FMT>((w >> 4) & 0x0F0F0F0Fu);
+    if constexpr (FMT == KVQ_FMT_INT4) {
+        lo = nib_bytes<FMT>(w & 0x0F0F0F0Fu);
+        hi = nib_bytes<FMT>((w >> 4) & 0x0F0F0F0Fu);
+    } else {
+        const uint32_t sl = w & 0x07070707u;
+        const uint32_t sh = (w >> 4) & 0x07070707u;
+        const uint32_t ml = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);   // w bits 3, 11, 19, 27
+        const uint32_t mh = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);         // w bits 7, 15, 23, 31
+        const uint32_t pl = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sl);
+        const uint32_t nl = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sl);
+        const uint32_t ph = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sh);
+        const uint32_t nh = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sh);
+        lo = (nl & ml) | (pl & ~ml);
+        hi = (nh & mh) | (ph & ~mh);
+    }
 }
 
 __device__ __forceinline__ float ulimbs_to_float(v4i d) {
