@@ -58,25 +58,9 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Key or value bytes of 4 nibbles (one per byte, in the low 4 bits of each
-// byte of n) as MFMA operands.  INT4: offset binary c + 8 (c xor 8).  MXFP4:
-// the signed byte 2 v of the E2M1 value v: magnitudes by table (0, 1, 2, 3,
-// 4, 6, 8, 12 for codes 0..7), negated where bit 3 is set.
-template <int FMT>
-__device__ __forceinline__ uint32_t nib_bytes(uint32_t n) {
-    if constexpr (FMT == KVQ_FMT_INT4) {
-        return (n ^ 0x08080808u) & 0x0F0F0F0Fu;
-    } else {
-        const uint32_t sel = n & 0x07070707u;
-        const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sel);
-        const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sel);
-        // 0xFF in each byte whose bit 3 is set: (t << 5) - (t >> 3) is
-        // sum_k (2^(8k+8) - 2^(8k)) over those bytes, modulo 2^32
-        const uint32_t t = n & 0x08080808u;
-        const uint32_t sm = (t << 5) - (t >> 3);
-        return (neg & sm) | (pos & ~sm);
-    }
-}
+// INT4 key or value bytes of 4 nibbles (one per byte, in the low 4 bits of
+// each byte of n) as MFMA operands: offset binary c + 8 (c xor 8).
+__device__ __forceinline__ uint32_t nib_bytes_int4(uint32_t n) { return (n ^ 0x08080808u) & 0x0F0F0F0Fu; }
 
 // Even / odd dims of 8 packed codes (one word) as two operand words.
 // MXFP4: the magnitudes by table from the low 3 bits of each nibble, the
@@ -89,8 +73,8 @@ __device__ __forceinline__ uint32_t nib_bytes(uint32_t n) {
 template <int FMT>
 __device__ __forceinline__ void split_codes(uint32_t w, uint32_t &lo, uint32_t &hi) {
     if constexpr (FMT == KVQ_FMT_INT4) {
-        lo = nib_bytes<FMT>(w & 0x0F0F0F0Fu);
-        hi = nib_bytes<FMT>((w >> 4) & 0x0F0F0F0Fu);
+        lo = nib_bytes_int4(w & 0x0F0F0F0Fu);
+        hi = nib_bytes_int4((w >> 4) & 0x0F0F0F0Fu);
     } else {
         const uint32_t sl = w & 0x07070707u;
         const uint32_t sh = (w >> 4) & 0x07070707u;
