@@ -218,3 +218,43 @@ def test_variant_decode_sharp_softmax(dev, cfg, mult):
     err = float(np.max(np.abs(out.cpu().numpy() - want)))
     say(f"variant decode {_ids(cfg)} at {mult}x scale: max-abs {err:.3e}")
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("cfg", [(1, 32, 32, 0, 0), (1, 128, 32, 0, MASK)], ids=_ids)
+@pytest.mark.parametrize("sched", ["split", "balanced"])
+def test_mxfp4_decode_reads_negative_zero_as_zero(dev, cfg, sched):
+    """E2M1 has two zeros; the append stores +0 only, but a cache may hold
+    -0 (code 8).  Every +0 code of the written code rows rewritten as -0
+    leaves the decode's output unchanged bit for bit (keys through the scaled
+    FP4 instruction, values through the sign-mask byte conversion), and the
+    oracle over the rewritten cache agrees."""
+    lens = [300, 77, 5] if sched == "split" else [int(x) for x in np.random.default_rng(44).integers(1, 300, 20)]
+    w = wl.small(len(lens), lens, cfg[1], 16, cfg_id=445)
+    kp, vp, hk, hv = _build(cfg, w, dev, seed=45)
+    q = w.query(0, dev)
+    pt = torch.as_tensor(w.table(0), device=dev)
+    cl = torch.as_tensor(w.context_lens, device=dev)
+    gcfg = kvq.quant_config(*cfg)
+
+    def decode(k_pool, v_pool):
+        o = kvq.paged_decode_attn_cfg(q, k_pool, v_pool, pt, cl, w.num_kv_heads, 16, gcfg, w.softmax_scale,
+                                      int(max(lens)))
+        torch.cuda.synchronize()
+        return o.clone()
+    before = decode(kp, vp)
+    ncode = w.num_kv_heads * 16 * (D // 2)   # code rows of every head come first in a page
+
+    def negative_zeros(pool):
+        flat = pool.reshape(pool.shape[0], -1).copy()
+        c = flat[:, :ncode]
+        lo, hi = c & 0x0F, c >> 4
+        flat[:, :ncode] = (np.where(hi == 0, 8, hi) << 4) | np.where(lo == 0, 8, lo)
+        return flat.reshape(pool.shape)
+    hk2, hv2 = negative_zeros(hk), negative_zeros(hv)
+    assert np.count_nonzero(hk2 != hk) > 0 and np.count_nonzero(hv2 != hv) > 0
+    say(f"MXFP4 decode over -0 codes {_ids(cfg)} {sched}: {np.count_nonzero(hv2 != hv)} value bytes rewritten")
+    after = decode(torch.as_tensor(hk2, device=dev), torch.as_tensor(hv2, device=dev))
+    assert torch.equal(after, before)
+    want = oracle.paged_decode_attn_cfg(q.cpu().numpy(), hk2, hv2, w.table(0), w.context_lens, w.num_kv_heads, 16,
+                                        oracle.qcfg(*cfg), w.softmax_scale)
+    assert float(np.max(np.abs(after.cpu().numpy() - want))) <= ATOL
