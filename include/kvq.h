@@ -56,7 +56,10 @@
  *     launch, for a page-table entry outside [0, num_pages), a position past
  *     max_pages_per_seq pages, a context length above max_context_len (the
  *     prefill: above max_pages_per_seq * page_size) or a prefill q_start
- *     that does not run from 0 to num_q without decreasing.
+ *     that does not run from 0 to num_q without decreasing.  An append's
+ *     token_seq entries must name rows the page table has: the calls do not
+ *     take its row count, so no mode can check that (KVQ_CHECK copies the
+ *     rows up to the largest sequence named).
  *
  * Layouts
  *   K/V input:      fp16 [num_tokens][num_kv_heads][head_dim] (row-major).
